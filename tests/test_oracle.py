@@ -1,0 +1,406 @@
+"""Pins for the float64 oracle (CPU only).
+
+Each test fixes the oracle to something other than itself: values the pages
+print (tests/golden/), closed forms, invariants, an arbitrary-precision brute
+force without the max shift, and PyTorch's float64 CPU cross-entropy.  The
+mutation tests at the end plant plausible mistakes in the oracle and check
+that at least one pin fails for each.
+"""
+
+import contextlib
+import math
+
+import mpmath
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from oracle import ce as oce
+from oracle import lce as olce
+from softmax_cross_entropy_amd import inputs
+from tests import golden_io
+
+LOG2 = math.log(2.0)
+
+
+def f32_rows(rows):
+    return oce.decode(np.asarray(rows, np.float64).astype(np.float32), "f32")
+
+
+# --- MLX PR #4188 "Shift by the max in cross_entropy", Proposed changes -----
+
+def pin_equal_logits(values=(1.0, 1e4, 1e6, 1e8, 1e36), g=2.5):
+    """[v, v] with target 0 gives log 2 and gradient g * (-1/2, 1/2) at every v."""
+    z = f32_rows([[v, v] for v in values])
+    y = np.zeros(len(values), np.int32)
+    loss, m, ls = oce.forward(z, y)
+    np.testing.assert_allclose(loss, LOG2, rtol=0, atol=1e-15)
+    # the log-sum-exp is kept as the pair (m, log s): m is the stored value itself
+    assert np.array_equal(m, z[:, 0])
+    np.testing.assert_allclose(ls, LOG2, rtol=0, atol=1e-15)
+    d = oce.grad(z, y, np.full(len(values), g))
+    np.testing.assert_allclose(d, np.tile([-0.5 * g, 0.5 * g], (len(values), 1)), rtol=0, atol=1e-15)
+
+
+def test_equal_logits_log2():
+    gold = golden_io.read("shift_by_max.txt")
+    pin_equal_logits(tuple(gold["equal_values"]) + (gold["equal_checked_max"],))
+    # PyTorch's printed value, at float32 print precision
+    assert abs(LOG2 - gold["equal_torch"][0]) < 5e-8
+
+
+def test_gap_rows():
+    """[2 + c, -1 + c], target 0: log(1 + e^-3) while the stored gap stays 3."""
+    gold = golden_io.read("shift_by_max.txt")
+    offs = gold["gap_offsets"]
+    z = f32_rows([[2.0 + c, -1.0 + c] for c in offs])
+    loss, _, _ = oce.forward(z, np.zeros(len(offs), np.int32))
+    expect = math.log1p(math.exp(-3.0))
+    for c, zr, l in zip(offs, z, loss):
+        if zr[0] - zr[1] == 3.0:
+            assert abs(l - expect) < 1e-15
+        else:
+            # float32 stores 1e8 + 2 and 1e8 - 1 both as 1e8 (its ulp there is 8):
+            # for the stored input the correct loss is log 2.
+            assert c == 1e8 and zr[0] == zr[1] == 1e8
+            assert abs(l - LOG2) < 1e-15
+    # at c = 0 the page's float32 value agrees to within one float32 ulp at |lse| ~ 2
+    assert abs(loss[0] - gold["gap_unshifted_f32"][0]) < 2.0 ** -22
+
+
+def unshifted_f32_loss(rows, y):
+    """The composition the page blames: a correctly rounded float32 lse minus z_y in float32."""
+    z = np.asarray(rows, np.float64).astype(np.float32)
+    out = []
+    for zr, yy in zip(z, y):
+        lse64 = float(mpmath.log(mpmath.fsum(mpmath.exp(mpmath.mpf(float(v))) for v in zr)))
+        out.append(np.float32(np.float32(lse64) - zr[yy]))
+    return np.array(out, np.float32)
+
+
+def test_unshifted_composition_reproduces_printed_losses():
+    """Negative control: the unshifted float32 composition gives the page's wrong numbers."""
+    gold = golden_io.read("shift_by_max.txt")
+    gap = unshifted_f32_loss([[2.0 + c, -1.0 + c] for c in gold["gap_offsets"]], [0] * 4)
+    eq = unshifted_f32_loss([[v, v] for v in gold["equal_values"]], [0] * 4)
+    for got, printed in list(zip(gap, gold["gap_unshifted_f32"])) + list(zip(eq, gold["equal_unshifted_f32"])):
+        if printed * 2 ** 12 == int(printed * 2 ** 12):
+            # the values that show the bug are multiples of the float32 ulp at the
+            # offset, so the composition must give them exactly
+            assert float(got) == printed, (got, printed)
+        else:
+            # at offset 0 the page prints a rounded float32; allow two ulps at |lse| ~ 2
+            assert abs(float(got) - printed) <= 2.0 ** -21, (got, printed)
+    # and those values fail the pins above
+    assert abs(float(eq[1]) - LOG2) > 1e-4 and float(eq[3]) == 0.0
+    assert abs(float(gap[2]) - math.log1p(math.exp(-3.0))) > 1e-2
+
+
+# --- closed forms -----------------------------------------------------------
+
+@pytest.mark.parametrize("V", [1, 2, 8, 1024, 151936])
+@pytest.mark.parametrize("v", [0.0, -3.5, 1e4])
+def test_uniform_row(V, v):
+    """All entries equal: loss = log V, lse = v + log V, grad = g (1/V - onehot)."""
+    z = np.full((3, V), v)
+    y = np.array([0, V // 2, V - 1], np.int32)
+    g = np.array([1.0, 0.5, -2.0])
+    loss, m, ls = oce.forward(z, y)
+    np.testing.assert_allclose(loss, math.log(V), rtol=1e-15, atol=1e-15)
+    np.testing.assert_allclose(m, v, rtol=0, atol=0)
+    np.testing.assert_allclose(ls, math.log(V), rtol=1e-15, atol=1e-15)
+    d = oce.grad(z, y, g)
+    expect = np.tile(g[:, None] / V, (1, V))
+    expect[np.arange(3), y] -= g
+    np.testing.assert_allclose(d, expect, rtol=1e-13, atol=1e-17)
+
+
+def test_only_target_finite():
+    """Every entry -inf except the target: loss 0, gradient 0."""
+    z = np.full((2, 7), -np.inf)
+    y = np.array([3, 6], np.int32)
+    z[0, 3], z[1, 6] = 1.25, -1e30
+    loss, _, _ = oce.forward(z, y)
+    assert np.all(loss == 0.0)
+    d = oce.grad(z, y, np.array([1.0, 3.0]))
+    assert np.all(d == 0.0)
+
+
+def test_target_neginf():
+    """Target entry -inf: loss +inf; grad_y = -g; the rest is g times the softmax."""
+    z = np.array([[-np.inf, 0.0, math.log(3.0)]])
+    loss, _, _ = oce.forward(z, np.array([0]))
+    assert loss[0] == np.inf
+    d = oce.grad(z, np.array([0]), np.array([2.0]))
+    np.testing.assert_allclose(d[0], [-2.0, 0.5, 1.5], rtol=1e-15)
+
+
+def test_degenerate_rows_are_nan():
+    """All -inf, a +inf entry, a NaN entry, or a target outside [0, V): NaN loss and gradient."""
+    z = np.array([[-np.inf, -np.inf, -np.inf], [0.0, np.inf, 1.0], [0.0, np.nan, 1.0], [0.0, 1.0, 2.0], [0.0, 1.0, 2.0]])
+    y = np.array([0, 0, 2, 3, -1], np.int32)
+    loss, _, _ = oce.forward(z, y)
+    assert np.all(np.isnan(loss))
+    d = oce.grad(z, y, np.ones(5))
+    assert np.all(np.isnan(d))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_grad_rows_sum_to_zero(dtype):
+    b = inputs.normal_rows(64, 1000, dtype, workload=90)
+    z = oce.decode(b.logits, dtype)
+    d = oce.grad(z, b.targets, np.linspace(-3, 3, 64))
+    assert np.max(np.abs(d.sum(axis=1))) <= 1e-14
+
+
+def test_target_probability_is_exp_minus_loss():
+    """softmax(z)_y = exp(-loss): ties the forward to the gradient at the target."""
+    b = inputs.normal_rows(128, 777, "f32", workload=91)
+    z = oce.decode(b.logits, "f32")
+    loss, _, _ = oce.forward(z, b.targets)
+    d = oce.grad(z, b.targets, np.ones(128))
+    np.testing.assert_allclose(d[np.arange(128), b.targets] + 1.0, np.exp(-loss), rtol=1e-12, atol=1e-15)
+
+
+# --- MLX issue #4686, Expected behavior: the strided-view gradient norm ------
+
+def test_strided_view_grad_norm_matches_page():
+    gold = golden_io.read("strided_view_grad_norm.txt")
+    x, y = inputs.strided_view_source(gold["B"], gold["L"], gold["V"])
+    view = x[:, :-1].reshape(-1, gold["V"])  # NumPy slicing, no strides passed on
+    yv = inputs.shifted_targets(y)
+    z = oce.decode(view, "f32")
+    loss, m, ls = oce.forward(z, yv)
+    d = oce.grad(z, yv, np.ones(len(yv)))
+    norm = float(np.sqrt(np.sum(d * d)))
+    # Frobenius identity |p - e_y|^2 = 1 - 2 p_y + sum_j p_j^2, with p_y = exp(-loss)
+    # and sum_j p_j^2 = exp(logsumexp(2 z) - 2 lse) from SciPy's logsumexp.
+    lse2 = scipy.special.logsumexp(2.0 * z, axis=1)
+    ident = np.sqrt(np.sum(1.0 - 2.0 * np.exp(-loss) + np.exp(lse2 - 2.0 * (m + ls))))
+    assert abs(norm - ident) < 1e-10 * norm
+    assert abs(round(norm, gold["grad_norm_decimals"]) - gold["grad_norm"]) <= 1e-3
+    # the page's buggy norms are far away
+    assert all(abs(norm - bad) > 30 for bad in gold["buggy_grad_norms"])
+
+
+# --- invariance to a shared offset (numerics stress workload) ---------------
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_offset_twins(dtype):
+    b = inputs.numerics_stress(dtype, rows=4096, n_twins=64, n_each_neginf=8)
+    src, dst = b.twin_pairs[:, 0], b.twin_pairs[:, 1]
+    z_src = oce.decode(b.logits[src], dtype)
+    z_dst = oce.decode(b.logits[dst], dtype)
+    l1, _, ls1 = oce.forward(z_src, b.targets[src])
+    l2, _, ls2 = oce.forward(z_dst, b.targets[dst])
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(ls1, ls2, rtol=0, atol=1e-12)
+    d1 = oce.grad(z_src, b.targets[src], b.g[src])
+    d2 = oce.grad(z_dst, b.targets[dst], b.g[dst])
+    np.testing.assert_allclose(d1, d2, rtol=0, atol=1e-15)
+
+
+def test_stress_special_rows():
+    b = inputs.numerics_stress("f32", rows=4096, n_twins=64, n_each_neginf=8)
+    z = oce.decode(b.logits, "f32")
+    loss, _, _ = oce.forward(z, b.targets)
+    assert np.all(loss[b.kind == inputs.KIND_ONLY_TARGET] == 0.0)
+    assert np.all(loss[b.kind == inputs.KIND_TARGET_NEGINF] == np.inf)
+    np.testing.assert_allclose(loss[b.equal_rows], LOG2, atol=1e-15)
+    ok = np.isin(b.kind, [inputs.KIND_NORMAL, inputs.KIND_HALF_NEGINF, inputs.KIND_TWIN])
+    assert np.all(np.isfinite(loss[ok])) and np.all(loss[ok] >= 0)
+
+
+# --- brute force at 50 digits, without the max shift ------------------------
+
+def brute_row(zrow, y, g):
+    with mpmath.workdps(50):
+        e = [mpmath.exp(mpmath.mpf(float(v))) if np.isfinite(v) else mpmath.mpf(0) for v in zrow]
+        tot = mpmath.fsum(e)
+        loss = -mpmath.log(e[y] / tot) if e[y] != 0 else mpmath.inf
+        d = [g * (ej / tot - (1 if j == y else 0)) for j, ej in enumerate(e)]
+        return float(loss), [float(v) for v in d]
+
+
+def brute_rows(seed=7):
+    g = np.random.default_rng(seed)
+    rows = []
+    for V in (1, 2, 3, 5, 8, 17):
+        for kind in range(6):
+            z = g.standard_normal(V) * (1 + 10 * (kind == 1))
+            if kind == 2:
+                z += 1e36 * np.sign(g.standard_normal())
+                z = z.astype(np.float32).astype(np.float64)
+            if kind == 3:
+                z += 1e8
+            if kind == 4 and V > 1:
+                z[g.integers(0, V)] = -np.inf
+            if kind == 5:
+                z *= 40.0
+            y = int(g.integers(0, V))
+            if not np.isfinite(z[y]):
+                y = int(np.flatnonzero(np.isfinite(z))[0])
+            rows.append((z, y, float(g.uniform(-2, 2))))
+    return rows
+
+
+def test_bruteforce_mpmath():
+    for z, y, gg in brute_rows():
+        loss, m, ls = oce.forward(z[None, :], np.array([y]))
+        d = oce.grad(z[None, :], np.array([y]), np.array([gg]))
+        bl, bd = brute_row(z, y, gg)
+        assert abs(loss[0] - bl) <= 1e-14 * max(1.0, abs(bl)), (z, y, loss[0], bl)
+        np.testing.assert_allclose(d[0], bd, rtol=1e-13, atol=1e-15)
+
+
+def test_torch_float64_cross_entropy():
+    """PyTorch's float64 CPU cross_entropy and its autograd agree with the oracle."""
+    g = np.random.default_rng(11)
+    z = g.standard_normal((200, 301)) * 3.0
+    z[:50] += 1e8
+    z[50:60, :100] = -np.inf
+    y = g.integers(100, 301, size=200)
+    w = g.uniform(0.1, 2.0, size=200)
+    zt = torch.tensor(z, dtype=torch.float64, requires_grad=True)
+    lt = torch.nn.functional.cross_entropy(zt, torch.tensor(y), reduction="none")
+    (lt * torch.tensor(w)).sum().backward()
+    loss, _, _ = oce.forward(z, y)
+    np.testing.assert_allclose(loss, lt.detach().numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(oce.grad(z, y, w), zt.grad.numpy(), rtol=1e-12, atol=1e-15)
+
+
+def test_chunked_equals_whole():
+    b = inputs.normal_rows(1000, 9, "bf16", workload=92)
+    a = oce.forward_stored(b.logits, "bf16", b.targets, chunk=7)
+    w = oce.forward(oce.decode(b.logits, "bf16"), b.targets)
+    for u, v in zip(a, w):
+        np.testing.assert_array_equal(u, v)
+
+
+# --- storage formats --------------------------------------------------------
+
+def test_decode_bf16_bit_patterns():
+    bits = np.array([0x3F80, 0xC000, 0x4049, 0x7F80, 0xFF80, 0x0001, 0x8000, 0x7F7F], np.uint16)
+    v = oce.decode(bits, "bf16")
+    assert list(v[:5]) == [1.0, -2.0, 3.140625, np.inf, -np.inf]
+    assert v[5] == 2.0 ** -133 and v[6] == 0.0 and math.copysign(1, v[6]) < 0
+    assert v[7] == (2 - 2 ** -7) * 2.0 ** 127
+    assert np.isnan(oce.decode(np.array([0x7FC0], np.uint16), "bf16")[0])
+
+
+def test_bf16_encoder_rounds_to_nearest_even():
+    x = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -20, -0.0, np.inf,
+                  np.float32(3.4028235e38), 1e-40], np.float32)
+    bits = inputs.f32_to_bf16_bits(x)
+    assert list(bits[:6]) == [0x3F80, 0x3F80, 0x3F82, 0x3F81, 0x8000, 0x7F80]
+    assert bits[6] == 0x7F80  # the largest float32 rounds up to infinity
+    assert np.isnan(oce.decode(inputs.f32_to_bf16_bits(np.array([np.nan], np.float32)), "bf16")[0])
+    r = np.random.default_rng(3).standard_normal(100000).astype(np.float32) * 1e3
+    ref = torch.from_numpy(r).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(inputs.f32_to_bf16_bits(r), ref)
+
+
+# --- linear cross-entropy ---------------------------------------------------
+
+@pytest.mark.parametrize("V", [1, 127, 300, 151936])
+def test_lce_zero_weights_give_log_v(V):
+    N, D = 5, 8
+    H = inputs.f32_to_bf16_bits(np.random.default_rng(1).standard_normal((N, D)).astype(np.float32))
+    W = np.zeros((V, D), np.uint16)
+    y = (np.arange(N) * 7919) % V
+    loss, m, ls = olce.forward(H, W, y)
+    np.testing.assert_allclose(loss, math.log(V), rtol=1e-15, atol=1e-15)
+    assert np.all(m == 0.0)
+
+
+def lce_brute(Hb, Wb, y):
+    """Triple loop over n, v, d with exact sums, then the unshifted loss at 50 digits."""
+    H = oce.decode(Hb, "bf16").tolist()
+    W = oce.decode(Wb, "bf16").tolist()
+    out = []
+    for n, hrow in enumerate(H):
+        zs = [math.fsum(hrow[k] * wrow[k] for k in range(len(hrow))) for wrow in W]
+        with mpmath.workdps(50):
+            tot = mpmath.fsum(mpmath.exp(mpmath.mpf(z)) for z in zs)
+            out.append(float(mpmath.log(tot) - mpmath.mpf(zs[y[n]])))
+    return np.array(out)
+
+
+@pytest.mark.parametrize("N,D,V", [(16, 64, 1), (9, 40, 127), (16, 64, 300), (4, 24, 24)])
+def test_lce_bruteforce(N, D, V):
+    H, W, y = inputs.linear_ce(N, D, V, seed_stream=N + D + V, w_scale=0.7)
+    loss, _, _ = olce.forward(H, W, y, block=5)
+    np.testing.assert_allclose(loss, lce_brute(H, W, y), rtol=1e-12, atol=1e-12)
+
+
+def test_lce_row_subset():
+    H, W, y = inputs.linear_ce(40, 16, 50, seed_stream=3)
+    full, _, _ = olce.forward(H, W, y)
+    rows = np.array([39, 0, 17])
+    sub, _, _ = olce.forward(H, W, y, rows=rows)
+    np.testing.assert_array_equal(sub, full[rows])
+
+
+# --- planted mistakes: each must fail at least one pin ----------------------
+
+@contextlib.contextmanager
+def planted(module, name, fn):
+    old = getattr(module, name)
+    setattr(module, name, fn)
+    try:
+        yield
+    finally:
+        setattr(module, name, old)
+
+
+def fails(pin, *args):
+    try:
+        pin(*args)
+    except (AssertionError, FloatingPointError, ValueError, OverflowError):
+        return True
+    return False
+
+
+def test_planted_no_max_shift_is_caught():
+    def no_shift(z, m):
+        with np.errstate(over="ignore", invalid="ignore"):
+            return np.log(np.exp(z).sum(axis=1)) - m
+    with planted(oce, "row_log_sum", no_shift):
+        assert fails(pin_equal_logits)
+
+
+def test_planted_dropped_max_term_is_caught():
+    def fwd(z, y):
+        m = oce.row_max(z)
+        ls = oce.row_log_sum(z, m)
+        zy, _ = oce.target_logit(z, y)
+        return ls - zy, m, ls
+    with planted(oce, "forward", fwd):
+        assert fails(test_uniform_row, 8, 1e4)
+
+
+def test_planted_target_off_by_one_is_caught():
+    real = oce.target_logit
+
+    def shifted(z, y):
+        return real(z, (np.asarray(y) + 1) % z.shape[1])
+    with planted(oce, "target_logit", shifted):
+        assert fails(test_bruteforce_mpmath)
+
+
+def test_planted_gradient_sign_is_caught():
+    real = oce.grad
+    with planted(oce, "grad", lambda *a, **k: -real(*a, **k)):
+        assert fails(pin_equal_logits)
+
+
+def test_planted_transposed_weight_is_caught():
+    with planted(olce, "logits", lambda H, W: H @ W):
+        assert fails(test_lce_bruteforce, 4, 24, 24)
+
+
+def test_planted_dropped_vocab_tail_is_caught():
+    with planted(olce, "logits", lambda H, W: H @ W[: max(1, W.shape[0] - 64)].T):
+        assert fails(test_lce_zero_weights_give_log_v, 300)
