@@ -1,0 +1,181 @@
+/*
+ * ce_mi355x.h: C ABI of the MI355X (gfx950) fused softmax cross-entropy library.
+ *
+ * Three operations, each computed by hand-written HIP kernels in libce_mi355x.so:
+ *
+ *   ce_forward   per-row loss and log-sum-exp of a [rows, V] logits view
+ *   ce_vjp       dlogits = g_i * (softmax(z_i) - onehot(y_i)) from the saved log-sum-exp
+ *   lce_forward  per-row loss and log-sum-exp of H.W^T, streamed over vocabulary
+ *                tiles without materialising the N x V logits
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers to tensors are DEVICE pointers owned by the caller.  The library keeps
+ *   no pointer after a call returns and allocates no device memory: lce_forward's
+ *   only scratch is the caller's workspace.
+ * - Work is enqueued on `stream` (NULL = the default stream) and the call returns
+ *   without synchronising.  Outputs are valid once the stream has been synchronised.
+ * - Every argument is checked on the host before any launch.  A failed check returns
+ *   a negative ce_status and enqueues nothing.  n_rows == 0 (or N == 0) is a no-op
+ *   that returns CE_OK.  A failed launch returns CE_ERR_LAUNCH.  No C++ exception
+ *   crosses this boundary, and the library holds no mutable global state, so the
+ *   calls may be made from several host threads at once.
+ * - Rows are indexed with 64-bit integers end to end; no launch wraps a 32-bit
+ *   grid, however many rows there are.  (MLX PR #4776 "fast.cross_entropy silently
+ *   skips rows when the Metal grid gets too large", Issue: a 32-bit grid of
+ *   rows x threads-per-row silently dropped rows past 2^32 threads.)
+ * - Targets are contiguous int32 [n_rows].  A target outside [0, V) never causes an
+ *   out-of-bounds read: that row's loss, and its dlogits row, are written as NaN.
+ *   There is no ignore_index.
+ * - Only per-row outputs are produced; a mean or sum over rows is the caller's.
+ */
+#ifndef CE_MI355X_H
+#define CE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of logits and dlogits (fp16 and bf16 are IEEE binary16 and bfloat16). */
+typedef enum { CE_F32 = 0, CE_F16 = 1, CE_BF16 = 2 } ce_dtype;
+
+/*
+ * Strided [batches x rows_per_batch x V] view of logits, in ELEMENTS.
+ * Logical row r (0 <= r < n_rows) starts at
+ *     base + (r / rows_per_batch) * batch_stride + (r % rows_per_batch) * row_stride
+ * and its V columns are contiguous (column stride 1).  A plain contiguous [n_rows, V]
+ * tensor is {rows_per_batch = n_rows, row_stride = V, batch_stride = n_rows * V}.
+ * The slice x[:, :-1] of a contiguous [B, L, V] tensor is
+ * {rows_per_batch = L - 1, row_stride = V, batch_stride = L * V} with n_rows = B * (L - 1).
+ * Views are read in place: the library never copies a view to a temporary.
+ * (MLX issue #4686 "fast.cross_entropy VJP returns wrong gradients for large
+ * non-contiguous inputs on Metal", Describe the bug: the gradient of the
+ * next-token loss over the view logits[:, :-1] came back wrong when the view was
+ * copied into a temporary whose buffer the output shared.)
+ * Requirements: rows_per_batch >= 1, row_stride >= V, batch_stride >= 0, and the
+ * base pointer aligned to the element size.
+ */
+typedef struct {
+    int64_t rows_per_batch;
+    int64_t row_stride;
+    int64_t batch_stride;
+} ce_layout;
+
+typedef enum {
+    CE_OK = 0,
+    CE_ERR_NULL = -1,      /* a required pointer is NULL                                   */
+    CE_ERR_SHAPE = -2,     /* n_rows < 0, V < 1, D < 1, V or D out of supported range      */
+    CE_ERR_DTYPE = -3,     /* dtype is not a ce_dtype                                      */
+    CE_ERR_LAYOUT = -4,    /* bad strides, or a pointer not aligned as required            */
+    CE_ERR_WORKSPACE = -5, /* lce workspace NULL or smaller than lce_workspace_size()      */
+    CE_ERR_LAUNCH = -6,    /* the HIP runtime rejected a kernel launch                     */
+    CE_ERR_ALIAS = -7,     /* an output overlaps an input it may not overlap               */
+    CE_ERR_DEVICE = -8     /* no usable HIP device, or the device is not gfx950            */
+} ce_status;
+
+/*
+ * ce_forward: loss_i = logsumexp(z_i) - z_{i, y_i} for each row of a logits view.
+ *
+ * Source: Ineshin, "A fused linear cross-entropy forward kernel for Apple GPUs",
+ * section 1 (the loss needs only the row's log-sum-exp and target logit; the
+ * online log-sum-exp keeps a running maximum m and a sum s rescaled to it).  MLX PR
+ * #4188 "Shift by the max in cross_entropy", Proposed changes: the row maximum is
+ * taken out before the target score is subtracted, so the loss is assembled as
+ * (m - z_y) + log s and two equal logits give log 2 at any magnitude.
+ *
+ *   logits  [n_rows rows of V] of dtype `dt`, addressed through `in`.
+ *   targets int32 [n_rows], contiguous.
+ *   loss    float32 [n_rows], contiguous (written).
+ *   lse     float32 [n_rows][2], contiguous, 8-byte aligned (written): lse[i][0] = m_i,
+ *           the row maximum (a stored logit, exactly), and lse[i][1] = log s_i with
+ *           s_i = sum_j exp(z_ij - m_i).  The log-sum-exp is lse[i][0] + lse[i][1].
+ *           Keeping the pair lets ce_vjp form exp((z - m) - log s) without the
+ *           cancellation that a single float32 lse suffers at large magnitudes.
+ * Accumulation is float32 whatever dt is.  Rows holding only -inf, or any +inf or
+ * NaN, give a NaN loss.  -inf entries carry zero probability.
+ * Outputs must not overlap the logits, the targets or each other (CE_ERR_ALIAS).
+ */
+ce_status ce_forward(const void* logits, ce_layout in, ce_dtype dt, const int32_t* targets,
+                     int64_t n_rows, int64_t V, float* loss, float* lse, hipStream_t stream);
+
+/*
+ * ce_forward_lanes: ce_forward with the row-to-lane mapping chosen by the caller.
+ * lanes_per_row = 0 picks the mapping from V and dt exactly as ce_forward does.
+ * A power of two in [1, 1024] assigns that many lanes to each row (up to 64 lanes:
+ * 64 / lanes rows per wavefront; above 64: one row per workgroup of that many
+ * threads, combined through LDS).  -1 asks for the one-lane-per-row path for
+ * short aligned rows and fails with CE_ERR_LAYOUT where that path does not apply.
+ * Results agree with ce_forward up to float32 summation order.  Intended for tests
+ * and tuning; any other value returns CE_ERR_SHAPE.
+ */
+ce_status ce_forward_lanes(const void* logits, ce_layout in, ce_dtype dt, const int32_t* targets,
+                           int64_t n_rows, int64_t V, float* loss, float* lse,
+                           int32_t lanes_per_row, hipStream_t stream);
+
+/*
+ * ce_vjp: dlogits_ij = g_i * (exp((z_ij - m_i) - log s_i) - [j == y_i]).
+ *
+ * The vector-Jacobian product of ce_forward's per-row loss with upstream gradient g.
+ * Source: Ineshin (above), section 1: the backward reuses the log-sum-exp saved by
+ * the forward; MLX issue #4686 (above) for the strided-view case.
+ *
+ *   logits  as in ce_forward (same view, same dt).
+ *   targets int32 [n_rows]; lse float32 [n_rows][2] as written by ce_forward;
+ *   g       float32 [n_rows], contiguous.
+ *   dlogits [n_rows rows of V] of dtype `dt`, addressed through `out` (written).
+ *           Values are computed in float32 and rounded to dt to nearest, ties to even.
+ * dlogits may be the logits themselves (an in-place VJP) only with an identical
+ * layout; otherwise it must not overlap the logits, targets, lse or g (CE_ERR_ALIAS).
+ * The output is always the caller's buffer: no library temporary is ever shared
+ * with it.
+ */
+ce_status ce_vjp(const void* logits, ce_layout in, ce_dtype dt, const int32_t* targets,
+                 const float* lse, const float* g, int64_t n_rows, int64_t V, void* dlogits,
+                 ce_layout out, hipStream_t stream);
+
+/* ce_vjp_lanes: ce_vjp with lanes_per_row chosen as in ce_forward_lanes. */
+ce_status ce_vjp_lanes(const void* logits, ce_layout in, ce_dtype dt, const int32_t* targets,
+                       const float* lse, const float* g, int64_t n_rows, int64_t V, void* dlogits,
+                       ce_layout out, int32_t lanes_per_row, hipStream_t stream);
+
+/*
+ * lce_workspace_size: bytes of device workspace lce_forward needs for (N, D, V).
+ * Returns 0 for arguments lce_forward would reject.
+ */
+size_t lce_workspace_size(int64_t N, int64_t D, int64_t V);
+
+/*
+ * lce_forward: per-row loss and log-sum-exp of Z = H.W^T without materialising Z.
+ *
+ * Source: Ineshin (above), section 1: for each vocabulary tile the kernel merges the
+ * tile into the running (m, s) of every row, m' = max(m, m_t),
+ * s' = s * exp(m - m') + sum_j exp(z_j - m'), and captures z_{i, y_i} when y_i falls
+ * in the tile; after the last tile the log-sum-exp is m + log s.
+ *
+ *   H        bf16 [N][D], row-major, contiguous, 16-byte aligned.
+ *   W        bf16 [V][D], row-major, contiguous, 16-byte aligned.
+ *   targets  int32 [N].
+ *   loss     float32 [N] (written); lse float32 [N][2] as in ce_forward (written).
+ *   workspace, workspace_bytes: device scratch of at least lce_workspace_size(N, D, V)
+ *            bytes, 256-byte aligned; its contents on entry are ignored.
+ * The product accumulates in float32 on the matrix cores (bf16 in, fp32 out).  The
+ * target logit is taken from the same float32 accumulator that feeds (m, s).
+ * Requires D % 8 == 0 (16-byte rows) and V < 2^31; N may be any non-negative size.
+ */
+ce_status lce_forward(const void* H, const void* W, const int32_t* targets, int64_t N, int64_t D,
+                      int64_t V, float* loss, float* lse, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* ce_status_string(ce_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CE_MI355X_H */

@@ -1,0 +1,176 @@
+"""ctypes binding for libce_mi355x.so (include/ce_mi355x.h).
+
+Argument marshalling only: it reads device pointers, shapes and strides from torch
+tensors, allocates output tensors with torch, passes the current HIP stream, and
+raises CEError on a negative status.  Every step of the computation runs in the
+library's HIP kernels; there is no fallback of any kind, and a missing library is
+an error.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libce_mi355x.so")
+
+CE_F32, CE_F16, CE_BF16 = 0, 1, 2
+DTYPE_CODE = {torch.float32: CE_F32, torch.float16: CE_F16, torch.bfloat16: CE_BF16}
+
+STATUS = {
+    0: "CE_OK", -1: "CE_ERR_NULL", -2: "CE_ERR_SHAPE", -3: "CE_ERR_DTYPE", -4: "CE_ERR_LAYOUT",
+    -5: "CE_ERR_WORKSPACE", -6: "CE_ERR_LAUNCH", -7: "CE_ERR_ALIAS", -8: "CE_ERR_DEVICE",
+}
+
+# every symbol include/ce_mi355x.h declares
+EXPORTS = ("ce_forward", "ce_forward_lanes", "ce_vjp", "ce_vjp_lanes", "lce_workspace_size",
+           "lce_forward", "ce_status_string")
+
+
+class CELayout(ctypes.Structure):
+    _fields_ = [("rows_per_batch", ctypes.c_int64), ("row_stride", ctypes.c_int64),
+                ("batch_stride", ctypes.c_int64)]
+
+
+class CEError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+_lib = None
+
+_vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing; build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        L.ce_forward.argtypes = [_vp, CELayout, ctypes.c_int, _vp, _i64, _i64, _vp, _vp, _vp]
+        L.ce_forward_lanes.argtypes = [_vp, CELayout, ctypes.c_int, _vp, _i64, _i64, _vp, _vp, _i32, _vp]
+        L.ce_vjp.argtypes = [_vp, CELayout, ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _vp, CELayout, _vp]
+        L.ce_vjp_lanes.argtypes = [_vp, CELayout, ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _vp, CELayout,
+                                   _i32, _vp]
+        L.lce_workspace_size.argtypes = [_i64, _i64, _i64]
+        L.lce_workspace_size.restype = _sz
+        L.lce_forward.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _sz, _vp]
+        L.ce_status_string.argtypes = [ctypes.c_int]
+        L.ce_status_string.restype = ctypes.c_char_p
+        for name in ("ce_forward", "ce_forward_lanes", "ce_vjp", "ce_vjp_lanes", "lce_forward"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().ce_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise CEError(status, where)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def rows_layout(t: torch.Tensor) -> tuple[CELayout, int, int]:
+    """(layout, n_rows, V) of a [rows, V] or [B, L, V] view with unit column stride."""
+    if t.dim() == 2:
+        R, V = t.shape
+        rs = t.stride(0)
+        return CELayout(max(R, 1), rs, rs * max(R, 1)), R, V
+    if t.dim() == 3:
+        B, L, V = t.shape
+        return CELayout(max(L, 1), t.stride(1), t.stride(0)), B * L, V
+    raise ValueError("logits must be [rows, V] or [B, L, V]")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need(t, dtype, n, name):
+    if t.dtype != dtype or not t.is_contiguous() or t.numel() != n:
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of {n} elements")
+
+
+def ce_forward(logits: torch.Tensor, targets: torch.Tensor, loss=None, lse=None, lanes_per_row: int = 0):
+    """Per-row (loss [n], lse [n, 2]) of a [rows, V] or [B, L, V] logits view."""
+    if logits.stride(-1) != 1 and logits.shape[-1] > 1:
+        raise ValueError("logits need unit column stride")
+    lay, n, V = rows_layout(logits)
+    _need(targets, torch.int32, n, "targets")
+    if loss is None:
+        loss = torch.empty(n, dtype=torch.float32, device=logits.device)
+    if lse is None:
+        lse = torch.empty(n, 2, dtype=torch.float32, device=logits.device)
+    _need(loss, torch.float32, n, "loss")
+    _need(lse, torch.float32, 2 * n, "lse")
+    args = (_ptr(logits), lay, DTYPE_CODE[logits.dtype], _ptr(targets), n, V, _ptr(loss), _ptr(lse))
+    if lanes_per_row == 0:
+        st = lib().ce_forward(*args, _stream(logits))
+    else:
+        st = lib().ce_forward_lanes(*args, int(lanes_per_row), _stream(logits))
+    _check(st, "ce_forward")
+    return loss, lse
+
+
+def ce_vjp(logits: torch.Tensor, targets: torch.Tensor, lse: torch.Tensor, g: torch.Tensor, dlogits=None,
+           lanes_per_row: int = 0):
+    """dlogits = g * (softmax(logits) - onehot(targets)) from the saved lse; same shape as logits."""
+    if logits.stride(-1) != 1 and logits.shape[-1] > 1:
+        raise ValueError("logits need unit column stride")
+    lay, n, V = rows_layout(logits)
+    _need(targets, torch.int32, n, "targets")
+    _need(lse, torch.float32, 2 * n, "lse")
+    _need(g, torch.float32, n, "g")
+    if dlogits is None:
+        dlogits = torch.empty(logits.shape, dtype=logits.dtype, device=logits.device)
+    if dlogits.dtype != logits.dtype or dlogits.shape != logits.shape:
+        raise ValueError("dlogits must match logits in dtype and shape")
+    if dlogits.stride(-1) != 1 and V > 1:
+        raise ValueError("dlogits need unit column stride")
+    olay, _, _ = rows_layout(dlogits)
+    args = (_ptr(logits), lay, DTYPE_CODE[logits.dtype], _ptr(targets), _ptr(lse), _ptr(g), n, V, _ptr(dlogits),
+            olay)
+    if lanes_per_row == 0:
+        st = lib().ce_vjp(*args, _stream(logits))
+    else:
+        st = lib().ce_vjp_lanes(*args, int(lanes_per_row), _stream(logits))
+    _check(st, "ce_vjp")
+    return dlogits
+
+
+def lce_workspace_size(N: int, D: int, V: int) -> int:
+    return int(lib().lce_workspace_size(N, D, V))
+
+
+def lce_forward(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, loss=None, lse=None, workspace=None):
+    """Per-row (loss [N], lse [N, 2]) of H.W^T for bf16 H [N, D] and W [V, D]."""
+    if H.dtype != torch.bfloat16 or W.dtype != torch.bfloat16 or H.dim() != 2 or W.dim() != 2:
+        raise ValueError("H and W must be 2-D bfloat16 tensors")
+    if not H.is_contiguous() or not W.is_contiguous() or H.shape[1] != W.shape[1]:
+        raise ValueError("H [N, D] and W [V, D] must be contiguous with the same D")
+    N, D = H.shape
+    V = W.shape[0]
+    _need(targets, torch.int32, N, "targets")
+    if loss is None:
+        loss = torch.empty(N, dtype=torch.float32, device=H.device)
+    if lse is None:
+        lse = torch.empty(N, 2, dtype=torch.float32, device=H.device)
+    need = lce_workspace_size(N, D, V)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=H.device)
+    st = lib().lce_forward(_ptr(H), _ptr(W), _ptr(targets), N, D, V, _ptr(loss), _ptr(lse), _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _stream(H))
+    _check(st, "lce_forward")
+    return loss, lse

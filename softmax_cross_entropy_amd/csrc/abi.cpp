@@ -1,0 +1,291 @@
+// C ABI of libce_mi355x: argument validation, row-to-lane planning and dispatch.
+// Every check runs on the host before anything is enqueued; a failed check returns
+// a negative ce_status and touches no device state.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "ce_mi355x.h"
+#include "launch.h"
+
+namespace {
+
+using ce::Dt;
+using ce::HostLayout;
+using ce::Plan;
+
+constexpr int kMaxDevices = 64;
+constexpr int64_t kMaxV = 0x7fffffff;  // targets are int32
+
+// Per-device CU count, 0 = not looked up yet, -1 = not a gfx950 device.  Racing
+// first calls store the same value, so plain relaxed atomics suffice.
+std::atomic<int> g_cus[kMaxDevices];
+
+ce_status device_cus(int* cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CE_ERR_DEVICE;
+    int v = g_cus[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return CE_ERR_DEVICE;
+        v = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? prop.multiProcessorCount : -1;
+        if (v == 0) v = -1;
+        g_cus[dev].store(v, std::memory_order_relaxed);
+    }
+    if (v < 0) return CE_ERR_DEVICE;
+    *cus = v;
+    return CE_OK;
+}
+
+int esize(ce_dtype dt) { return dt == CE_F32 ? 4 : 2; }
+
+bool valid_dtype(int dt) { return dt == CE_F32 || dt == CE_F16 || dt == CE_BF16; }
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Byte range [lo, hi) covered by n_rows rows of V elements under layout L.
+struct Extent {
+    uintptr_t lo, hi;
+};
+
+int64_t row_off(const ce_layout& L, int64_t r) {
+    const int64_t b = r / L.rows_per_batch;
+    return b * L.batch_stride + (r - b * L.rows_per_batch) * L.row_stride;
+}
+
+Extent view_extent(const void* base, const ce_layout& L, int64_t n_rows, int64_t V, int es) {
+    // offsets grow with the row index inside a batch and with the batch index, so the
+    // furthest row is the last row, or the last row of the last full batch
+    int64_t far = row_off(L, n_rows - 1);
+    const int64_t last_b = (n_rows - 1) / L.rows_per_batch;
+    if (last_b >= 1) {
+        const int64_t r = last_b * L.rows_per_batch - 1;
+        const int64_t o = row_off(L, r);
+        if (o > far) far = o;
+    }
+    const uintptr_t lo = (uintptr_t)base;
+    return Extent{lo, lo + (uintptr_t)((far + V) * es)};
+}
+
+Extent flat_extent(const void* p, int64_t bytes) {
+    return Extent{(uintptr_t)p, (uintptr_t)p + (uintptr_t)bytes};
+}
+
+bool overlaps(Extent a, Extent b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Strides are in elements.  Inputs may use any non-negative strides (rows may even
+// repeat); outputs must give every row its own V elements.
+bool layout_ok(const ce_layout& L, int64_t n_rows, int64_t V, bool output) {
+    if (L.rows_per_batch < 1 || L.row_stride < 0 || L.batch_stride < 0) return false;
+    // byte offsets must fit comfortably in 63 bits
+    const double far = (double)L.batch_stride * (double)((n_rows - 1) / L.rows_per_batch + 1) +
+                       (double)L.row_stride * (double)L.rows_per_batch + (double)V;
+    if (far > 1.0e18) return false;
+    if (!output) return true;
+    if (L.row_stride < V && n_rows > 1) return false;
+    if (n_rows > L.rows_per_batch &&
+        L.batch_stride < (L.rows_per_batch - 1) * L.row_stride + V)
+        return false;
+    return true;
+}
+
+HostLayout host_layout(const ce_layout& L, int64_t n_rows) {
+    const bool uniform = n_rows <= L.rows_per_batch || L.batch_stride == L.rows_per_batch * L.row_stride;
+    return HostLayout{L.rows_per_batch, L.row_stride, L.batch_stride, uniform ? 1 : 0};
+}
+
+bool rows_aligned16(const void* base, const ce_layout& L, int64_t n_rows, int es) {
+    if (!aligned(base, 16)) return false;
+    if ((L.row_stride * es) % 16 != 0) return false;
+    if (n_rows > L.rows_per_batch && (L.batch_stride * es) % 16 != 0) return false;
+    return true;
+}
+
+int pow2_ceil(int64_t x) {
+    int p = 1;
+    while (p < x && p < 1024) p <<= 1;
+    return p;
+}
+
+int narrow_rows_per_thread(int nv) { return nv == 1 ? 4 : nv == 2 ? 2 : 1; }
+
+// Picks the row-to-lane mapping and the (capped) grid.  The grid never needs to
+// cover every row: all kernels loop over 64-bit row indices.
+ce_status make_plan(bool narrow_ok, int64_t V, int es, int64_t n_rows, int32_t lanes_req, bool vjp,
+                    int cus, Plan* plan) {
+    const int vec = 16 / es;
+    const int64_t nvec = (V + vec - 1) / vec;
+    Plan p{0, 0, 0};
+    if (lanes_req == -1) {
+        if (!narrow_ok) return CE_ERR_LAYOUT;
+        p.narrow_nv = (int)(V / vec);
+    } else if (lanes_req == 0) {
+        if (narrow_ok)
+            p.narrow_nv = (int)(V / vec);
+        else
+            p.lanes = pow2_ceil((nvec + 7) / 8);  // about 8 vectors per lane
+    } else {
+        if (lanes_req < 1 || lanes_req > 1024 || (lanes_req & (lanes_req - 1)) != 0) return CE_ERR_SHAPE;
+        p.lanes = lanes_req;
+    }
+    int64_t per_block, threads;
+    if (p.narrow_nv > 0) {
+        threads = 256;
+        per_block = 256 * narrow_rows_per_thread(p.narrow_nv);
+    } else if (!vjp && p.lanes > 64) {
+        threads = p.lanes;
+        per_block = 1;
+    } else {
+        threads = p.lanes > 256 ? p.lanes : 256;
+        per_block = threads / p.lanes;
+    }
+    const int64_t needed = (n_rows + per_block - 1) / per_block;
+    const int64_t resident = (int64_t)cus * (2048 / threads);
+    const int64_t cap = resident * 4;
+    p.blocks = needed < cap ? needed : cap;
+    if (p.blocks < 1) p.blocks = 1;
+    *plan = p;
+    return CE_OK;
+}
+
+ce_status from_hip(hipError_t e) { return e == hipSuccess ? CE_OK : CE_ERR_LAUNCH; }
+
+ce_status forward_impl(const void* logits, ce_layout in, ce_dtype dt, const int32_t* targets,
+                       int64_t n_rows, int64_t V, float* loss, float* lse, int32_t lanes,
+                       hipStream_t stream) {
+    if (!valid_dtype((int)dt)) return CE_ERR_DTYPE;
+    if (n_rows < 0 || V < 1 || V > kMaxV) return CE_ERR_SHAPE;
+    if (lanes != 0 && lanes != -1 && (lanes < 1 || lanes > 1024 || (lanes & (lanes - 1)) != 0))
+        return CE_ERR_SHAPE;
+    if (n_rows == 0) return CE_OK;
+    if (!logits || !targets || !loss || !lse) return CE_ERR_NULL;
+    const int es = esize(dt);
+    if (!layout_ok(in, n_rows, V, false) || !aligned(logits, es) || !aligned(targets, 4) ||
+        !aligned(loss, 4) || !aligned(lse, 8))
+        return CE_ERR_LAYOUT;
+    const Extent ex_in = view_extent(logits, in, n_rows, V, es);
+    const Extent ex_t = flat_extent(targets, n_rows * 4);
+    const Extent ex_loss = flat_extent(loss, n_rows * 4);
+    const Extent ex_lse = flat_extent(lse, n_rows * 8);
+    if (overlaps(ex_loss, ex_in) || overlaps(ex_loss, ex_t) || overlaps(ex_lse, ex_in) ||
+        overlaps(ex_lse, ex_t) || overlaps(ex_loss, ex_lse))
+        return CE_ERR_ALIAS;
+    int cus = 0;
+    if (ce_status s = device_cus(&cus)) return s;
+    const bool narrow_ok = rows_aligned16(logits, in, n_rows, es) && V % (16 / es) == 0 &&
+                           (V / (16 / es) == 1 || V / (16 / es) == 2 || V / (16 / es) == 4 ||
+                            V / (16 / es) == 8);
+    Plan plan;
+    if (ce_status s = make_plan(narrow_ok, V, es, n_rows, lanes, false, cus, &plan)) return s;
+    ce::FwdCall c{logits, host_layout(in, n_rows), (Dt)dt, targets, n_rows, V, loss, lse, plan, stream};
+    return from_hip(ce::launch_ce_forward(c));
+}
+
+bool same_layout(const ce_layout& a, const ce_layout& b, int64_t n_rows) {
+    if (a.row_stride != b.row_stride) return false;
+    if (n_rows <= a.rows_per_batch && n_rows <= b.rows_per_batch) return true;
+    return a.rows_per_batch == b.rows_per_batch && a.batch_stride == b.batch_stride;
+}
+
+ce_status vjp_impl(const void* logits, ce_layout in, ce_dtype dt, const int32_t* targets,
+                   const float* lse, const float* g, int64_t n_rows, int64_t V, void* dlogits,
+                   ce_layout out, int32_t lanes, hipStream_t stream) {
+    if (!valid_dtype((int)dt)) return CE_ERR_DTYPE;
+    if (n_rows < 0 || V < 1 || V > kMaxV) return CE_ERR_SHAPE;
+    if (lanes != 0 && lanes != -1 && (lanes < 1 || lanes > 1024 || (lanes & (lanes - 1)) != 0))
+        return CE_ERR_SHAPE;
+    if (n_rows == 0) return CE_OK;
+    if (!logits || !targets || !lse || !g || !dlogits) return CE_ERR_NULL;
+    const int es = esize(dt);
+    if (!layout_ok(in, n_rows, V, false) || !layout_ok(out, n_rows, V, true) || !aligned(logits, es) ||
+        !aligned(dlogits, es) || !aligned(targets, 4) || !aligned(lse, 8) || !aligned(g, 4))
+        return CE_ERR_LAYOUT;
+    const Extent ex_in = view_extent(logits, in, n_rows, V, es);
+    const Extent ex_out = view_extent(dlogits, out, n_rows, V, es);
+    const bool in_place = logits == dlogits && same_layout(in, out, n_rows);
+    if (!in_place && overlaps(ex_in, ex_out)) return CE_ERR_ALIAS;
+    if (overlaps(ex_out, flat_extent(targets, n_rows * 4)) || overlaps(ex_out, flat_extent(lse, n_rows * 8)) ||
+        overlaps(ex_out, flat_extent(g, n_rows * 4)))
+        return CE_ERR_ALIAS;
+    int cus = 0;
+    if (ce_status s = device_cus(&cus)) return s;
+    const int vec = 16 / es;
+    const bool narrow_ok = rows_aligned16(logits, in, n_rows, es) && rows_aligned16(dlogits, out, n_rows, es) &&
+                           V % vec == 0 && (V / vec == 1 || V / vec == 2 || V / vec == 4 || V / vec == 8);
+    Plan plan;
+    if (ce_status s = make_plan(narrow_ok, V, es, n_rows, lanes, true, cus, &plan)) return s;
+    ce::VjpCall c{logits, host_layout(in, n_rows), (Dt)dt, targets, lse, g, n_rows, V, dlogits,
+                  host_layout(out, n_rows), plan, stream};
+    return from_hip(ce::launch_ce_vjp(c));
+}
+
+}  // namespace
+
+extern "C" {
+
+ce_status ce_forward(const void* logits, ce_layout in, ce_dtype dt, const int32_t* targets, int64_t n_rows,
+                     int64_t V, float* loss, float* lse, hipStream_t stream) {
+    return forward_impl(logits, in, dt, targets, n_rows, V, loss, lse, 0, stream);
+}
+
+ce_status ce_forward_lanes(const void* logits, ce_layout in, ce_dtype dt, const int32_t* targets,
+                           int64_t n_rows, int64_t V, float* loss, float* lse, int32_t lanes_per_row,
+                           hipStream_t stream) {
+    return forward_impl(logits, in, dt, targets, n_rows, V, loss, lse, lanes_per_row, stream);
+}
+
+ce_status ce_vjp(const void* logits, ce_layout in, ce_dtype dt, const int32_t* targets, const float* lse,
+                 const float* g, int64_t n_rows, int64_t V, void* dlogits, ce_layout out, hipStream_t stream) {
+    return vjp_impl(logits, in, dt, targets, lse, g, n_rows, V, dlogits, out, 0, stream);
+}
+
+ce_status ce_vjp_lanes(const void* logits, ce_layout in, ce_dtype dt, const int32_t* targets, const float* lse,
+                       const float* g, int64_t n_rows, int64_t V, void* dlogits, ce_layout out,
+                       int32_t lanes_per_row, hipStream_t stream) {
+    return vjp_impl(logits, in, dt, targets, lse, g, n_rows, V, dlogits, out, lanes_per_row, stream);
+}
+
+size_t lce_workspace_size(int64_t N, int64_t D, int64_t V) {
+    if (N < 0 || D < 1 || D % 8 != 0 || V < 1 || V > kMaxV) return 0;
+    return ce::lce_workspace_bytes(N, D, V);
+}
+
+ce_status lce_forward(const void* H, const void* W, const int32_t* targets, int64_t N, int64_t D, int64_t V,
+                      float* loss, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (N < 0 || D < 1 || D % 8 != 0 || V < 1 || V > kMaxV || D > (int64_t)1 << 24) return CE_ERR_SHAPE;
+    if (N == 0) return CE_OK;
+    if (!H || !W || !targets || !loss || !lse) return CE_ERR_NULL;
+    if (!workspace || workspace_bytes < ce::lce_workspace_bytes(N, D, V)) return CE_ERR_WORKSPACE;
+    if (!aligned(H, 16) || !aligned(W, 16) || !aligned(targets, 4) || !aligned(loss, 4) || !aligned(lse, 8) ||
+        !aligned(workspace, 256))
+        return CE_ERR_LAYOUT;
+    const Extent ex_loss = flat_extent(loss, N * 4);
+    const Extent ex_lse = flat_extent(lse, N * 8);
+    const Extent ex_ws = flat_extent(workspace, (int64_t)ce::lce_workspace_bytes(N, D, V));
+    const Extent ins[3] = {flat_extent(H, N * D * 2), flat_extent(W, V * D * 2), flat_extent(targets, N * 4)};
+    for (const Extent& e : ins)
+        if (overlaps(ex_loss, e) || overlaps(ex_lse, e) || overlaps(ex_ws, e)) return CE_ERR_ALIAS;
+    if (overlaps(ex_loss, ex_lse) || overlaps(ex_loss, ex_ws) || overlaps(ex_lse, ex_ws)) return CE_ERR_ALIAS;
+    int cus = 0;
+    if (ce_status s = device_cus(&cus)) return s;
+    ce::LceCall c{H, W, targets, N, D, V, loss, lse, workspace, cus, stream};
+    return from_hip(ce::launch_lce_forward(c));
+}
+
+const char* ce_status_string(ce_status s) {
+    switch (s) {
+        case CE_OK: return "CE_OK: success";
+        case CE_ERR_NULL: return "CE_ERR_NULL: a required pointer is NULL";
+        case CE_ERR_SHAPE: return "CE_ERR_SHAPE: a size or lane count is out of range";
+        case CE_ERR_DTYPE: return "CE_ERR_DTYPE: unknown element type";
+        case CE_ERR_LAYOUT: return "CE_ERR_LAYOUT: bad strides or misaligned pointer";
+        case CE_ERR_WORKSPACE: return "CE_ERR_WORKSPACE: workspace missing or too small";
+        case CE_ERR_LAUNCH: return "CE_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
+        case CE_ERR_ALIAS: return "CE_ERR_ALIAS: an output overlaps an input";
+        case CE_ERR_DEVICE: return "CE_ERR_DEVICE: no gfx950 HIP device is current";
+    }
+    return "unknown ce_status";
+}
+
+}  // extern "C"

@@ -1,0 +1,403 @@
+// Softmax cross-entropy forward and vector-Jacobian product for gfx950.
+//
+// Forward (per row z, target y):  m = max_j z_j,  s = sum_j exp(z_j - m),
+//   loss = (m - z_y) + log s,  lse = (m, log s).
+//   Ineshin, "A fused linear cross-entropy forward kernel for Apple GPUs", section 1
+//   (loss from the log-sum-exp and the target logit; online (m, s) update); MLX PR
+//   #4188 "Shift by the max in cross_entropy", Proposed changes (the max is taken
+//   out before the target score, so the gap between logits survives at any
+//   magnitude).
+// VJP:  dlogits_j = g * (exp((z_j - m) - log s) - [j == y]), from the saved pair.
+//
+// Three row layouts, all HBM streaming with 16-byte loads coalesced across lanes:
+//   * narrow: rows of 1, 2, 4 or 8 aligned vectors; one lane per row and several
+//     rows per lane in flight (the 1,048,576 x 8 fp32 shape is 2 vectors per row);
+//   * lanes:  G lanes per row (G <= 64), 64 / G rows per wavefront, online state
+//     per lane, then a butterfly merge of (m, s) pairs across the G lanes;
+//   * rowwg:  one workgroup of 64 * NW threads per row for long rows, per-wave
+//     butterfly merge, then one exchange of (m, s) pairs through LDS.
+// Every row loop is a grid-stride loop over 64-bit row indices, so the launch grid
+// never has to cover all rows (MLX PR #4776 "fast.cross_entropy silently skips
+// rows when the Metal grid gets too large", Issue).
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace ce {
+namespace {
+
+constexpr int kBlock = 256;
+
+struct FwdArgs {
+    const void* logits;
+    RowLayout in;
+    const int32_t* targets;
+    int64_t n_rows;
+    int64_t V;
+    float* loss;
+    float2* lse;
+};
+
+struct VjpArgs {
+    const void* logits;
+    RowLayout in;
+    const int32_t* targets;
+    const float2* lse;
+    const float* g;
+    int64_t n_rows;
+    int64_t V;
+    void* dlogits;
+    RowLayout out;
+};
+
+__device__ __forceinline__ bool target_ok(int32_t y, int64_t V) { return y >= 0 && (int64_t)y < V; }
+
+__device__ __forceinline__ void store_forward(const FwdArgs& a, int64_t r, MS st, float zy, bool ok) {
+    float ls = log_e(st.s);
+    a.loss[r] = ok ? (st.m - zy) + ls : __builtin_nanf("");
+    a.lse[r] = make_float2(st.m, ls);
+}
+
+// Streams this lane's share of one row into `st`: vectors lane, lane + G, ... (U
+// vectors per step, all loads issued before any arithmetic), then the scalar head
+// and tail elements.
+template <typename T, int G, int U>
+__device__ __forceinline__ void stream_row(const T* row, int64_t V, int lane, MS& st) {
+    constexpr int kVec = Elem<T>::kVec;
+    RowSplit<T> sp(row, V);
+    const char* vb = reinterpret_cast<const char*>(row + sp.head);
+    int64_t j = lane;
+    for (; j + (int64_t)(U - 1) * G < sp.nvec; j += (int64_t)U * G) {
+        U4 buf[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) buf[u] = load_u4(vb + (j + (int64_t)u * G) * 16);
+        float f[U * kVec];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float t[kVec];
+            Elem<T>::unpack(buf[u], t);
+#pragma unroll
+            for (int k = 0; k < kVec; ++k) f[u * kVec + k] = t[k];
+        }
+        ms_add<U * kVec>(st, f);
+    }
+    for (; j < sp.nvec; j += G) {
+        float f[kVec];
+        Elem<T>::unpack(load_u4(vb + j * 16), f);
+        ms_add<kVec>(st, f);
+    }
+    const int64_t ns = sp.n_scalar(V);
+    for (int64_t k = lane; k < ns; k += G) ms_add1(st, Elem<T>::load1(row + sp.scalar_index(k)));
+}
+
+// ---- forward: one lane per short aligned row ------------------------------------
+
+template <typename T, int NV, int UR>
+__global__ __launch_bounds__(kBlock) void ce_fwd_narrow(FwdArgs a) {
+    constexpr int kVec = Elem<T>::kVec;
+    constexpr int kN = NV * kVec;
+    const int64_t nthreads = (int64_t)gridDim.x * kBlock;
+    const T* base = static_cast<const T*>(a.logits);
+    for (int64_t r0 = (int64_t)blockIdx.x * kBlock + threadIdx.x; r0 < a.n_rows; r0 += nthreads * UR) {
+        U4 buf[UR][NV];
+        int32_t ys[UR];
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+            const int64_t r = r0 + u * nthreads;
+            if (r < a.n_rows) {
+                const char* row = reinterpret_cast<const char*>(base + row_offset(r, a.in));
+#pragma unroll
+                for (int v = 0; v < NV; ++v) buf[u][v] = load_u4(row + v * 16);
+                ys[u] = a.targets[r];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+            const int64_t r = r0 + u * nthreads;
+            if (r < a.n_rows) {
+                float f[kN];
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    float t[kVec];
+                    Elem<T>::unpack(buf[u][v], t);
+#pragma unroll
+                    for (int k = 0; k < kVec; ++k) f[v * kVec + k] = t[k];
+                }
+                MS st = ms_empty();
+                ms_add<kN>(st, f);
+                // the target logit is already in registers
+                const int32_t y = ys[u];
+                float zy = 0.0f;
+#pragma unroll
+                for (int k = 0; k < kN; ++k) zy = (y == k) ? f[k] : zy;
+                store_forward(a, r, st, zy, target_ok(y, kN));
+            }
+        }
+    }
+}
+
+// ---- forward: G lanes per row, 64 / G rows per wavefront -------------------------
+
+template <typename T, int G, int U>
+__global__ __launch_bounds__(kBlock) void ce_fwd_lanes(FwdArgs a) {
+    constexpr int kRowsPerBlock = kBlock / G;
+    const int lane = threadIdx.x % G;
+    const int64_t stride = (int64_t)gridDim.x * kRowsPerBlock;
+    for (int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / G; r < a.n_rows; r += stride) {
+        const T* row = static_cast<const T*>(a.logits) + row_offset(r, a.in);
+        const int32_t y = a.targets[r];
+        const bool ok = target_ok(y, a.V);
+        float zy = 0.0f;
+        if (lane == 0 && ok) zy = Elem<T>::load1(row + y);
+        MS st = ms_empty();
+        stream_row<T, G, U>(row, a.V, lane, st);
+        st = ms_group_reduce<G>(st);
+        if (lane == 0) store_forward(a, r, st, zy, ok);
+    }
+}
+
+// ---- forward: one workgroup of 64 * NW threads per row ---------------------------
+
+template <typename T, int NW, int U>
+__global__ __launch_bounds__(64 * NW) void ce_fwd_rowwg(FwdArgs a) {
+    constexpr int G = 64 * NW;
+    // One (m, s) slot per wave.  Each row is one exchange of pairs: lane 0 of every
+    // wave writes its slot, one barrier, then wave 0 reads all slots.  The slots
+    // alternate between two buffers from row to row, so a wave that races ahead to
+    // the next row writes the other buffer, and the barrier of that next row keeps
+    // it from reaching this buffer again before wave 0 has read it.  ("One barrier
+    // short", sections "Sixty-four floats" and "The fix": reusing one scratch slot
+    // for two exchanges without a barrier between them corrupted the row maximum.)
+    __shared__ MS slots[2][NW];
+    const int tid = threadIdx.x;
+    const int wave = tid / 64;
+    const int lane = tid % 64;
+    int parity = 0;
+    for (int64_t r = blockIdx.x; r < a.n_rows; r += gridDim.x, parity ^= 1) {
+        const T* row = static_cast<const T*>(a.logits) + row_offset(r, a.in);
+        const int32_t y = a.targets[r];
+        const bool ok = target_ok(y, a.V);
+        float zy = 0.0f;
+        if (tid == 0 && ok) zy = Elem<T>::load1(row + y);
+        MS st = ms_empty();
+        stream_row<T, G, U>(row, a.V, tid, st);
+        st = ms_group_reduce<64>(st);
+        if (lane == 0) slots[parity][wave] = st;
+        __syncthreads();
+        if (wave == 0) {
+            MS t = lane < NW ? slots[parity][lane] : ms_empty();
+            t = ms_group_reduce<NW>(t);
+            if (lane == 0) store_forward(a, r, t, zy, ok);
+        }
+    }
+}
+
+// ---- VJP ------------------------------------------------------------------------
+
+struct RowGrad {
+    float m;   // row maximum, or NaN for a row whose target is out of range
+    float ls;  // log of the scaled sum
+    float g;
+    int32_t y;
+};
+
+__device__ __forceinline__ RowGrad load_row_grad(const VjpArgs& a, int64_t r) {
+    RowGrad rg;
+    rg.y = a.targets[r];
+    const float2 l = a.lse[r];
+    rg.m = target_ok(rg.y, a.V) ? l.x : __builtin_nanf("");
+    rg.ls = l.y;
+    rg.g = a.g[r];
+    return rg;
+}
+
+__device__ __forceinline__ float grad_elem(float z, const RowGrad& rg, bool is_target) {
+    float p = exp_e((z - rg.m) - rg.ls);
+    return rg.g * (is_target ? p - 1.0f : p);
+}
+
+template <typename T, int N>
+__device__ __forceinline__ void grad_vec(float (&f)[N], const RowGrad& rg, int64_t first) {
+    const int64_t rel = (int64_t)rg.y - first;
+    const int yr = (rel >= 0 && rel < N) ? (int)rel : -1;
+#pragma unroll
+    for (int k = 0; k < N; ++k) f[k] = grad_elem(f[k], rg, k == yr);
+}
+
+template <typename T, int NV, int UR>
+__global__ __launch_bounds__(kBlock) void ce_vjp_narrow(VjpArgs a) {
+    constexpr int kVec = Elem<T>::kVec;
+    const int64_t nthreads = (int64_t)gridDim.x * kBlock;
+    const T* base = static_cast<const T*>(a.logits);
+    T* obase = static_cast<T*>(a.dlogits);
+    for (int64_t r0 = (int64_t)blockIdx.x * kBlock + threadIdx.x; r0 < a.n_rows; r0 += nthreads * UR) {
+        U4 buf[UR][NV];
+        RowGrad rg[UR];
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+            const int64_t r = r0 + u * nthreads;
+            if (r < a.n_rows) {
+                const char* row = reinterpret_cast<const char*>(base + row_offset(r, a.in));
+#pragma unroll
+                for (int v = 0; v < NV; ++v) buf[u][v] = load_u4(row + v * 16);
+                rg[u] = load_row_grad(a, r);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+            const int64_t r = r0 + u * nthreads;
+            if (r < a.n_rows) {
+                char* orow = reinterpret_cast<char*>(obase + row_offset(r, a.out));
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    float f[kVec];
+                    Elem<T>::unpack(buf[u][v], f);
+                    grad_vec<T, kVec>(f, rg[u], (int64_t)v * kVec);
+                    store_u4(orow + v * 16, Elem<T>::pack(f));
+                }
+            }
+        }
+    }
+}
+
+template <typename T, int G, int U>
+__global__ __launch_bounds__(G > kBlock ? G : kBlock) void ce_vjp_lanes(VjpArgs a) {
+    constexpr int kVec = Elem<T>::kVec;
+    constexpr int kThreads = G > kBlock ? G : kBlock;
+    constexpr int kRowsPerBlock = kThreads / G;
+    const int lane = threadIdx.x % G;
+    const int64_t stride = (int64_t)gridDim.x * kRowsPerBlock;
+    for (int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / G; r < a.n_rows; r += stride) {
+        const T* row = static_cast<const T*>(a.logits) + row_offset(r, a.in);
+        T* orow = static_cast<T*>(a.dlogits) + row_offset(r, a.out);
+        const RowGrad rg = load_row_grad(a, r);
+        const bool same_phase = (((uintptr_t)row ^ (uintptr_t)orow) & 15u) == 0;
+        if (same_phase) {
+            RowSplit<T> sp(row, a.V);
+            const char* vb = reinterpret_cast<const char*>(row + sp.head);
+            char* ob = reinterpret_cast<char*>(orow + sp.head);
+            int64_t j = lane;
+            for (; j + (int64_t)(U - 1) * G < sp.nvec; j += (int64_t)U * G) {
+                U4 buf[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) buf[u] = load_u4(vb + (j + (int64_t)u * G) * 16);
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    float f[kVec];
+                    Elem<T>::unpack(buf[u], f);
+                    grad_vec<T, kVec>(f, rg, sp.head + (j + (int64_t)u * G) * kVec);
+                    store_u4(ob + (j + (int64_t)u * G) * 16, Elem<T>::pack(f));
+                }
+            }
+            for (; j < sp.nvec; j += G) {
+                float f[kVec];
+                Elem<T>::unpack(load_u4(vb + j * 16), f);
+                grad_vec<T, kVec>(f, rg, sp.head + j * kVec);
+                store_u4(ob + j * 16, Elem<T>::pack(f));
+            }
+            const int64_t ns = sp.n_scalar(a.V);
+            for (int64_t k = lane; k < ns; k += G) {
+                const int64_t idx = sp.scalar_index(k);
+                Elem<T>::store1(orow + idx, grad_elem(Elem<T>::load1(row + idx), rg, idx == rg.y));
+            }
+        } else {
+            // input and output rows differ in 16-byte phase: element by element
+            for (int64_t idx = lane; idx < a.V; idx += G)
+                Elem<T>::store1(orow + idx, grad_elem(Elem<T>::load1(row + idx), rg, idx == rg.y));
+        }
+    }
+}
+
+// ---- dispatch -------------------------------------------------------------------
+
+RowLayout dev_layout(const HostLayout& h) {
+    return RowLayout{h.rows_per_batch, h.row_stride, h.batch_stride, h.uniform};
+}
+
+template <typename T>
+hipError_t fwd_typed(const FwdCall& c) {
+    FwdArgs a{c.logits, dev_layout(c.in), c.targets, c.n_rows, c.V, c.loss, reinterpret_cast<float2*>(c.lse)};
+    const dim3 grid((unsigned)c.plan.blocks);
+    constexpr int kU = Elem<T>::kVec == 8 ? 4 : 8;  // 64 elements in flight per lane per step
+    if (c.plan.narrow_nv > 0) {
+        switch (c.plan.narrow_nv) {
+            case 1: hipLaunchKernelGGL((ce_fwd_narrow<T, 1, 4>), grid, dim3(kBlock), 0, c.stream, a); break;
+            case 2: hipLaunchKernelGGL((ce_fwd_narrow<T, 2, 2>), grid, dim3(kBlock), 0, c.stream, a); break;
+            case 4: hipLaunchKernelGGL((ce_fwd_narrow<T, 4, 1>), grid, dim3(kBlock), 0, c.stream, a); break;
+            case 8: hipLaunchKernelGGL((ce_fwd_narrow<T, 8, 1>), grid, dim3(kBlock), 0, c.stream, a); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
+    switch (c.plan.lanes) {
+        case 1: hipLaunchKernelGGL((ce_fwd_lanes<T, 1, 2>), grid, dim3(kBlock), 0, c.stream, a); break;
+        case 2: hipLaunchKernelGGL((ce_fwd_lanes<T, 2, 2>), grid, dim3(kBlock), 0, c.stream, a); break;
+        case 4: hipLaunchKernelGGL((ce_fwd_lanes<T, 4, 2>), grid, dim3(kBlock), 0, c.stream, a); break;
+        case 8: hipLaunchKernelGGL((ce_fwd_lanes<T, 8, 4>), grid, dim3(kBlock), 0, c.stream, a); break;
+        case 16: hipLaunchKernelGGL((ce_fwd_lanes<T, 16, 4>), grid, dim3(kBlock), 0, c.stream, a); break;
+        case 32: hipLaunchKernelGGL((ce_fwd_lanes<T, 32, 4>), grid, dim3(kBlock), 0, c.stream, a); break;
+        case 64: hipLaunchKernelGGL((ce_fwd_lanes<T, 64, 4>), grid, dim3(kBlock), 0, c.stream, a); break;
+        case 128: hipLaunchKernelGGL((ce_fwd_rowwg<T, 2, kU>), grid, dim3(128), 0, c.stream, a); break;
+        case 256: hipLaunchKernelGGL((ce_fwd_rowwg<T, 4, kU>), grid, dim3(256), 0, c.stream, a); break;
+        case 512: hipLaunchKernelGGL((ce_fwd_rowwg<T, 8, kU>), grid, dim3(512), 0, c.stream, a); break;
+        case 1024: hipLaunchKernelGGL((ce_fwd_rowwg<T, 16, kU>), grid, dim3(1024), 0, c.stream, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t vjp_typed(const VjpCall& c) {
+    VjpArgs a{c.logits, dev_layout(c.in), c.targets, reinterpret_cast<const float2*>(c.lse), c.g,
+              c.n_rows, c.V, c.dlogits, dev_layout(c.out)};
+    const dim3 grid((unsigned)c.plan.blocks);
+    constexpr int kU = Elem<T>::kVec == 8 ? 4 : 8;
+    if (c.plan.narrow_nv > 0) {
+        switch (c.plan.narrow_nv) {
+            case 1: hipLaunchKernelGGL((ce_vjp_narrow<T, 1, 4>), grid, dim3(kBlock), 0, c.stream, a); break;
+            case 2: hipLaunchKernelGGL((ce_vjp_narrow<T, 2, 2>), grid, dim3(kBlock), 0, c.stream, a); break;
+            case 4: hipLaunchKernelGGL((ce_vjp_narrow<T, 4, 1>), grid, dim3(kBlock), 0, c.stream, a); break;
+            case 8: hipLaunchKernelGGL((ce_vjp_narrow<T, 8, 1>), grid, dim3(kBlock), 0, c.stream, a); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
+    switch (c.plan.lanes) {
+        case 1: hipLaunchKernelGGL((ce_vjp_lanes<T, 1, 2>), grid, dim3(kBlock), 0, c.stream, a); break;
+        case 2: hipLaunchKernelGGL((ce_vjp_lanes<T, 2, 2>), grid, dim3(kBlock), 0, c.stream, a); break;
+        case 4: hipLaunchKernelGGL((ce_vjp_lanes<T, 4, 2>), grid, dim3(kBlock), 0, c.stream, a); break;
+        case 8: hipLaunchKernelGGL((ce_vjp_lanes<T, 8, 4>), grid, dim3(kBlock), 0, c.stream, a); break;
+        case 16: hipLaunchKernelGGL((ce_vjp_lanes<T, 16, 4>), grid, dim3(kBlock), 0, c.stream, a); break;
+        case 32: hipLaunchKernelGGL((ce_vjp_lanes<T, 32, 4>), grid, dim3(kBlock), 0, c.stream, a); break;
+        case 64: hipLaunchKernelGGL((ce_vjp_lanes<T, 64, 4>), grid, dim3(kBlock), 0, c.stream, a); break;
+        case 128: hipLaunchKernelGGL((ce_vjp_lanes<T, 128, kU>), grid, dim3(kBlock), 0, c.stream, a); break;
+        case 256: hipLaunchKernelGGL((ce_vjp_lanes<T, 256, kU>), grid, dim3(256), 0, c.stream, a); break;
+        case 512: hipLaunchKernelGGL((ce_vjp_lanes<T, 512, kU>), grid, dim3(512), 0, c.stream, a); break;
+        case 1024: hipLaunchKernelGGL((ce_vjp_lanes<T, 1024, kU>), grid, dim3(1024), 0, c.stream, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_ce_forward(const FwdCall& c) {
+    switch (c.dt) {
+        case Dt::F32: return fwd_typed<float>(c);
+        case Dt::F16: return fwd_typed<_Float16>(c);
+        case Dt::BF16: return fwd_typed<__bf16>(c);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_ce_vjp(const VjpCall& c) {
+    switch (c.dt) {
+        case Dt::F32: return vjp_typed<float>(c);
+        case Dt::F16: return vjp_typed<_Float16>(c);
+        case Dt::BF16: return vjp_typed<__bf16>(c);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace ce

@@ -1,0 +1,78 @@
+// Internal interface between the C ABI (abi.cpp) and the kernel launchers.
+// Everything here has already been validated by abi.cpp.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ce {
+
+enum class Dt : int { F32 = 0, F16 = 1, BF16 = 2 };
+
+struct HostLayout {
+    int64_t rows_per_batch;
+    int64_t row_stride;
+    int64_t batch_stride;
+    int32_t uniform;
+};
+
+// How rows map onto lanes.  narrow_nv > 0: one lane per row, each row exactly
+// narrow_nv aligned 16-byte vectors.  Otherwise `lanes` lanes per row (a power of two
+// in [1, 1024]); above 64 one workgroup of `lanes` threads holds each row.
+struct Plan {
+    int narrow_nv;
+    int lanes;
+    int64_t blocks;
+};
+
+struct FwdCall {
+    const void* logits;
+    HostLayout in;
+    Dt dt;
+    const int32_t* targets;
+    int64_t n_rows;
+    int64_t V;
+    float* loss;
+    float* lse;
+    Plan plan;
+    hipStream_t stream;
+};
+
+struct VjpCall {
+    const void* logits;
+    HostLayout in;
+    Dt dt;
+    const int32_t* targets;
+    const float* lse;
+    const float* g;
+    int64_t n_rows;
+    int64_t V;
+    void* dlogits;
+    HostLayout out;
+    Plan plan;
+    hipStream_t stream;
+};
+
+hipError_t launch_ce_forward(const FwdCall& c);
+hipError_t launch_ce_vjp(const VjpCall& c);
+
+// lce_forward.  Workspace layout is described in lce_kernels.hip.
+struct LceCall {
+    const void* H;
+    const void* W;
+    const int32_t* targets;
+    int64_t N;
+    int64_t D;
+    int64_t V;
+    float* loss;
+    float* lse;
+    void* workspace;
+    int cu_count;
+    hipStream_t stream;
+};
+
+size_t lce_workspace_bytes(int64_t N, int64_t D, int64_t V);
+hipError_t launch_lce_forward(const LceCall& c);
+
+}  // namespace ce

@@ -180,10 +180,12 @@ def numerics_stress(dtype: str, rows: int = 65536, V: int = 1024, n_twins: int =
         off[r] = 0.0
     kind[eq_rows] = KIND_EQUAL
 
-    # de-offset twins of normal rows with a nonzero offset
+    # de-offset twins of normal rows with a nonzero offset; the twin rows are reserved
+    # first so that no row serves as both a source and a twin
+    dst = take(n_twins)
+    kind[dst] = KIND_TWIN
     cand = np.flatnonzero((kind == KIND_NORMAL) & (off != 0.0))
     src = np.sort(g.choice(cand, size=n_twins, replace=False))
-    dst = take(n_twins)
     for s_row, d_row in zip(src, dst):
         tw = store[s_row].astype(np.float64) - off[s_row]
         tw_t = tw.astype(np_t)

@@ -1,0 +1,142 @@
+"""The C ABI without a GPU: the library loads, exports what the header declares, and
+rejects invalid arguments on the host with the documented status before any launch.
+
+Pointers below are fake addresses that are never dereferenced: every call here fails
+validation first.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from softmax_cross_entropy_amd import abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ce_mi355x.h")
+
+OK, NULL, SHAPE, DTYPE, LAYOUT, WORKSPACE, LAUNCH, ALIAS, DEVICE = 0, -1, -2, -3, -4, -5, -6, -7, -8
+
+pytestmark = pytest.mark.skipif(not os.path.exists(abi.LIB_PATH), reason="library not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(\w+)\s*\([^;{]*\)\s*;", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(abi.EXPORTS)
+    L = ctypes.CDLL(abi.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for code, name in abi.STATUS.items():
+        assert abi.status_string(code).startswith(name)
+    assert "unknown" in abi.status_string(-99)
+
+
+A = 1 << 20  # fake, 256-byte aligned device addresses, far apart
+P_LOGITS, P_T, P_LOSS, P_LSE, P_G, P_OUT, P_W, P_WS = (ctypes.c_void_p(A * k) for k in range(1, 9))
+
+
+def lay(rows, rs, bs=None):
+    return abi.CELayout(rows, rs, rs * rows if bs is None else bs)
+
+
+def fwd(logits=P_LOGITS, layout=None, dt=0, t=P_T, n=16, V=8, loss=P_LOSS, lse=P_LSE, lanes=0):
+    layout = layout or lay(n, V)
+    return abi.lib().ce_forward_lanes(logits, layout, dt, t, n, V, loss, lse, lanes, None)
+
+
+def vjp(logits=P_LOGITS, layout=None, dt=0, t=P_T, lse=P_LSE, g=P_G, n=16, V=8, out=P_OUT, olayout=None, lanes=0):
+    layout = layout or lay(n, V)
+    olayout = olayout or lay(n, V)
+    return abi.lib().ce_vjp_lanes(logits, layout, dt, t, lse, g, n, V, out, olayout, lanes, None)
+
+
+def test_forward_rejects_bad_arguments():
+    assert fwd(logits=None) == NULL
+    assert fwd(t=None) == NULL
+    assert fwd(loss=None) == NULL
+    assert fwd(lse=None) == NULL
+    assert fwd(V=0) == SHAPE
+    assert fwd(V=-3) == SHAPE
+    assert fwd(V=1 << 31) == SHAPE
+    assert fwd(n=-1) == SHAPE
+    assert fwd(dt=3) == DTYPE
+    assert fwd(dt=-1) == DTYPE
+    assert fwd(lanes=3) == SHAPE
+    assert fwd(lanes=2048) == SHAPE
+    assert fwd(lanes=-2) == SHAPE
+    assert fwd(layout=abi.CELayout(0, 8, 0)) == LAYOUT
+    assert fwd(layout=abi.CELayout(16, -8, 0)) == LAYOUT
+    assert fwd(logits=ctypes.c_void_p(A + 2)) == LAYOUT  # fp32 logits not 4-byte aligned
+    assert fwd(lse=ctypes.c_void_p(5 * A + 4)) == LAYOUT  # lse pairs need 8 bytes
+    assert fwd(loss=ctypes.c_void_p(3 * A + 2)) == LAYOUT
+
+
+def test_forward_rejects_aliasing_outputs():
+    assert fwd(loss=ctypes.c_void_p(A + 64)) == ALIAS  # loss inside the logits
+    assert fwd(lse=ctypes.c_void_p(2 * A)) == ALIAS  # lse on the targets
+    assert fwd(lse=ctypes.c_void_p(3 * A + 32)) == ALIAS  # lse over loss
+
+
+def test_zero_rows_is_a_noop():
+    assert fwd(n=0, logits=None, t=None, loss=None, lse=None) == OK
+    assert vjp(n=0, logits=None, t=None, lse=None, g=None, out=None) == OK
+    assert abi.lib().lce_forward(None, None, None, 0, 64, 100, None, None, None, 0, None) == OK
+
+
+def test_vjp_rejects_bad_arguments():
+    assert vjp(out=None) == NULL
+    assert vjp(g=None) == NULL
+    assert vjp(lse=None) == NULL
+    assert vjp(V=0) == SHAPE
+    assert vjp(dt=7) == DTYPE
+    assert vjp(olayout=abi.CELayout(16, 4, 64)) == LAYOUT  # output rows overlap
+    assert vjp(olayout=abi.CELayout(4, 8, 16)) == LAYOUT  # output batches overlap
+    assert vjp(out=ctypes.c_void_p(6 * A + 2)) == LAYOUT
+
+
+def test_vjp_aliasing():
+    # the output may be the input only with an identical layout
+    assert vjp(out=ctypes.c_void_p(A + 64)) == ALIAS
+    assert vjp(out=P_LOGITS, olayout=lay(16, 16, 256), layout=lay(16, 8, 128)) == ALIAS
+    assert vjp(out=ctypes.c_void_p(5 * A)) == ALIAS  # output over g
+    assert vjp(out=ctypes.c_void_p(4 * A - 16)) == ALIAS  # output runs into lse
+
+
+def lce(H=P_LOGITS, W=P_W, t=P_T, N=32, D=64, V=1000, loss=P_LOSS, lse=P_LSE, ws=P_WS, wsb=None):
+    if wsb is None:
+        wsb = abi.lce_workspace_size(N, D, V)
+    return abi.lib().lce_forward(H, W, t, N, D, V, loss, lse, ws, wsb, None)
+
+
+def test_lce_rejects_bad_arguments():
+    assert abi.lce_workspace_size(32, 64, 1000) > 0
+    assert abi.lce_workspace_size(32, 60, 1000) == 0
+    assert lce(D=60) == SHAPE
+    assert lce(D=0) == SHAPE
+    assert lce(V=0) == SHAPE
+    assert lce(N=-1) == SHAPE
+    assert lce(H=None) == NULL
+    assert lce(W=None) == NULL
+    assert lce(ws=None) == WORKSPACE
+    assert lce(wsb=abi.lce_workspace_size(32, 64, 1000) - 1) == WORKSPACE
+    assert lce(H=ctypes.c_void_p(A + 8)) == LAYOUT
+    assert lce(ws=ctypes.c_void_p(8 * A + 64)) == LAYOUT
+    assert lce(loss=ctypes.c_void_p(2 * A - 64)) == ALIAS  # loss inside W's range? no: inside H..W
+    assert lce(ws=ctypes.c_void_p(7 * A + 256)) == ALIAS  # workspace inside W
+
+
+@pytest.mark.skipif(os.environ.get("HIP_VISIBLE_DEVICES", None) is not None or os.path.exists("/dev/kfd"),
+                    reason="only meaningful without a GPU")
+def test_valid_call_without_device_reports_device_error():
+    assert fwd() == DEVICE
+    assert vjp() == DEVICE
