@@ -1,0 +1,218 @@
+"""Benchmark of the fused softmax cross-entropy hot path on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic input:
+  * ce_forward + ce_vjp on bf16 logits [2048 x 151,936] (N(0,1), uniform targets,
+    g = 1): the configuration the CE fwd+VJP figure is quoted on;
+  * lce_forward on bf16 H [8192 x 4096] ~ N(0,1), W [151,936 x 4096] ~ N(0, 1/D),
+    uniform targets: the linear-CE configuration.
+Inputs are resident in HBM before the timed region.  Two copies of the logits
+alternate between steps (each copy is 622 MB, larger than the 256 MB Infinity Cache,
+so no step reads logits cached by the previous one).
+
+Timing: W untimed warm-up steps, then exactly K steps bracketed by
+torch.cuda.synchronize(); HIP events on the launch stream around every call give
+per-kernel-call durations.  Prints ONE JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+CE_ROWS, CE_V = 2048, 151936
+LCE_N, LCE_D, LCE_V = 8192, 4096, 151936
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
+
+METRIC = "fused CE fwd+VJP ms & GB/s (% HBM peak); linear-CE fwd TFLOP/s (% MFMA)"
+
+
+def ce_bytes(rows, V, e):
+    """Algorithmic HBM bytes per call: forward reads V*e per row and writes loss (4)
+    and lse (8), reading the target (4); the VJP reads V*e plus lse, target and g
+    (16 per row) and writes V*e."""
+    fwd = rows * (V * e + 16)
+    vjp = rows * (2 * V * e + 16)
+    return fwd, vjp
+
+
+def lce_flops(N, D, V):
+    return 2.0 * N * D * V
+
+
+def cpu_baseline(ce_batch, lce_inputs, lce_rows=32):
+    """The float64 oracle, as it stands, on a bounded sample of the same workload."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import ce as oce
+    from oracle import lce as olce
+
+    b = ce_batch
+    t0 = time.perf_counter()
+    for r0 in range(0, b.rows, 256):
+        r1 = min(b.rows, r0 + 256)
+        z = oce.decode(b.logits[r0:r1], "bf16")
+        _, m, ls = oce.forward(z, b.targets[r0:r1])
+        oce.grad(z, b.targets[r0:r1], b.g[r0:r1], m, ls)
+    ce_s = time.perf_counter() - t0
+    fwd_b, vjp_b = ce_bytes(b.rows, b.V, 2)
+    H, W, y = lce_inputs
+    rows = np.arange(lce_rows)
+    t0 = time.perf_counter()
+    olce.forward(H, W, y, rows=rows)
+    lce_s = time.perf_counter() - t0
+    blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    return {
+        "value": (fwd_b + vjp_b) / ce_s / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"CE fwd+grad oracle (float64 NumPy, single-threaded) over all {b.rows} rows of the "
+                  f"{b.rows}x{b.V} bf16 batch: {ce_s:.2f} s",
+        "lce": {"value": lce_flops(lce_rows, LCE_D, LCE_V) / lce_s / 1e12, "unit": "TFLOP/s",
+                "cores": blas, "seconds": lce_s,
+                "sample": f"lce oracle (float64 BLAS matmul + CE) on {lce_rows} of {LCE_N} rows, "
+                          f"all {LCE_V} columns"},
+        "host_cores": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--parts", default="ce,lce", help="comma list of ce, lce")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(rows shard across GPUs with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    parts = set(args.parts.split(","))
+
+    import torch
+
+    from softmax_cross_entropy_amd import abi, inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    abi.lib()
+
+    def up(x, bf16=False):
+        t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16) if bf16 else x)
+        return (t.view(torch.bfloat16) if bf16 else t).to(dev)
+
+    ce_batch = lce_in = None
+    if "ce" in parts:
+        ce_batch = inputs.large_vocab(CE_ROWS, CE_V)
+        X = [up(ce_batch.logits, True), up(ce_batch.logits, True)]
+        T = up(ce_batch.targets)
+        G = up(ce_batch.g)
+        loss = torch.empty(CE_ROWS, device=dev)
+        lse = torch.empty(CE_ROWS, 2, device=dev)
+        dX = torch.empty_like(X[0])
+    if "lce" in parts:
+        lce_in = inputs.linear_ce(LCE_N, LCE_D, LCE_V)
+        Hd, Wd, Yd = up(lce_in[0], True), up(lce_in[1], True), up(lce_in[2])
+        lloss = torch.empty(LCE_N, device=dev)
+        llse = torch.empty(LCE_N, 2, device=dev)
+        ws = torch.empty(abi.lce_workspace_size(LCE_N, LCE_D, LCE_V), dtype=torch.uint8, device=dev)
+
+    stream = torch.cuda.current_stream(dev)
+    n_ev = 4
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(K)]
+
+    def step(i, events=None):
+        if events:
+            events[0].record(stream)
+        if ce_batch is not None:
+            x = X[i % 2]
+            abi.ce_forward(x, T, loss=loss, lse=lse)
+            if events:
+                events[1].record(stream)
+            abi.ce_vjp(x, T, lse, G, dlogits=dX)
+        if events:
+            events[2].record(stream)
+        if lce_in is not None:
+            abi.lce_forward(Hd, Wd, Yd, loss=lloss, lse=llse, workspace=ws)
+        if events:
+            events[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i, ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    def ms(a, b):
+        return [ev[i][a].elapsed_time(ev[i][b]) for i in range(K)]
+
+    step_ms = float(np.mean(ms(0, 3)))
+    out = {"metric": METRIC, "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": step_ms,
+           "wall_ms_per_step": wall / K * 1e3, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) logits/hidden states, "
+           "N(0,1/D) weights, uniform targets)"}
+    cfg = {"workload": []}
+    parts_out = {}
+    rooflines = {}
+    if ce_batch is not None:
+        fwd_b, vjp_b = ce_bytes(CE_ROWS, CE_V, 2)
+        f_ms = float(np.mean(ms(0, 1)))
+        v_ms = float(np.mean(ms(1, 2)))
+        fv_ms = float(np.mean(ms(0, 2)))
+        gbs = (fwd_b + vjp_b) / (fv_ms * 1e-3) / 1e9
+        parts_out["ce_fwd_vjp"] = {"ms": fv_ms, "GB_s": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS,
+                                   "algorithmic_bytes": fwd_b + vjp_b,
+                                   "fwd_ms": f_ms, "fwd_GB_s": fwd_b / (f_ms * 1e-3) / 1e9,
+                                   "vjp_ms": v_ms, "vjp_GB_s": vjp_b / (v_ms * 1e-3) / 1e9}
+        for name, byts, t in (("ce_forward", fwd_b, f_ms), ("ce_vjp", vjp_b, v_ms)):
+            a = byts / (t * 1e-3) / 1e9
+            rooflines[name] = {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": a / HBM_PEAK_GBS, "traffic": None, "ms": t, "algorithmic_bytes": byts}
+        cfg["workload"].append(f"ce_forward+ce_vjp bf16 [{CE_ROWS} x {CE_V}]")
+        cfg["ce"] = {"rows": CE_ROWS, "V": CE_V, "dtype": "bf16"}
+        out["value"] = gbs
+        out["unit"] = "GB/s"
+    if lce_in is not None:
+        l_ms = float(np.mean(ms(2, 3)))
+        fl = lce_flops(LCE_N, LCE_D, LCE_V)
+        tf = fl / (l_ms * 1e-3) / 1e12
+        parts_out["lce_forward"] = {"ms": l_ms, "TFLOP_s": tf, "frac_mfma_bf16_peak": tf / MFMA_BF16_PEAK_TFLOPS,
+                                    "flop": fl}
+        rooflines["lce_forward"] = {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS,
+                                    "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                                    "ms": l_ms, "algorithmic_flop": fl,
+                                    "kernels": "lce_tile_mfma + lce_merge (one lce_forward call)"}
+        cfg["workload"].append(f"lce_forward bf16 N={LCE_N} D={LCE_D} V={LCE_V}")
+        cfg["lce"] = {"N": LCE_N, "D": LCE_D, "V": LCE_V, "dtype": "bf16 in, fp32 accumulate"}
+        if "value" not in out:
+            out["value"] = tf
+            out["unit"] = "TFLOP/s"
+    cfg["workload"] = " + ".join(cfg["workload"])
+    out["config"] = cfg
+    out["parts"] = parts_out
+    # the dominant kernel of the step by time
+    dom = max(rooflines, key=lambda k: rooflines[k]["ms"])
+    out["roofline"] = dict(rooflines[dom], kernel=dom)
+    out["rooflines"] = rooflines
+    if not args.no_cpu and ce_batch is not None and lce_in is not None:
+        out["cpu_baseline"] = cpu_baseline(ce_batch, lce_in)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -59,28 +59,49 @@ __device__ __forceinline__ void store_forward(const FwdArgs& a, int64_t r, MS st
     a.lse[r] = make_float2(st.m, ls);
 }
 
-// Streams this lane's share of one row into `st`: vectors lane, lane + G, ... (U
-// vectors per step, all loads issued before any arithmetic), then the scalar head
-// and tail elements.
+// Streams this lane's share of one row into `st`: vectors lane, lane + G, ... in
+// groups of U.  The loads of the next group are issued before the current group is
+// folded in, so each lane keeps U vectors in flight while it computes.  Then the
+// scalar head and tail elements.
+template <typename T, int U>
+__device__ __forceinline__ void fold_group(MS& st, const U4 (&buf)[U]) {
+    constexpr int kVec = Elem<T>::kVec;
+    float f[U * kVec];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        float t[kVec];
+        Elem<T>::unpack(buf[u], t);
+#pragma unroll
+        for (int k = 0; k < kVec; ++k) f[u * kVec + k] = t[k];
+    }
+    ms_add<U * kVec>(st, f);
+}
+
 template <typename T, int G, int U>
 __device__ __forceinline__ void stream_row(const T* row, int64_t V, int lane, MS& st) {
     constexpr int kVec = Elem<T>::kVec;
     RowSplit<T> sp(row, V);
     const char* vb = reinterpret_cast<const char*>(row + sp.head);
+    constexpr int64_t kStep = (int64_t)U * G;
     int64_t j = lane;
-    for (; j + (int64_t)(U - 1) * G < sp.nvec; j += (int64_t)U * G) {
-        U4 buf[U];
+    if (j + (int64_t)(U - 1) * G < sp.nvec) {
+        U4 cur[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) buf[u] = load_u4(vb + (j + (int64_t)u * G) * 16);
-        float f[U * kVec];
+        for (int u = 0; u < U; ++u) cur[u] = load_u4(vb + (j + (int64_t)u * G) * 16);
+        while (true) {
+            const int64_t jn = j + kStep;
+            const bool more = jn + (int64_t)(U - 1) * G < sp.nvec;
+            U4 nxt[U];
+            if (more) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float t[kVec];
-            Elem<T>::unpack(buf[u], t);
+                for (int u = 0; u < U; ++u) nxt[u] = load_u4(vb + (jn + (int64_t)u * G) * 16);
+            }
+            fold_group<T, U>(st, cur);
+            j = jn;
+            if (!more) break;
 #pragma unroll
-            for (int k = 0; k < kVec; ++k) f[u * kVec + k] = t[k];
+            for (int u = 0; u < U; ++u) cur[u] = nxt[u];
         }
-        ms_add<U * kVec>(st, f);
     }
     for (; j < sp.nvec; j += G) {
         float f[kVec];
