@@ -165,7 +165,8 @@ size_t lce_workspace_size(int64_t N, int64_t D, int64_t V);
  *            bytes, 256-byte aligned; its contents on entry are ignored.
  * The product accumulates in float32 on the matrix cores (bf16 in, fp32 out).  The
  * target logit is taken from the same float32 accumulator that feeds (m, s).
- * Requires D % 8 == 0 (16-byte rows) and V < 2^31; N may be any non-negative size.
+ * Requires D % 8 == 0 (16-byte rows), D <= 2^22 and V < 2^31; N may be any
+ * non-negative size.
  */
 ce_status lce_forward(const void* H, const void* W, const int32_t* targets, int64_t N, int64_t D,
                       int64_t V, float* loss, float* lse, void* workspace, size_t workspace_bytes,

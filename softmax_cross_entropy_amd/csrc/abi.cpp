@@ -253,7 +253,7 @@ size_t lce_workspace_size(int64_t N, int64_t D, int64_t V) {
 
 ce_status lce_forward(const void* H, const void* W, const int32_t* targets, int64_t N, int64_t D, int64_t V,
                       float* loss, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    if (N < 0 || D < 1 || D % 8 != 0 || V < 1 || V > kMaxV || D > (int64_t)1 << 24) return CE_ERR_SHAPE;
+    if (N < 0 || D < 1 || D % 8 != 0 || V < 1 || V > kMaxV || D > (int64_t)1 << 22) return CE_ERR_SHAPE;
     if (N == 0) return CE_OK;
     if (!H || !W || !targets || !loss || !lse) return CE_ERR_NULL;
     if (!workspace || workspace_bytes < ce::lce_workspace_bytes(N, D, V)) return CE_ERR_WORKSPACE;

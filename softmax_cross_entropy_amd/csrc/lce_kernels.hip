@@ -7,14 +7,14 @@
 // is captured by the tile that holds the target column.
 //
 // Two kernels:
-//   lce_tile   one 256 x 256 tile of Z per workgroup (bf16 MFMA, fp32 accumulate,
+//   lce_tile   one 256 x 256 tile of Z per workgroup (bf16 MFMA 32x32x16, fp32 accumulate,
 //              K = D streamed through LDS in 64-wide double-buffered stages).  Its
 //              epilogue turns the fp32 accumulators straight into one (m, s) pair per
 //              row for each 128-column slab, and stores the target logit from the
 //              same accumulator when the target column is in the slab.
 //   lce_merge  folds the slabs of each row in slab order into (m, s), then
 //              loss = (m - z_y) + log s and lse = (m, log s).
-// Workspace: partial (m, s) float2 [n_slabs][N], then z_y float [N].
+// Workspace: partial (m, s) float2 [N][n_slabs], then z_y float [N].
 //
 // The page's kernel merges fixed 8192-column tiles in a chain of dependent
 // dispatches.  Here every tile of the grid is independent (the merge is associative,
@@ -29,7 +29,7 @@ namespace ce {
 namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int BM = 256;              // rows of H per tile
@@ -37,7 +37,7 @@ constexpr int BN = 256;              // rows of W (vocabulary columns) per tile
 constexpr int BK = 64;               // reduction depth per LDS stage
 constexpr int kThreads = 256;        // 4 waves as 2 x 2, each owning 128 x 128 of the tile
 constexpr int WT = 128;              // wave tile edge
-constexpr int FB = WT / 16;          // 8 x 8 MFMA 16x16 blocks per wave
+constexpr int FB = WT / 32;          // 4 x 4 MFMA 32x32 blocks per wave
 constexpr int kStageBytes = BM * BK * 2;  // 32 KiB per operand per stage
 constexpr int kTilesPerGroup = 32;   // tiles per super-block (one per CU of an XCD)
 constexpr int kXcds = 8;
@@ -52,7 +52,8 @@ struct TileArgs {
     int n_row_tiles, n_col_tiles;
     int gr, gc;      // super-block shape in tiles (gr * gc == 32)
     int n_rg, n_sb;  // row groups, super-blocks
-    float2* partial;  // [n_slabs][N]
+    int n_slabs;
+    float2* partial;  // [N][n_slabs]
     float* zy;        // [N]
 };
 
@@ -92,116 +93,170 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
     // at (row = first + i / 8, physical chunk i % 8), so it fetches the logical chunk
     // that the swizzle maps there.  Rows past N (or V) re-read the last valid row; their
     // results are never stored (columns past V are masked in the epilogue).
-    const __bf16* a_src[8];
-    const __bf16* b_src[8];
+    const int lrow = wave * 64 + (lane >> 3);  // LDS row of load q = 0; q adds 8 rows
     int koff[2];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const int r = wave * 64 + q * 8 + (lane >> 3);
-        int64_t ra = row0 + r;
-        ra = ra < a.N ? ra : a.N - 1;
-        int64_t rb = col0 + r;
-        rb = rb < a.V ? rb : a.V - 1;
-        a_src[q] = a.H + ra * a.D;
-        b_src[q] = a.W + rb * a.D;
-    }
-#pragma unroll
     for (int par = 0; par < 2; ++par) {
-        const int r = par * 8 + (lane >> 3);  // (r >> 1) & 7 for the two row parities
+        const int r = par * 8 + (lane >> 3);  // (row >> 1) & 7 depends only on q's parity
         koff[par] = ((lane & 7) ^ ((r >> 1) & 7)) * 8;
     }
-    const int nk = (int)((a.D + BK - 1) / BK);
+    // Addresses: a wave-uniform base (the tile's first row at K offset k0) plus a 32-bit
+    // per-lane byte offset; rows past N (or V) are clamped to the last valid row.
+    const int64_t a_rows = a.N - row0 < BM ? a.N - row0 : BM;  // valid rows in this tile
+    const int64_t b_rows = a.V - col0 < BN ? a.V - col0 : BN;
+    const uint32_t row_bytes = (uint32_t)(a.D * 2);
+    const char* a_tile = reinterpret_cast<const char*>(a.H + row0 * a.D);
+    const char* b_tile = reinterpret_cast<const char*>(a.W + col0 * a.D);
 
     auto issue = [&](int kt, int buf) {
         const int64_t k0 = (int64_t)kt * BK;
+        const char* a_k = a_tile + k0 * 2;
+        const char* b_k = b_tile + k0 * 2;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            int64_t k = k0 + koff[q & 1];
-            k = k < a.D ? k : a.D - 8;  // K tail: a valid chunk, zeroed after the LDS read
+            const int r = lrow + q * 8;
+            const int ra = r < a_rows ? r : (int)a_rows - 1;
+            const int rb = r < b_rows ? r : (int)b_rows - 1;
+            // K tail: past D, re-read this row's last chunk; zeroed in LDS once it lands
+            const uint32_t kb = (uint32_t)(k0 + koff[q & 1] < a.D ? koff[q & 1] : a.D - 8 - k0) * 2;
             char* dst_a = &lds[buf][0][(wave * 64 + q * 8) * 128];
             char* dst_b = &lds[buf][1][(wave * 64 + q * 8) * 128];
-            __builtin_amdgcn_global_load_lds((const void*)(a_src[q] + k), (lds_void_t*)dst_a, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void*)(b_src[q] + k), (lds_void_t*)dst_b, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(a_k + ((uint32_t)ra * row_bytes + kb)),
+                                             (lds_void_t*)dst_a, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(b_k + ((uint32_t)rb * row_bytes + kb)),
+                                             (lds_void_t*)dst_b, 16, 0, 0);
+        }
+    };
+    // In a K-tail stage the chunks past D hold copies of a valid chunk: overwrite this
+    // lane's slots with zeros after its loads have landed, before the barrier that
+    // publishes the stage.
+    auto zero_tail = [&](int kt, int buf) {
+        const int64_t k0 = (int64_t)kt * BK;
+        if (k0 + BK <= a.D) return;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            if (k0 + koff[q & 1] >= a.D) {
+                const int o = (wave * 64 + q * 8) * 128 + lane * 16;
+                *reinterpret_cast<U4*>(&lds[buf][0][o]) = U4{{0u, 0u, 0u, 0u}};
+                *reinterpret_cast<U4*>(&lds[buf][1][o]) = U4{{0u, 0u, 0u, 0u}};
+            }
         }
     };
 
-    f32x4 acc[FB][FB];
+    // v_mfma_f32_32x32x16_bf16: lane l supplies row l % 32 of the A block and column
+    // l % 32 of the B block, K elements 8 * (l / 32) .. + 7 of the 16; it receives
+    // D[row = 8 * (e / 4) + 4 * (l / 32) + e % 4][col = l % 32] in element e.
+    f32x16 acc[FB][FB];
 #pragma unroll
     for (int i = 0; i < FB; ++i)
 #pragma unroll
-        for (int j = 0; j < FB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < FB; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     const int wm = wave >> 1, wn = wave & 1;
-    const int q16 = lane & 15, g4 = lane >> 4;
-    const int rd_row = q16 * 128;
-    const int sw = q16 >> 1;
+    const int l32 = lane & 31, h2 = lane >> 5;
+    const int sw = (l32 >> 1) & 7;
+    int off[4];  // byte offset of this lane's operand row and chunk for K16 step kk
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) off[kk] = l32 * 128 + (((kk * 2 + h2) ^ sw) << 4);
 
-    issue(0, 0);
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        // Stage kt was issued one iteration earlier.  Issue stage kt + 1, then wait until
-        // at most its 16 loads are outstanding (loads retire in order), and meet the
-        // other waves at a plain barrier: no fence, so the next stage stays in flight.
-        if (kt + 1 < nk) {
-            issue(kt + 1, cur ^ 1);
-            asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-        } else {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    auto read_frags = [&](int buf, int kk, bf16x8 (&fa)[FB], bf16x8 (&fb)[FB]) {
+        const char* As = &lds[buf][0][wm * WT * 128];
+        const char* Bs = &lds[buf][1][wn * WT * 128];
+#pragma unroll
+        for (int i = 0; i < FB; ++i) {
+            fa[i] = *reinterpret_cast<const bf16x8*>(As + i * 32 * 128 + off[kk]);
+            fb[i] = *reinterpret_cast<const bf16x8*>(Bs + i * 32 * 128 + off[kk]);
         }
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        const char* As = &lds[cur][0][wm * WT * 128];
-        const char* Bs = &lds[cur][1][wn * WT * 128];
-        const int64_t kvalid = a.D - (int64_t)kt * BK;  // >= BK except in a K tail
+    };
+    auto mfma_all = [&](const bf16x8 (&fa)[FB], const bf16x8 (&fb)[FB]) {
 #pragma unroll
-        for (int kk = 0; kk < BK / 32; ++kk) {
-            const int c = kk * 4 + g4;
-            const int off = rd_row + ((c ^ sw) << 4);
-            const bool kok = (int64_t)c * 8 < kvalid;
-            bf16x8 af[FB], bfr[FB];
+        for (int i = 0; i < FB; ++i)
 #pragma unroll
-            for (int i = 0; i < FB; ++i) {
-                af[i] = *reinterpret_cast<const bf16x8*>(As + i * 16 * 128 + off);
-                bfr[i] = *reinterpret_cast<const bf16x8*>(Bs + i * 16 * 128 + off);
-            }
-            if (!kok) {
+            for (int j = 0; j < FB; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    };
+    // 16 MFMAs and 8 LDS reads: one read after every 2 MFMAs
+    auto interleave = [&]() {
 #pragma unroll
-                for (int i = 0; i < FB; ++i) {
-                    af[i] = bf16x8{};
-                    bfr[i] = bf16x8{};
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < FB; ++i)
-#pragma unroll
-                for (int j = 0; j < FB; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int t = 0; t < 8; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        // every wave has consumed its LDS reads of this buffer (the MFMAs used them)
-        // before any wave issues the loads that overwrite it
+    };
+    auto sync_stage = [&](int kt, int cur, int nk) {
+        // stage kt + 1 has landed (issued one stage earlier); after this barrier every
+        // wave has finished reading buffer `cur`, which then takes stage kt + 2
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (kt + 1 < nk) zero_tail(kt + 1, cur ^ 1);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
+        if (kt + 2 < nk) issue(kt + 2, cur);
+    };
+
+    // Pipeline: the four K16 steps of a stage each run their 16 MFMAs while the
+    // fragments of the next step are read from LDS; the last step of a stage reads the
+    // first fragments of the next stage, after the stage's single barrier.
+    const int nk = (int)((a.D + BK - 1) / BK);
+    bf16x8 fa0[FB], fb0[FB], fa1[FB], fb1[FB];
+    issue(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    zero_tail(0, 0);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (nk > 1) issue(1, 1);
+    read_frags(0, 0, fa0, fb0);
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+        const int cur = kt & 1;
+        read_frags(cur, 1, fa1, fb1);
+        mfma_all(fa0, fb0);
+        interleave();
+        read_frags(cur, 2, fa0, fb0);
+        mfma_all(fa1, fb1);
+        interleave();
+        read_frags(cur, 3, fa1, fb1);
+        mfma_all(fa0, fb0);
+        interleave();
+        sync_stage(kt, cur, nk);
+        read_frags(cur ^ 1, 0, fa0, fb0);
+        mfma_all(fa1, fb1);
+        interleave();
+    }
+    {
+        const int cur = (nk - 1) & 1;
+        read_frags(cur, 1, fa1, fb1);
+        mfma_all(fa0, fb0);
+        interleave();
+        read_frags(cur, 2, fa0, fb0);
+        mfma_all(fa1, fb1);
+        interleave();
+        read_frags(cur, 3, fa1, fb1);
+        mfma_all(fa0, fb0);
+        interleave();
+        mfma_all(fa1, fb1);
     }
 
     // ---- epilogue: (m, s) per row over this wave's 128 columns ----------------
-    // acc[i][j][e] holds Z[row = wm*128 + i*16 + g4*4 + e][col = wn*128 + j*16 + q16].
+    // acc[i][j][e] holds Z[row = wm*128 + i*32 + 8*(e/4) + 4*h2 + e%4][col = wn*128 + j*32 + l32].
     const int64_t wcol0 = col0 + wn * WT;
+    const int64_t wrow0 = row0 + wm * WT;
     bool col_ok[FB];
 #pragma unroll
-    for (int j = 0; j < FB; ++j) col_ok[j] = wcol0 + j * 16 + q16 < a.V;
+    for (int j = 0; j < FB; ++j) col_ok[j] = wcol0 + j * 32 + l32 < a.V;
 
     // target logits: captured from the accumulator that holds the target column
-    const int64_t wrow0 = row0 + wm * WT;
 #pragma unroll
     for (int i = 0; i < FB; ++i) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int64_t r = wrow0 + i * 16 + g4 * 4 + e;
+        for (int e = 0; e < 16; ++e) {
+            const int64_t r = wrow0 + i * 32 + 8 * (e / 4) + 4 * h2 + (e % 4);
             if (r < a.N) {
                 const int64_t yrel = (int64_t)a.targets[r] - wcol0;
-                if (yrel >= 0 && yrel < WT && (int)(yrel & 15) == q16) {
-                    const int jj = (int)(yrel >> 4);
+                if (yrel >= 0 && yrel < WT && (int)(yrel & 31) == l32) {
+                    const int jj = (int)(yrel >> 5);
                     float v = 0.f;
 #pragma unroll
                     for (int j = 0; j < FB; ++j) v = (j == jj) ? acc[i][j][e] : v;
@@ -211,71 +266,84 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
         }
     }
 
-    MS st[32];  // state index i * 4 + e
+    MS st[64];  // state index i * 16 + e
 #pragma unroll
     for (int i = 0; i < FB; ++i) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < 16; ++e) {
             float v[FB];
 #pragma unroll
             for (int j = 0; j < FB; ++j) v[j] = col_ok[j] ? acc[i][j][e] : kNegInf;
             MS s0 = ms_empty();
             ms_add<FB>(s0, v);
-            st[i * 4 + e] = s0;
+            st[i * 16 + e] = s0;
         }
     }
-    // Reduce-scatter across the 16 lanes that share a row set (lane bits 3..0): at each
+    // Reduce-scatter across the 32 lanes that share a row set (lane bits 4..0): at each
     // step a lane keeps one half of its states, sends the other half to its partner and
-    // merges what it receives.  After four steps lane q16 holds rows 2*q16 and 2*q16+1.
+    // merges what it receives.  After five steps lane l32 holds states 2*l32, 2*l32+1.
 #pragma unroll
-    for (int step = 0; step < 4; ++step) {
-        const int mask = 8 >> step;
-        const int half = 16 >> step;  // states held before this step: 2 * half
+    for (int step = 0; step < 5; ++step) {
+        const int mask = 16 >> step;
+        const int half = 32 >> step;  // states held before this step: 2 * half
         const bool upper = (lane & mask) != 0;
 #pragma unroll
         for (int k = 0; k < half; ++k) {
             const MS lo = st[k], hi = st[k + half];
             const MS keep = upper ? hi : lo;
             const MS send = upper ? lo : hi;
-            MS recv{__shfl_xor(send.m, mask, 16), __shfl_xor(send.s, mask, 16)};
+            MS recv{__shfl_xor(send.m, mask, 32), __shfl_xor(send.s, mask, 32)};
             st[k] = ms_merge(keep, recv);
         }
     }
-    // state index 2*q16 + t  ->  i = q16 / 2, e = 2 * (q16 % 2) + t
+    // state 2*l32 + t  ->  i = l32 / 8, e = 2 * (l32 % 8) + t
     const int64_t slab = (int64_t)col_tile * 2 + wn;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-        const int64_t r = wrow0 + (q16 >> 1) * 16 + g4 * 4 + 2 * (q16 & 1) + t;
-        if (r < a.N) a.partial[slab * a.N + r] = make_float2(st[t].m, st[t].s);
+        const int e = 2 * (l32 & 7) + t;
+        const int64_t r = wrow0 + (l32 >> 3) * 32 + 8 * (e / 4) + 4 * h2 + (e % 4);
+        if (r < a.N) a.partial[r * a.n_slabs + slab] = make_float2(st[t].m, st[t].s);
     }
 }
 
 constexpr int kMergeThreads = 256;
+constexpr int kMergeLanes = 16;  // lanes per row; 16 rows per workgroup
 
+// Folds one row's slabs: lane l takes slabs l, l + 16, ... (16 consecutive float2 per
+// step across the lanes, one 128-byte line), four at a time with one rescale, then the
+// 16 lane states merge by butterfly.  The order is fixed, so the result is too.
 __global__ __launch_bounds__(kMergeThreads) void lce_merge(const float2* __restrict__ partial,
                                                             const float* __restrict__ zy,
                                                             const int32_t* __restrict__ targets, int64_t N,
                                                             int n_slabs, int64_t V, float* loss, float2* lse) {
-    const int64_t r = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
-    if (r >= N) return;
+    const int64_t r = (int64_t)blockIdx.x * (kMergeThreads / kMergeLanes) + threadIdx.x / kMergeLanes;
+    const int lane = threadIdx.x % kMergeLanes;
+    if (r >= N) return;  // the whole 16-lane group leaves together
+    const float2* p = partial + r * n_slabs;
     MS st = ms_empty();
-    int s = 0;
-    for (; s + 8 <= n_slabs; s += 8) {
-        float2 p[8];
+    int s = lane;
+    for (; s + 3 * kMergeLanes < n_slabs; s += 4 * kMergeLanes) {
+        float2 v[4];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) p[u] = partial[(int64_t)(s + u) * N + r];
+        for (int u = 0; u < 4; ++u) v[u] = p[s + u * kMergeLanes];
+        float m = st.m;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) st = ms_merge(st, MS{p[u].x, p[u].y});
+        for (int u = 0; u < 4; ++u) m = fmaxf(m, v[u].x);
+        const float rr = ref_point(m);
+        float acc = __fmul_rn(st.s, exp_e(st.m - rr));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc += __fmul_rn(v[u].y, exp_e(v[u].x - rr));
+        st = MS{m, acc};
     }
-    for (; s < n_slabs; ++s) {
-        const float2 p = partial[(int64_t)s * N + r];
-        st = ms_merge(st, MS{p.x, p.y});
+    for (; s < n_slabs; s += kMergeLanes) st = ms_merge(st, MS{p[s].x, p[s].y});
+    st = ms_group_reduce<kMergeLanes>(st);
+    if (lane == 0) {
+        const int32_t y = targets[r];
+        const bool ok = y >= 0 && (int64_t)y < V;
+        const float ls = log_e(st.s);
+        loss[r] = ok ? (st.m - zy[r]) + ls : __builtin_nanf("");
+        lse[r] = make_float2(st.m, ls);
     }
-    const int32_t y = targets[r];
-    const bool ok = y >= 0 && (int64_t)y < V;
-    const float ls = log_e(st.s);
-    loss[r] = ok ? (st.m - zy[r]) + ls : __builtin_nanf("");
-    lse[r] = make_float2(st.m, ls);
 }
 
 struct Geometry {
@@ -313,11 +381,12 @@ hipError_t launch_lce_forward(const LceCall& c) {
     float2* partial = reinterpret_cast<float2*>(ws);
     float* zy = reinterpret_cast<float*>(ws + align256((size_t)g.n_slabs * (size_t)c.N * sizeof(float2)));
     TileArgs a{static_cast<const __bf16*>(c.H), static_cast<const __bf16*>(c.W), c.targets, c.N, c.D, c.V,
-               g.n_row_tiles, g.n_col_tiles, g.gr, g.gc, g.n_rg, g.n_sb, partial, zy};
+               g.n_row_tiles, g.n_col_tiles, g.gr, g.gc, g.n_rg, g.n_sb, g.n_slabs, partial, zy};
     hipLaunchKernelGGL(lce_tile, dim3((unsigned)g.blocks), dim3(kThreads), 0, c.stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t mblocks = (c.N + kMergeThreads - 1) / kMergeThreads;
+    constexpr int kRowsPerBlock = kMergeThreads / kMergeLanes;
+    const int64_t mblocks = (c.N + kRowsPerBlock - 1) / kRowsPerBlock;
     hipLaunchKernelGGL(lce_merge, dim3((unsigned)mblocks), dim3(kMergeThreads), 0, c.stream, partial, zy,
                        c.targets, c.N, g.n_slabs, c.V, c.loss, reinterpret_cast<float2*>(c.lse));
     return hipGetLastError();
