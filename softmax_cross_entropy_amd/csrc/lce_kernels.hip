@@ -22,6 +22,8 @@
 // 256 compute units work on the whole vocabulary at once.
 #include <hip/hip_runtime.h>
 
+#include <utility>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -62,8 +64,59 @@ struct TileArgs {
 // read touches at one K chunk land in 16 different 16-byte bank groups:
 //   byte offset of (row, chunk) = row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4).
 
+// ---- epilogue helpers ------------------------------------------------------------
+
+// (m, s) of N values directly: one max, N exponentials, no rescale.
+template <int N>
+__device__ __forceinline__ MS ms_of(const float (&v)[N]) {
+    float m = v[0];
+#pragma unroll
+    for (int k = 1; k < N; ++k) m = fmaxf(m, v[k]);
+    const float r = ref_point(m);
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < N; ++k) s += exp_e(v[k] - r);
+    return MS{m, s};
+}
+
+// Value held by this lane's partner for reduce-scatter step STEP (partner lane differs in
+// bit 4 - STEP): DPP within 16-lane rows for bits 3..0, a swizzle for bit 4.
+template <int STEP>
+__device__ __forceinline__ float partner(float v) {
+    const int x = __float_as_int(v);
+    int y;
+    if constexpr (STEP == 0)
+        y = __builtin_amdgcn_ds_swizzle(x, 0x401F);  // lane ^ 16 within 32
+    else if constexpr (STEP == 1)
+        y = __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);  // row_ror:8 = lane ^ 8 within 16
+    else if constexpr (STEP == 2)
+        y = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false);  // row_half_mirror: 7 - i within 8
+    else if constexpr (STEP == 3)
+        y = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1] = lane ^ 2
+    else
+        y = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2] = lane ^ 1
+    return __int_as_float(y);
+}
+
+template <int STEP, int HALF>
+__device__ __forceinline__ void reduce_scatter_step(MS (&st)[64], int lane) {
+    const bool upper = ((lane >> (4 - STEP)) & 1) != 0;
+#pragma unroll
+    for (int k = 0; k < HALF; ++k) {
+        const MS lo = st[k], hi = st[k + HALF];
+        const MS keep = upper ? hi : lo;
+        const MS send = upper ? lo : hi;
+        const MS recv{partner<STEP>(send.m), partner<STEP>(send.s)};
+        st[k] = ms_merge(keep, recv);
+    }
+}
+
 __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
-    __shared__ __attribute__((aligned(16))) char lds[2][2][kStageBytes];  // [stage][A|B]
+    // One LDS object (the compiler then sees the DMA writes and the fragment reads as
+    // one array and inserts no waits of its own): two stages of A and B, then targets.
+    __shared__ __attribute__((aligned(16))) char smem[2 * 2 * kStageBytes + BM * 4];
+    char (*lds)[2][kStageBytes] = reinterpret_cast<char (*)[2][kStageBytes]>(smem);
+    int32_t* tile_targets = reinterpret_cast<int32_t*>(smem + 2 * 2 * kStageBytes);
 
     // ---- which tile: XCD-aware super-blocks ----------------------------------
     // Consecutive workgroups go to the 8 XCDs in turn.  The k-th workgroup an XCD
@@ -108,25 +161,34 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
     const char* a_tile = reinterpret_cast<const char*>(a.H + row0 * a.D);
     const char* b_tile = reinterpret_cast<const char*>(a.W + col0 * a.D);
 
-    auto issue = [&](int kt, int buf) {
+    // The LDS destination of group q is the group-0 slot plus q * 1 KiB; the instruction's
+    // immediate offset moves the LDS and the global address together, so every group
+    // shares one LDS base (M0) and the global address is pre-biased by -q KiB.
+    // DMA of one stage, group by group: groups 0..7 load A rows, 8..15 load W rows.
+    // Group q fills LDS rows wave * 64 + (q % 8) * 8 .. + 7.  Global addresses are a
+    // wave-uniform tile base plus a non-negative 32-bit byte offset (row * 2D + K bytes,
+    // below 256 * 2D), which the hardware zero-extends.
+    auto dma_group = [&](auto qc, int kt, int buf) {
+        constexpr int q = decltype(qc)::value % 8;
+        constexpr bool is_b = decltype(qc)::value >= 8;
         const int64_t k0 = (int64_t)kt * BK;
-        const char* a_k = a_tile + k0 * 2;
-        const char* b_k = b_tile + k0 * 2;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int r = lrow + q * 8;
-            const int ra = r < a_rows ? r : (int)a_rows - 1;
-            const int rb = r < b_rows ? r : (int)b_rows - 1;
-            // K tail: past D, re-read this row's last chunk; zeroed in LDS once it lands
-            const uint32_t kb = (uint32_t)(k0 + koff[q & 1] < a.D ? koff[q & 1] : a.D - 8 - k0) * 2;
-            char* dst_a = &lds[buf][0][(wave * 64 + q * 8) * 128];
-            char* dst_b = &lds[buf][1][(wave * 64 + q * 8) * 128];
-            __builtin_amdgcn_global_load_lds((const void*)(a_k + ((uint32_t)ra * row_bytes + kb)),
-                                             (lds_void_t*)dst_a, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void*)(b_k + ((uint32_t)rb * row_bytes + kb)),
-                                             (lds_void_t*)dst_b, 16, 0, 0);
-        }
+        const int r = lrow + q * 8;
+        const int64_t nrows = is_b ? b_rows : a_rows;
+        const int rr = r < nrows ? r : (int)nrows - 1;
+        // K tail: past D, re-read this row's last chunk; zeroed in LDS once it lands
+        const uint32_t kb = (uint32_t)(k0 + koff[q & 1] < a.D ? koff[q & 1] : a.D - 8 - k0) * 2;
+        const char* g = (is_b ? b_tile : a_tile) + k0 * 2 + ((uint32_t)rr * row_bytes + kb);
+        char* dst = &lds[buf][is_b ? 1 : 0][(wave * 64 + q * 8) * 128];
+        __builtin_amdgcn_global_load_lds((const void*)g, (lds_void_t*)dst, 16, 0, 0);
     };
+    auto issue = [&](int kt, int buf) {
+        [&]<int... Q>(std::integer_sequence<int, Q...>) {
+            (dma_group(std::integral_constant<int, Q>{}, kt, buf), ...);
+        }(std::make_integer_sequence<int, 16>{});
+    };
+    // Waits until the DMA of stage s has landed (loads retire in order; nothing else is
+    // in flight by then).
+    auto wait_stage = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
     // In a K-tail stage the chunks past D hold copies of a valid chunk: overwrite this
     // lane's slots with zeros after its loads have landed, before the barrier that
     // publishes the stage.
@@ -177,23 +239,49 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
             for (int j = 0; j < FB; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     };
-    // 16 MFMAs and 8 LDS reads: one read after every 2 MFMAs
+    // One K16 step is 16 MFMAs and 8 LDS reads: one read after every 2 MFMAs.  The step
+    // that also issues the next stage's 16 DMA loads spreads them the same way, so the
+    // matrix pipe is never left idle while they are issued.
     auto interleave = [&]() {
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
         }
+    };
+    // The K16 step after a stage's barrier: its 16 MFMAs (on fa, fb), the 8 LDS reads of
+    // the next stage's first fragments (into na, nb from buffer cur ^ 1) and the 16 DMA
+    // loads of stage kt_load (into buffer cur), in 8 chunks of 2 MFMAs + 1 read + 2 loads.
+    // The scheduler keeps the chunk order, so the DMA issue never idles the matrix pipe.
+    auto step_with_dma = [&](int kt_load, int cur, const bf16x8 (&fa)[FB], const bf16x8 (&fb)[FB],
+                             bf16x8 (&na)[FB], bf16x8 (&nb)[FB]) {
+        const char* As = &lds[cur ^ 1][0][wm * WT * 128];
+        const char* Bs = &lds[cur ^ 1][1][wn * WT * 128];
+        auto chunk = [&](auto cc) {
+            constexpr int c = decltype(cc)::value;
+            constexpr int i = c / 2, j0 = 2 * (c % 2);
+            acc[i][j0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j0], acc[i][j0], 0, 0, 0);
+            acc[i][j0 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j0 + 1], acc[i][j0 + 1], 0, 0, 0);
+            if constexpr (c < 4)
+                na[c] = *reinterpret_cast<const bf16x8*>(As + c * 32 * 128 + off[0]);
+            else
+                nb[c - 4] = *reinterpret_cast<const bf16x8*>(Bs + (c - 4) * 32 * 128 + off[0]);
+            dma_group(std::integral_constant<int, 2 * c>{}, kt_load, cur);
+            dma_group(std::integral_constant<int, 2 * c + 1>{}, kt_load, cur);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        [&]<int... C>(std::integer_sequence<int, C...>) {
+            (chunk(std::integral_constant<int, C>{}), ...);
+        }(std::make_integer_sequence<int, 8>{});
     };
     auto sync_stage = [&](int kt, int cur, int nk) {
         // stage kt + 1 has landed (issued one stage earlier); after this barrier every
         // wave has finished reading buffer `cur`, which then takes stage kt + 2
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        wait_stage();
         if (kt + 1 < nk) zero_tail(kt + 1, cur ^ 1);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (kt + 2 < nk) issue(kt + 2, cur);
     };
 
     // Pipeline: the four K16 steps of a stage each run their 16 MFMAs while the
@@ -201,8 +289,10 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
     // first fragments of the next stage, after the stage's single barrier.
     const int nk = (int)((a.D + BK - 1) / BK);
     bf16x8 fa0[FB], fb0[FB], fa1[FB], fb1[FB];
+    // targets of this tile's rows, for the epilogue
+    tile_targets[tid] = row0 + tid < a.N ? a.targets[row0 + tid] : -1;
     issue(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_stage();
     zero_tail(0, 0);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -221,9 +311,9 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
         mfma_all(fa0, fb0);
         interleave();
         sync_stage(kt, cur, nk);
-        read_frags(cur ^ 1, 0, fa0, fb0);
-        mfma_all(fa1, fb1);
-        interleave();
+        // the last stage re-issues stage nk - 1 into the free buffer, which is never read:
+        // no branch around the DMA, so it can interleave with the MFMAs
+        step_with_dma(kt + 2 < nk ? kt + 2 : nk - 1, cur, fa1, fb1, fa0, fb0);
     }
     {
         const int cur = (nk - 1) & 1;
@@ -238,6 +328,8 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
         interleave();
         mfma_all(fa1, fb1);
     }
+    // the last loop iteration's (redundant) DMA must land before the workgroup can end
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // ---- epilogue: (m, s) per row over this wave's 128 columns ----------------
     // acc[i][j][e] holds Z[row = wm*128 + i*32 + 8*(e/4) + 4*h2 + e%4][col = wn*128 + j*32 + l32].
@@ -251,22 +343,25 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
 #pragma unroll
     for (int i = 0; i < FB; ++i) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int64_t r = wrow0 + i * 32 + 8 * (e / 4) + 4 * h2 + (e % 4);
-            if (r < a.N) {
-                const int64_t yrel = (int64_t)a.targets[r] - wcol0;
+        for (int c = 0; c < 4; ++c) {
+            const int lr = wm * WT + i * 32 + 8 * c + 4 * h2;  // 4 consecutive rows e = 4c..4c+3
+            const int4 y4 = *reinterpret_cast<const int4*>(&tile_targets[lr]);
+            const int ys[4] = {y4.x, y4.y, y4.z, y4.w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int64_t yrel = (int64_t)ys[t] - wcol0;
                 if (yrel >= 0 && yrel < WT && (int)(yrel & 31) == l32) {
                     const int jj = (int)(yrel >> 5);
                     float v = 0.f;
 #pragma unroll
-                    for (int j = 0; j < FB; ++j) v = (j == jj) ? acc[i][j][e] : v;
-                    a.zy[r] = v;
+                    for (int j = 0; j < FB; ++j) v = (j == jj) ? acc[i][j][4 * c + t] : v;
+                    a.zy[row0 + lr + t] = v;  // a valid target implies a valid row
                 }
             }
         }
     }
 
-    MS st[64];  // state index i * 16 + e
+    MS st[64];  // state index i * 16 + e: this lane's 4 columns of one row
 #pragma unroll
     for (int i = 0; i < FB; ++i) {
 #pragma unroll
@@ -274,28 +369,19 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
             float v[FB];
 #pragma unroll
             for (int j = 0; j < FB; ++j) v[j] = col_ok[j] ? acc[i][j][e] : kNegInf;
-            MS s0 = ms_empty();
-            ms_add<FB>(s0, v);
-            st[i * 16 + e] = s0;
+            st[i * 16 + e] = ms_of<FB>(v);
         }
     }
-    // Reduce-scatter across the 32 lanes that share a row set (lane bits 4..0): at each
-    // step a lane keeps one half of its states, sends the other half to its partner and
-    // merges what it receives.  After five steps lane l32 holds states 2*l32, 2*l32+1.
-#pragma unroll
-    for (int step = 0; step < 5; ++step) {
-        const int mask = 16 >> step;
-        const int half = 32 >> step;  // states held before this step: 2 * half
-        const bool upper = (lane & mask) != 0;
-#pragma unroll
-        for (int k = 0; k < half; ++k) {
-            const MS lo = st[k], hi = st[k + half];
-            const MS keep = upper ? hi : lo;
-            const MS send = upper ? lo : hi;
-            MS recv{__shfl_xor(send.m, mask, 32), __shfl_xor(send.s, mask, 32)};
-            st[k] = ms_merge(keep, recv);
-        }
-    }
+    // Reduce-scatter across the 32 lanes that share a row set: at each step a lane keeps
+    // one half of its states, sends the other half to its partner and merges what it
+    // receives; after five steps lane l32 holds states 2*l32 and 2*l32 + 1.  Partners
+    // differ in lane bit 4, 3, 2, 1, 0 in turn (for bit 2 the partner is the mirror lane
+    // within 8, 7 - i, which also differs in bit 2).
+    reduce_scatter_step<0, 32>(st, lane);
+    reduce_scatter_step<1, 16>(st, lane);
+    reduce_scatter_step<2, 8>(st, lane);
+    reduce_scatter_step<3, 4>(st, lane);
+    reduce_scatter_step<4, 2>(st, lane);
     // state 2*l32 + t  ->  i = l32 / 8, e = 2 * (l32 % 8) + t
     const int64_t slab = (int64_t)col_tile * 2 + wn;
 #pragma unroll
