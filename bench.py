@@ -19,6 +19,7 @@ per-kernel-call durations.  Prints ONE JSON line.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -32,6 +33,41 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 
 METRIC = "fused CE fwd+VJP ms & GB/s (% HBM peak); linear-CE fwd TFLOP/s (% MFMA)"
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "softmax_cross_entropy_amd", "csrc")
+
+# HBM traffic per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this script
+# (--steps 1 --warmup 0 --calibrate-copy 1024), each scaled by the same counter on a
+# copy of known size; see profiles/.  Keyed by the sha256 of the kernel's source file
+# at measurement time: a changed kernel reports traffic null until it is measured again.
+TRAFFIC = {
+    "ce_forward": {
+        "source_sha": "e6ff2b676f9a9c6b",
+        "bytes": 622740871
+    },
+    "ce_vjp": {
+        "source_sha": "e6ff2b676f9a9c6b",
+        "bytes": 1245046179
+    },
+    "lce_forward": {
+        "source_sha": "ad705f3f61532e7a",
+        "bytes": 15155200468
+    },
+}
+
+
+def source_sha(kernel):
+    fname = "lce_kernels.hip" if kernel.startswith("lce") else "ce_kernels.hip"
+    with open(os.path.join(CSRC, fname), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(kernel):
+    t = TRAFFIC.get(kernel)
+    if not t or t.get("source_sha") != source_sha(kernel):
+        return None
+    return t["bytes"]
 
 
 def ce_bytes(rows, V, e):
@@ -91,6 +127,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--parts", default="ce,lce", help="comma list of ce, lce")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="run one elementwise copy (torch.neg) of MIB MiB fp32 first, so a counter "
+                         "profile holds a kernel of known traffic")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -125,6 +164,17 @@ def main():
         lloss = torch.empty(LCE_N, device=dev)
         llse = torch.empty(LCE_N, 2, device=dev)
         ws = torch.empty(abi.lce_workspace_size(LCE_N, LCE_D, LCE_V), dtype=torch.uint8, device=dev)
+
+    calib = None
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        calib = {"kernel": "torch.neg fp32", "bytes_read": n * 4, "bytes_written": n * 4}
+        del src, dst
 
     stream = torch.cuda.current_stream(dev)
     n_ev = 4
@@ -180,7 +230,8 @@ def main():
         for name, byts, t in (("ce_forward", fwd_b, f_ms), ("ce_vjp", vjp_b, v_ms)):
             a = byts / (t * 1e-3) / 1e9
             rooflines[name] = {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                               "frac": a / HBM_PEAK_GBS, "traffic": None, "ms": t, "algorithmic_bytes": byts}
+                               "frac": a / HBM_PEAK_GBS, "traffic": traffic_for(name), "ms": t,
+                               "algorithmic_bytes": byts}
         cfg["workload"].append(f"ce_forward+ce_vjp bf16 [{CE_ROWS} x {CE_V}]")
         cfg["ce"] = {"rows": CE_ROWS, "V": CE_V, "dtype": "bf16"}
         out["value"] = gbs
@@ -192,7 +243,8 @@ def main():
         parts_out["lce_forward"] = {"ms": l_ms, "TFLOP_s": tf, "frac_mfma_bf16_peak": tf / MFMA_BF16_PEAK_TFLOPS,
                                     "flop": fl}
         rooflines["lce_forward"] = {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS,
-                                    "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                                    "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS,
+                                    "traffic": traffic_for("lce_forward"),
                                     "ms": l_ms, "algorithmic_flop": fl,
                                     "kernels": "lce_tile_mfma + lce_merge (one lce_forward call)"}
         cfg["workload"].append(f"lce_forward bf16 N={LCE_N} D={LCE_D} V={LCE_V}")
@@ -207,6 +259,8 @@ def main():
     dom = max(rooflines, key=lambda k: rooflines[k]["ms"])
     out["roofline"] = dict(rooflines[dom], kernel=dom)
     out["rooflines"] = rooflines
+    if calib:
+        out["calibration"] = calib
     if not args.no_cpu and ce_batch is not None and lce_in is not None:
         out["cpu_baseline"] = cpu_baseline(ce_batch, lce_in)
     else:
