@@ -60,9 +60,10 @@ __device__ __forceinline__ void store_forward(const FwdArgs& a, int64_t r, MS st
 }
 
 // Streams this lane's share of one row into `st`: vectors lane, lane + G, ... in
-// groups of U.  The loads of the next group are issued before the current group is
-// folded in, so each lane keeps U vectors in flight while it computes.  Then the
-// scalar head and tail elements.
+// groups of U loads issued together, then the scalar head and tail elements.  There
+// is no software pipelining across groups on purpose: a second group buffer would
+// push the kernel past 64 VGPRs and halve the workgroups resident per CU, and the
+// other resident waves hide load latency better than one wave's own prefetch does.
 template <typename T, int U>
 __device__ __forceinline__ void fold_group(MS& st, const U4 (&buf)[U]) {
     constexpr int kVec = Elem<T>::kVec;
@@ -82,30 +83,16 @@ __device__ __forceinline__ void stream_row(const T* row, int64_t V, int lane, MS
     constexpr int kVec = Elem<T>::kVec;
     RowSplit<T> sp(row, V);
     const char* vb = reinterpret_cast<const char*>(row + sp.head);
-    constexpr int64_t kStep = (int64_t)U * G;
     int64_t j = lane;
-    if (j + (int64_t)(U - 1) * G < sp.nvec) {
-        U4 cur[U];
+    for (; j + (int64_t)(U - 1) * G < sp.nvec; j += (int64_t)U * G) {
+        U4 buf[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) cur[u] = load_u4(vb + (j + (int64_t)u * G) * 16);
-        while (true) {
-            const int64_t jn = j + kStep;
-            const bool more = jn + (int64_t)(U - 1) * G < sp.nvec;
-            U4 nxt[U];
-            if (more) {
-#pragma unroll
-                for (int u = 0; u < U; ++u) nxt[u] = load_u4(vb + (jn + (int64_t)u * G) * 16);
-            }
-            fold_group<T, U>(st, cur);
-            j = jn;
-            if (!more) break;
-#pragma unroll
-            for (int u = 0; u < U; ++u) cur[u] = nxt[u];
-        }
+        for (int u = 0; u < U; ++u) buf[u] = load_u4_stream(vb + (j + (int64_t)u * G) * 16);
+        fold_group<T, U>(st, buf);
     }
     for (; j < sp.nvec; j += G) {
         float f[kVec];
-        Elem<T>::unpack(load_u4(vb + j * 16), f);
+        Elem<T>::unpack(load_u4_stream(vb + j * 16), f);
         ms_add<kVec>(st, f);
     }
     const int64_t ns = sp.n_scalar(V);
@@ -129,7 +116,7 @@ __global__ __launch_bounds__(kBlock) void ce_fwd_narrow(FwdArgs a) {
             if (r < a.n_rows) {
                 const char* row = reinterpret_cast<const char*>(base + row_offset(r, a.in));
 #pragma unroll
-                for (int v = 0; v < NV; ++v) buf[u][v] = load_u4(row + v * 16);
+                for (int v = 0; v < NV; ++v) buf[u][v] = load_u4_stream(row + v * 16);
                 ys[u] = a.targets[r];
             }
         }
@@ -217,8 +204,8 @@ __global__ __launch_bounds__(64 * NW) void ce_fwd_rowwg(FwdArgs a) {
 // ---- VJP ------------------------------------------------------------------------
 
 struct RowGrad {
-    float m;   // row maximum, or NaN for a row whose target is out of range
-    float ls;  // log of the scaled sum
+    float m;    // row maximum, or NaN for a row whose target is out of range
+    float lsl;  // log(s) * log2(e)
     float g;
     int32_t y;
 };
@@ -228,22 +215,44 @@ __device__ __forceinline__ RowGrad load_row_grad(const VjpArgs& a, int64_t r) {
     rg.y = a.targets[r];
     const float2 l = a.lse[r];
     rg.m = target_ok(rg.y, a.V) ? l.x : __builtin_nanf("");
-    rg.ls = l.y;
+    rg.lsl = l.y * kLog2e;
     rg.g = a.g[r];
     return rg;
 }
 
+// softmax probability of logit z: exp((z - m) - log s) = 2^((z - m) log2 e - log s log2 e).
+// z - m is formed first (exact for nearby logits), and one fused multiply-add applies
+// log2 e and subtracts log s: no large magnitude ever meets the small gap.
+__device__ __forceinline__ float prob(float z, const RowGrad& rg) {
+    return __builtin_amdgcn_exp2f(__builtin_fmaf(z - rg.m, kLog2e, -rg.lsl));
+}
+
 __device__ __forceinline__ float grad_elem(float z, const RowGrad& rg, bool is_target) {
-    float p = exp_e((z - rg.m) - rg.ls);
+    const float p = prob(z, rg);
     return rg.g * (is_target ? p - 1.0f : p);
 }
 
-template <typename T, int N>
-__device__ __forceinline__ void grad_vec(float (&f)[N], const RowGrad& rg, int64_t first) {
-    const int64_t rel = (int64_t)rg.y - first;
-    const int yr = (rel >= 0 && rel < N) ? (int)rel : -1;
+// Gradient of one 16-byte vector of logits, written to `dst` inside output row `orow`.  Every element is
+// stored as g * p first; the one lane whose vector holds the target column (elements
+// first .. first + kVec - 1) then stores that element again as g * (p - 1).  Both
+// stores come from the same lane to the same address, so they land in program order,
+// and the common path carries no per-element target test.
+template <typename T>
+__device__ __forceinline__ void grad_store_vec(const U4& in, const RowGrad& rg, int64_t first, char* dst,
+                                               T* orow) {
+    constexpr int kVec = Elem<T>::kVec;
+    float f[kVec], out[kVec];
+    Elem<T>::unpack(in, f);
 #pragma unroll
-    for (int k = 0; k < N; ++k) f[k] = grad_elem(f[k], rg, k == yr);
+    for (int k = 0; k < kVec; ++k) out[k] = rg.g * prob(f[k], rg);
+    store_u4(dst, Elem<T>::pack(out));
+    const int64_t rel = (int64_t)rg.y - first;
+    if ((uint64_t)rel < (uint64_t)kVec) {
+        float zy = f[0];
+#pragma unroll
+        for (int k = 1; k < kVec; ++k) zy = rel == k ? f[k] : zy;
+        Elem<T>::store1(orow + rg.y, grad_elem(zy, rg, true));
+    }
 }
 
 template <typename T, int NV, int UR>
@@ -271,12 +280,9 @@ __global__ __launch_bounds__(kBlock) void ce_vjp_narrow(VjpArgs a) {
             if (r < a.n_rows) {
                 char* orow = reinterpret_cast<char*>(obase + row_offset(r, a.out));
 #pragma unroll
-                for (int v = 0; v < NV; ++v) {
-                    float f[kVec];
-                    Elem<T>::unpack(buf[u][v], f);
-                    grad_vec<T, kVec>(f, rg[u], (int64_t)v * kVec);
-                    store_u4(orow + v * 16, Elem<T>::pack(f));
-                }
+                for (int v = 0; v < NV; ++v)
+                    grad_store_vec<T>(buf[u][v], rg[u], (int64_t)v * kVec, orow + v * 16,
+                                      reinterpret_cast<T*>(orow));
             }
         }
     }
@@ -304,19 +310,12 @@ __global__ __launch_bounds__(G > kBlock ? G : kBlock) void ce_vjp_lanes(VjpArgs 
 #pragma unroll
                 for (int u = 0; u < U; ++u) buf[u] = load_u4(vb + (j + (int64_t)u * G) * 16);
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    float f[kVec];
-                    Elem<T>::unpack(buf[u], f);
-                    grad_vec<T, kVec>(f, rg, sp.head + (j + (int64_t)u * G) * kVec);
-                    store_u4(ob + (j + (int64_t)u * G) * 16, Elem<T>::pack(f));
-                }
+                for (int u = 0; u < U; ++u)
+                    grad_store_vec<T>(buf[u], rg, sp.head + (j + (int64_t)u * G) * kVec,
+                                      ob + (j + (int64_t)u * G) * 16, orow);
             }
-            for (; j < sp.nvec; j += G) {
-                float f[kVec];
-                Elem<T>::unpack(load_u4(vb + j * 16), f);
-                grad_vec<T, kVec>(f, rg, sp.head + j * kVec);
-                store_u4(ob + j * 16, Elem<T>::pack(f));
-            }
+            for (; j < sp.nvec; j += G)
+                grad_store_vec<T>(load_u4(vb + j * 16), rg, sp.head + j * kVec, ob + j * 16, orow);
             const int64_t ns = sp.n_scalar(a.V);
             for (int64_t k = lane; k < ns; k += G) {
                 const int64_t idx = sp.scalar_index(k);

@@ -146,14 +146,16 @@ template <> struct Elem<__bf16> {
     __device__ static __forceinline__ float load1(const __bf16* p) {
         return __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, *p) << 16);
     }
-    // float -> bfloat16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
-    __device__ static __forceinline__ uint32_t bits(float v) {
-        return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v);
+    // float pair -> packed bfloat16 pair, round to nearest even: one v_cvt_pk_bf16_f32.
+    __device__ static __forceinline__ uint32_t bits2(float lo, float hi) {
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){lo, hi}, b2));
     }
     __device__ static __forceinline__ U4 pack(const float (&f)[8]) {
         U4 u;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) u.w[k] = bits(f[2 * k]) | (bits(f[2 * k + 1]) << 16);
+        for (int k = 0; k < 4; ++k) u.w[k] = bits2(f[2 * k], f[2 * k + 1]);
         return u;
     }
     __device__ static __forceinline__ void store1(__bf16* p, float v) { *p = (__bf16)v; }
@@ -199,6 +201,15 @@ struct RowSplit {
 
 __device__ __forceinline__ U4 load_u4(const void* p) {
     return *reinterpret_cast<const U4*>(p);
+}
+
+// The same load with the non-temporal hint, for a stream read once per call.
+__device__ __forceinline__ U4 load_u4_stream(const void* p) {
+    const U4* q = reinterpret_cast<const U4*>(p);
+    U4 u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) u.w[k] = __builtin_nontemporal_load(&q->w[k]);
+    return u;
 }
 
 __device__ __forceinline__ void store_u4(void* p, const U4& u) {
