@@ -270,7 +270,7 @@ __global__ __launch_bounds__(kBlock) void ce_vjp_narrow(VjpArgs a) {
             if (r < a.n_rows) {
                 const char* row = reinterpret_cast<const char*>(base + row_offset(r, a.in));
 #pragma unroll
-                for (int v = 0; v < NV; ++v) buf[u][v] = load_u4(row + v * 16);
+                for (int v = 0; v < NV; ++v) buf[u][v] = load_u4_stream(row + v * 16);
                 rg[u] = load_row_grad(a, r);
             }
         }
@@ -308,14 +308,14 @@ __global__ __launch_bounds__(G > kBlock ? G : kBlock) void ce_vjp_lanes(VjpArgs 
             for (; j + (int64_t)(U - 1) * G < sp.nvec; j += (int64_t)U * G) {
                 U4 buf[U];
 #pragma unroll
-                for (int u = 0; u < U; ++u) buf[u] = load_u4(vb + (j + (int64_t)u * G) * 16);
+                for (int u = 0; u < U; ++u) buf[u] = load_u4_stream(vb + (j + (int64_t)u * G) * 16);
 #pragma unroll
                 for (int u = 0; u < U; ++u)
                     grad_store_vec<T>(buf[u], rg, sp.head + (j + (int64_t)u * G) * kVec,
                                       ob + (j + (int64_t)u * G) * 16, orow);
             }
             for (; j < sp.nvec; j += G)
-                grad_store_vec<T>(load_u4(vb + j * 16), rg, sp.head + j * kVec, ob + j * 16, orow);
+                grad_store_vec<T>(load_u4_stream(vb + j * 16), rg, sp.head + j * kVec, ob + j * 16, orow);
             const int64_t ns = sp.n_scalar(a.V);
             for (int64_t k = lane; k < ns; k += G) {
                 const int64_t idx = sp.scalar_index(k);

@@ -199,11 +199,10 @@ struct RowSplit {
     __device__ __forceinline__ int64_t n_scalar(int64_t V) const { return head + (V - tail0); }
 };
 
-__device__ __forceinline__ U4 load_u4(const void* p) {
-    return *reinterpret_cast<const U4*>(p);
-}
-
-// The same load with the non-temporal hint, for a stream read once per call.
+// 16-byte load with the non-temporal hint: every logit is read once per call (the
+// forward and the VJP each stream the whole batch, which is larger than the caches),
+// so the lines are not worth keeping.  Stores stay ordinary; marking them
+// non-temporal measured slower.
 __device__ __forceinline__ U4 load_u4_stream(const void* p) {
     const U4* q = reinterpret_cast<const U4*>(p);
     U4 u;
