@@ -10,8 +10,9 @@
 //   lce_tile   one 256 x 256 tile of Z per workgroup (bf16 MFMA 32x32x16, fp32 accumulate,
 //              K = D streamed through LDS in 64-wide double-buffered stages).  Its
 //              epilogue turns the fp32 accumulators straight into one (m, s) pair per
-//              row for each 128-column slab, and stores the target logit from the
-//              same accumulator when the target column is in the slab.
+//              row for each 128-column slab (exact slab maximum, then one exponential
+//              per logit), and stores the target logit from the same accumulator when
+//              the target column is in the slab.
 //   lce_merge  folds the slabs of each row in slab order into (m, s), then
 //              loss = (m - z_y) + log s and lse = (m, log s).
 // Workspace: partial (m, s) float2 [N][n_slabs], then z_y float [N].
@@ -63,53 +64,6 @@ struct TileArgs {
 // The chunk index is XORed with (row / 2) % 8 so that the 16 rows an MFMA operand
 // read touches at one K chunk land in 16 different 16-byte bank groups:
 //   byte offset of (row, chunk) = row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4).
-
-// ---- epilogue helpers ------------------------------------------------------------
-
-// (m, s) of N values directly: one max, N exponentials, no rescale.
-template <int N>
-__device__ __forceinline__ MS ms_of(const float (&v)[N]) {
-    float m = v[0];
-#pragma unroll
-    for (int k = 1; k < N; ++k) m = fmaxf(m, v[k]);
-    const float r = ref_point(m);
-    float s = 0.f;
-#pragma unroll
-    for (int k = 0; k < N; ++k) s += exp_e(v[k] - r);
-    return MS{m, s};
-}
-
-// Value held by this lane's partner for reduce-scatter step STEP (partner lane differs in
-// bit 4 - STEP): DPP within 16-lane rows for bits 3..0, a swizzle for bit 4.
-template <int STEP>
-__device__ __forceinline__ float partner(float v) {
-    const int x = __float_as_int(v);
-    int y;
-    if constexpr (STEP == 0)
-        y = __builtin_amdgcn_ds_swizzle(x, 0x401F);  // lane ^ 16 within 32
-    else if constexpr (STEP == 1)
-        y = __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);  // row_ror:8 = lane ^ 8 within 16
-    else if constexpr (STEP == 2)
-        y = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false);  // row_half_mirror: 7 - i within 8
-    else if constexpr (STEP == 3)
-        y = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1] = lane ^ 2
-    else
-        y = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2] = lane ^ 1
-    return __int_as_float(y);
-}
-
-template <int STEP, int HALF>
-__device__ __forceinline__ void reduce_scatter_step(MS (&st)[64], int lane) {
-    const bool upper = ((lane >> (4 - STEP)) & 1) != 0;
-#pragma unroll
-    for (int k = 0; k < HALF; ++k) {
-        const MS lo = st[k], hi = st[k + HALF];
-        const MS keep = upper ? hi : lo;
-        const MS send = upper ? lo : hi;
-        const MS recv{partner<STEP>(send.m), partner<STEP>(send.s)};
-        st[k] = ms_merge(keep, recv);
-    }
-}
 
 __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
     // One LDS object (the compiler then sees the DMA writes and the fragment reads as
@@ -207,7 +161,11 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
 
     // v_mfma_f32_32x32x16_bf16: lane l supplies row l % 32 of the A block and column
     // l % 32 of the B block, K elements 8 * (l / 32) .. + 7 of the 16; it receives
-    // D[row = 8 * (e / 4) + 4 * (l / 32) + e % 4][col = l % 32] in element e.
+    // D[row = 8 * (e / 4) + 4 * (l / 32) + e % 4][col = l % 32] in element e.  The two
+    // operands have the same register layout, so the W fragment is passed as A and the
+    // H fragment as B: D is then a block of Z^T, and each lane collects 16 vocabulary
+    // columns of one token row per block, which keeps the epilogue's row reductions
+    // inside the lane.
     f32x16 acc[FB][FB];
 #pragma unroll
     for (int i = 0; i < FB; ++i)
@@ -237,7 +195,7 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
         for (int i = 0; i < FB; ++i)
 #pragma unroll
             for (int j = 0; j < FB; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
     };
     // One K16 step is 16 MFMAs and 8 LDS reads: one read after every 2 MFMAs.  The step
     // that also issues the next stage's 16 DMA loads spreads them the same way, so the
@@ -260,8 +218,8 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
         auto chunk = [&](auto cc) {
             constexpr int c = decltype(cc)::value;
             constexpr int i = c / 2, j0 = 2 * (c % 2);
-            acc[i][j0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j0], acc[i][j0], 0, 0, 0);
-            acc[i][j0 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j0 + 1], acc[i][j0 + 1], 0, 0, 0);
+            acc[i][j0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j0], fa[i], acc[i][j0], 0, 0, 0);
+            acc[i][j0 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j0 + 1], fa[i], acc[i][j0 + 1], 0, 0, 0);
             if constexpr (c < 4)
                 na[c] = *reinterpret_cast<const bf16x8*>(As + c * 32 * 128 + off[0]);
             else
@@ -332,64 +290,79 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // ---- epilogue: (m, s) per row over this wave's 128 columns ----------------
-    // acc[i][j][e] holds Z[row = wm*128 + i*32 + 8*(e/4) + 4*h2 + e%4][col = wn*128 + j*32 + l32].
+    // acc[i][j][e] holds Z[row = wrow0 + i*32 + l32][col = wcol0 + j*32 + 8*(e/4) + 4*h2 + e%4]:
+    // this lane holds 64 of the wave's 128 columns of 4 rows, lane ^ 32 the other 64.
     const int64_t wcol0 = col0 + wn * WT;
     const int64_t wrow0 = row0 + wm * WT;
-    bool col_ok[FB];
-#pragma unroll
-    for (int j = 0; j < FB; ++j) col_ok[j] = wcol0 + j * 32 + l32 < a.V;
+    auto col_of = [&](int j, int e) { return j * 32 + 8 * (e / 4) + 4 * h2 + (e % 4); };
 
-    // target logits: captured from the accumulator that holds the target column
+    // target logits: the lane holding the target column of a row stores it.  A row's
+    // target lies in this wave's columns for about one wave in ten, so the select runs
+    // rarely and only in those lanes: column c = j*32 + 8*(e/4) + 4*h2 + e%4 gives
+    // j = c / 32 and e = 4 * ((c / 8) % 4) + c % 4; pick j first, then e.
 #pragma unroll
     for (int i = 0; i < FB; ++i) {
+        const int lr = wm * WT + i * 32 + l32;
+        const int64_t yrel = (int64_t)tile_targets[lr] - wcol0;
+        if (yrel >= 0 && yrel < WT && (((int)yrel >> 2) & 1) == h2) {
+            const int c = (int)yrel;
+            const int jj = c >> 5, ee = (((c >> 3) & 3) << 2) | (c & 3);
+            float v = 0.f;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int lr = wm * WT + i * 32 + 8 * c + 4 * h2;  // 4 consecutive rows e = 4c..4c+3
-            const int4 y4 = *reinterpret_cast<const int4*>(&tile_targets[lr]);
-            const int ys[4] = {y4.x, y4.y, y4.z, y4.w};
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int64_t yrel = (int64_t)ys[t] - wcol0;
-                if (yrel >= 0 && yrel < WT && (int)(yrel & 31) == l32) {
-                    const int jj = (int)(yrel >> 5);
-                    float v = 0.f;
-#pragma unroll
-                    for (int j = 0; j < FB; ++j) v = (j == jj) ? acc[i][j][4 * c + t] : v;
-                    a.zy[row0 + lr + t] = v;  // a valid target implies a valid row
-                }
+            for (int e = 0; e < 16; ++e) {
+                const float lo = (jj & 1) ? acc[i][1][e] : acc[i][0][e];
+                const float hi = (jj & 1) ? acc[i][3][e] : acc[i][2][e];
+                v = ee == e ? ((jj & 2) ? hi : lo) : v;
             }
+            a.zy[row0 + lr] = v;  // a valid target implies a valid row
         }
     }
 
-    MS st[64];  // state index i * 16 + e: this lane's 4 columns of one row
-#pragma unroll
-    for (int i = 0; i < FB; ++i) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            float v[FB];
-#pragma unroll
-            for (int j = 0; j < FB; ++j) v[j] = col_ok[j] ? acc[i][j][e] : kNegInf;
-            st[i * 16 + e] = ms_of<FB>(v);
-        }
-    }
-    // Reduce-scatter across the 32 lanes that share a row set: at each step a lane keeps
-    // one half of its states, sends the other half to its partner and merges what it
-    // receives; after five steps lane l32 holds states 2*l32 and 2*l32 + 1.  Partners
-    // differ in lane bit 4, 3, 2, 1, 0 in turn (for bit 2 the partner is the mirror lane
-    // within 8, 7 - i, which also differs in bit 2).
-    reduce_scatter_step<0, 32>(st, lane);
-    reduce_scatter_step<1, 16>(st, lane);
-    reduce_scatter_step<2, 8>(st, lane);
-    reduce_scatter_step<3, 4>(st, lane);
-    reduce_scatter_step<4, 2>(st, lane);
-    // state 2*l32 + t  ->  i = l32 / 8, e = 2 * (l32 % 8) + t
+    // Per row: the exact maximum over the 128 columns (this lane's 64, then lane ^ 32's),
+    // then sum exp(z - m) with one exponential per logit, and the partner's sum.  Both
+    // lanes of a pair end with the same (m, s); the lower one stores it.  Columns past V
+    // hold copies of the last W row and count as -inf: only the last column tile has
+    // any, so the masked form is a separate instance (the accumulators stay read-only).
     const int64_t slab = (int64_t)col_tile * 2 + wn;
+    auto row_states = [&](auto mask_c) {
+        constexpr bool kMask = decltype(mask_c)::value;
+        auto z = [&](int i, int j, int e) {
+            if constexpr (kMask)
+                return wcol0 + col_of(j, e) < a.V ? acc[i][j][e] : kNegInf;
+            else
+                return acc[i][j][e];
+        };
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int e = 2 * (l32 & 7) + t;
-        const int64_t r = wrow0 + (l32 >> 3) * 32 + 8 * (e / 4) + 4 * h2 + (e % 4);
-        if (r < a.N) a.partial[r * a.n_slabs + slab] = make_float2(st[t].m, st[t].s);
-    }
+        for (int i = 0; i < FB; ++i) {
+            float mj[FB];
+#pragma unroll
+            for (int j = 0; j < FB; ++j) {
+                float t = z(i, j, 0);
+#pragma unroll
+                for (int e = 1; e < 16; ++e) t = fmaxf(t, z(i, j, e));
+                mj[j] = t;
+            }
+            float m = fmaxf(fmaxf(mj[0], mj[1]), fmaxf(mj[2], mj[3]));
+            m = fmaxf(m, __shfl_xor(m, 32));
+            const float r = ref_point(m);
+            float sj[FB];
+#pragma unroll
+            for (int j = 0; j < FB; ++j) {
+                float t = 0.f;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) t += exp_e(z(i, j, e) - r);
+                sj[j] = t;
+            }
+            float s = (sj[0] + sj[1]) + (sj[2] + sj[3]);
+            s += __shfl_xor(s, 32);
+            const int64_t row = wrow0 + i * 32 + l32;
+            if (h2 == 0 && row < a.N) a.partial[row * a.n_slabs + slab] = make_float2(m, s);
+        }
+    };
+    if (wcol0 + WT > a.V)
+        row_states(std::true_type{});
+    else
+        row_states(std::false_type{});
 }
 
 constexpr int kMergeThreads = 256;
