@@ -40,27 +40,32 @@ CSRC = os.path.join(ROOT, "softmax_cross_entropy_amd", "csrc")
 # HBM traffic per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this script
 # (--steps 1 --warmup 0 --calibrate-copy 1024), each scaled by the same counter on a
 # copy of known size; see profiles/.  Keyed by the sha256 of the kernel's source file
-# at measurement time: a changed kernel reports traffic null until it is measured again.
+# and device header at measurement time: a changed kernel reports traffic null until it is measured again.
 TRAFFIC = {
     "ce_forward": {
-        "source_sha": "e6ff2b676f9a9c6b",
-        "bytes": 622740871
+        "source_sha": "e0eaeaabbba34d72",
+        "bytes": 622629720
     },
     "ce_vjp": {
-        "source_sha": "e6ff2b676f9a9c6b",
-        "bytes": 1245046179
+        "source_sha": "e0eaeaabbba34d72",
+        "bytes": 1245124781
     },
     "lce_forward": {
-        "source_sha": "ad705f3f61532e7a",
-        "bytes": 15155200468
+        "source_sha": "910ab9952babd6d2",
+        "bytes": 15154197279
     },
 }
 
 
 def source_sha(kernel):
+    """sha256 (first 16 hex digits) of the kernel's source file and the device header it
+    includes."""
     fname = "lce_kernels.hip" if kernel.startswith("lce") else "ce_kernels.hip"
-    with open(os.path.join(CSRC, fname), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in (fname, "device_common.h"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_for(kernel):

@@ -57,8 +57,12 @@ typedef enum { CE_F32 = 0, CE_F16 = 1, CE_BF16 = 2 } ce_dtype;
  * non-contiguous inputs on Metal", Describe the bug: the gradient of the
  * next-token loss over the view logits[:, :-1] came back wrong when the view was
  * copied into a temporary whose buffer the output shared.)
- * Requirements: rows_per_batch >= 1, row_stride >= V, batch_stride >= 0, and the
- * base pointer aligned to the element size.
+ * Requirements: rows_per_batch >= 1, row_stride >= 0, batch_stride >= 0, and the
+ * base pointer aligned to the element size.  An input view may overlap itself (for
+ * example row_stride 0 repeats one row).  An output view (dlogits) must not: when it
+ * has more than one row, row_stride >= V, and when it spans more than one batch,
+ * batch_stride >= (rows_per_batch - 1) * row_stride + V.  A layout that breaks these
+ * rules, or whose furthest element lies beyond 1e18 elements, returns CE_ERR_LAYOUT.
  */
 typedef struct {
     int64_t rows_per_batch;
