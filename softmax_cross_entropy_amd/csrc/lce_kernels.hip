@@ -90,7 +90,9 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
     if (row_tile >= a.n_row_tiles || col_tile >= a.n_col_tiles) return;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    // Wave index read into a scalar register, so that the per-load LDS destinations (M0)
+    // are computed with scalar adds instead of a vector add and a v_readfirstlane each.
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int64_t row0 = (int64_t)row_tile * BM;
     const int64_t col0 = (int64_t)col_tile * BN;
