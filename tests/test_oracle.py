@@ -343,6 +343,107 @@ def test_lce_row_subset():
     np.testing.assert_array_equal(sub, full[rows])
 
 
+# --- linear cross-entropy gradients (Ineshin, section 1: the backward regenerates
+# the logits from the saved log-sum-exp) ---------------------------------------
+
+def lce_objective(H64, W64, y, g):
+    """sum_i g_i loss_i with the pinned softmax cross-entropy forward."""
+    loss, _, _ = oce.forward(H64 @ W64.T, y)
+    return float(np.dot(g, loss))
+
+
+def pin_lce_grad_finite_differences(seed=0, N=6, D=5, V=7, h=1e-6):
+    rng = np.random.default_rng(seed)
+    H = rng.standard_normal((N, D))
+    W = rng.standard_normal((V, D)) * 0.8
+    y = rng.integers(0, V, N)
+    g = rng.uniform(0.5, 2.0, N)
+    dH, dW = olce.grad64(H, W, y, g)
+    for X, dX in ((H, dH), (W, dW)):
+        fd = np.zeros_like(X)
+        for idx in np.ndindex(X.shape):
+            old = X[idx]
+            X[idx] = old + h
+            up = lce_objective(H, W, y, g)
+            X[idx] = old - h
+            down = lce_objective(H, W, y, g)
+            X[idx] = old
+            fd[idx] = (up - down) / (2 * h)
+        np.testing.assert_allclose(dX, fd, rtol=0, atol=1e-7)
+
+
+def test_lce_grad_matches_finite_differences():
+    for seed in range(3):
+        pin_lce_grad_finite_differences(seed)
+
+
+def pin_lce_grad_zero_weights(N=7, D=6, V=11):
+    """W = 0: softmax is uniform, so dH = dZ W = 0 and dW_v = sum_i g_i (1/V - [y_i = v]) H_i."""
+    rng = np.random.default_rng(5)
+    H = inputs.f32_to_bf16_bits(rng.standard_normal((N, D)).astype(np.float32))
+    W = np.zeros((V, D), np.uint16)
+    y = rng.integers(0, V, N)
+    g = rng.uniform(0.5, 2.0, N)
+    dH, dW = olce.grad(H, W, y, g)
+    H64 = oce.decode(H, "bf16")
+    expect = np.zeros((V, D))
+    for i in range(N):
+        expect += g[i] / V * H64[i]
+        expect[y[i]] -= g[i] * H64[i]
+    np.testing.assert_array_equal(dH, 0.0)
+    np.testing.assert_allclose(dW, expect, rtol=1e-14, atol=1e-14)
+
+
+def test_lce_grad_zero_weights():
+    pin_lce_grad_zero_weights()
+
+
+def pin_lce_grad_column_sum():
+    """Every row of dZ sums to zero, so the rows of dW sum to zero."""
+    H, W, y = inputs.linear_ce(33, 24, 301, seed_stream=11, w_scale=0.9)
+    g = np.random.default_rng(2).uniform(0.5, 2.0, 33)
+    _, dW = olce.grad(H, W, y, g, block=8)
+    scale = np.abs(dW).sum(axis=0)
+    assert np.all(np.abs(dW.sum(axis=0)) <= 1e-13 * np.maximum(scale, 1.0))
+
+
+def test_lce_grad_column_sum():
+    pin_lce_grad_column_sum()
+
+
+def test_lce_grad_matches_torch_autograd():
+    Hb, Wb, y = inputs.linear_ce(24, 40, 130, seed_stream=4, w_scale=0.9)
+    g = np.random.default_rng(8).uniform(0.5, 2.0, 24)
+    dH, dW = olce.grad(Hb, Wb, y, g, block=7)
+    H = torch.tensor(oce.decode(Hb, "bf16"), dtype=torch.float64, requires_grad=True)
+    W = torch.tensor(oce.decode(Wb, "bf16"), dtype=torch.float64, requires_grad=True)
+    loss = torch.nn.functional.cross_entropy(H @ W.T, torch.from_numpy(np.asarray(y, np.int64)),
+                                             reduction="none")
+    (loss * torch.from_numpy(g)).sum().backward()
+    np.testing.assert_allclose(dH, H.grad.numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dW, W.grad.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_lce_grad_from_saved_statistics_and_columns():
+    H, W, y = inputs.linear_ce(40, 16, 50, seed_stream=3)
+    g = np.random.default_rng(1).uniform(0.5, 2.0, 40)
+    _, m, ls = olce.forward(H, W, y)
+    dH, dW = olce.grad(H, W, y, g)
+    dH2, dW2 = olce.grad(H, W, y, g, m, ls, block=9)
+    np.testing.assert_allclose(dH2, dH, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(dW2, dW, rtol=1e-13, atol=1e-15)
+    cols = np.array([49, 0, 13])
+    np.testing.assert_allclose(olce.grad_columns(H, W, y, g, m, ls, cols, block=11), dW[cols],
+                               rtol=1e-13, atol=1e-15)
+
+
+def test_lce_grad_bounds_dominate():
+    H, W, y = inputs.linear_ce(12, 8, 40, seed_stream=6)
+    g = np.ones(12)
+    dH, dW, bH, bW = olce.grad(H, W, y, g, bounds=True)
+    assert np.all(bH >= np.abs(dH) - 1e-15) and np.all(bW >= np.abs(dW) - 1e-15)
+
+
 # --- planted mistakes: each must fail at least one pin ----------------------
 
 @contextlib.contextmanager
@@ -404,3 +505,31 @@ def test_planted_transposed_weight_is_caught():
 def test_planted_dropped_vocab_tail_is_caught():
     with planted(olce, "logits", lambda H, W: H @ W[: max(1, W.shape[0] - 64)].T):
         assert fails(test_lce_zero_weights_give_log_v, 300)
+
+
+def test_planted_scaled_logits_in_backward_is_caught():
+    with planted(olce, "logits", lambda H, W: 1.5 * (H @ W.T)):
+        assert fails(pin_lce_grad_finite_differences)
+
+
+def test_planted_missing_onehot_in_backward_is_caught():
+    real = oce.grad
+
+    def no_onehot(z, y, g, m=None, ls=None):
+        d = real(z, y, g, m, ls)
+        rows = np.arange(d.shape[0])
+        d[rows, np.asarray(y)] += np.asarray(g, np.float64)
+        return d
+    with planted(oce, "grad", no_onehot):
+        assert fails(pin_lce_grad_column_sum)
+        assert fails(pin_lce_grad_finite_differences)
+
+
+def test_planted_dropped_weight_scale_in_backward_is_caught():
+    real = olce.grad64
+
+    def half(H64, W64, *a, **k):
+        out = real(H64, W64, *a, **k)
+        return (out[0] * 0.5,) + tuple(out[1:])
+    with planted(olce, "grad64", half):
+        assert fails(pin_lce_grad_zero_weights) or fails(pin_lce_grad_finite_differences)
