@@ -1,25 +1,31 @@
 /*
  * ce_mi355x.h: C ABI of the MI355X (gfx950) fused softmax cross-entropy library.
  *
- * Three operations, each computed by hand-written HIP kernels in libce_mi355x.so:
+ * Four operations, computed by hand-written HIP kernels in libce_mi355x.so:
  *
- *   ce_forward   per-row loss and log-sum-exp of a [rows, V] logits view
- *   ce_vjp       dlogits = g_i * (softmax(z_i) - onehot(y_i)) from the saved log-sum-exp
- *   lce_forward  per-row loss and log-sum-exp of H.W^T, streamed over vocabulary
- *                tiles without materialising the N x V logits
+ *   ce_forward    per-row loss and log-sum-exp of a [rows, V] logits view
+ *   ce_vjp        dlogits = g_i * (softmax(z_i) - onehot(y_i)) from the saved log-sum-exp
+ *   lce_forward   per-row loss and log-sum-exp of H.W^T, streamed over vocabulary
+ *                 tiles without materialising the N x V logits
+ *   lce_backward  dH and dW of sum_i g_i loss_i for lce_forward's loss; the logits
+ *                 are regenerated chunk by chunk, and the two products with the
+ *                 regenerated gradient chunk run on rocBLAS
  *
  * Conventions shared by every call
  * --------------------------------
  * - Pointers to tensors are DEVICE pointers owned by the caller.  The library keeps
- *   no pointer after a call returns and allocates no device memory: lce_forward's
- *   only scratch is the caller's workspace.
+ *   no pointer after a call returns and allocates no device memory: the lce calls'
+ *   only scratch is the caller's workspace.  (lce_backward's first call on a host
+ *   thread creates a rocBLAS handle for the current device and keeps it for the life
+ *   of that thread; rocBLAS works in the caller's workspace.)
  * - Work is enqueued on `stream` (NULL = the default stream) and the call returns
  *   without synchronising.  Outputs are valid once the stream has been synchronised.
  * - Every argument is checked on the host before any launch.  A failed check returns
  *   a negative ce_status and enqueues nothing.  n_rows == 0 (or N == 0) is a no-op
- *   that returns CE_OK.  A failed launch returns CE_ERR_LAUNCH.  No C++ exception
- *   crosses this boundary, and the library holds no mutable global state, so the
- *   calls may be made from several host threads at once.
+ *   that returns CE_OK, except that lce_backward still writes dW = 0.  A failed
+ *   launch returns CE_ERR_LAUNCH.  No C++ exception crosses this boundary, and the
+ *   library's only mutable state is per host thread, so the calls may be made from
+ *   several host threads at once.
  * - Rows are indexed with 64-bit integers end to end; no launch wraps a 32-bit
  *   grid, however many rows there are.  (MLX PR #4776 "fast.cross_entropy silently
  *   skips rows when the Metal grid gets too large", Issue: a 32-bit grid of
@@ -76,7 +82,7 @@ typedef enum {
     CE_ERR_SHAPE = -2,     /* n_rows < 0, V < 1, D < 1, V or D out of supported range      */
     CE_ERR_DTYPE = -3,     /* dtype is not a ce_dtype                                      */
     CE_ERR_LAYOUT = -4,    /* bad strides, or a pointer not aligned as required            */
-    CE_ERR_WORKSPACE = -5, /* lce workspace NULL or smaller than lce_workspace_size()      */
+    CE_ERR_WORKSPACE = -5, /* lce workspace NULL or smaller than the *_workspace_size()    */
     CE_ERR_LAUNCH = -6,    /* the HIP runtime rejected a kernel launch                     */
     CE_ERR_ALIAS = -7,     /* an output overlaps an input it may not overlap               */
     CE_ERR_DEVICE = -8     /* no usable HIP device, or the device is not gfx950            */
@@ -175,6 +181,42 @@ size_t lce_workspace_size(int64_t N, int64_t D, int64_t V);
 ce_status lce_forward(const void* H, const void* W, const int32_t* targets, int64_t N, int64_t D,
                       int64_t V, float* loss, float* lse, void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
+
+/*
+ * lce_backward_workspace_size: bytes of device workspace lce_backward needs for
+ * (N, D, V): one 8192-column chunk of the logits gradient in bf16 (N * 16 KiB) plus
+ * 64 MiB of GEMM scratch.  Returns 0 for arguments lce_backward would reject.
+ */
+size_t lce_backward_workspace_size(int64_t N, int64_t D, int64_t V);
+
+/*
+ * lce_backward: gradients of sum_i g_i loss_i, with loss_i as lce_forward computes it,
+ * with respect to H and W:
+ *   dZ = diag(g) (softmax(Z) - onehot(y)),   dH = dZ W,   dW = dZ^T H,   Z = H.W^T.
+ *
+ * Source: Ineshin (above), section 1: training saves the forward's log-sum-exp and a
+ * separate chunked backward regenerates the logits it needs tile by tile.  For each
+ * chunk of 8192 vocabulary columns (the page's tile width), the forward's MFMA tile
+ * kernel recomputes the chunk of Z and its epilogue writes
+ * dZ = g_i (exp((z - m_i) - log s_i) - [col == y_i]) in bf16 (round to nearest even)
+ * into the workspace; rocBLAS then adds dZ_c W_c into dH and writes dZ_c^T H into the
+ * chunk's rows of dW, both with float32 accumulation.
+ *
+ *   H, W, targets  as in lce_forward.
+ *   lse      float32 [N][2], the (m, log s) pairs lce_forward wrote for the same H, W.
+ *   g        float32 [N], the upstream gradient of each row's loss.
+ *   dH       float32 [N][D], row-major (written).
+ *   dW       float32 [V][D], row-major (written).
+ *   workspace, workspace_bytes: device scratch of at least
+ *            lce_backward_workspace_size(N, D, V) bytes, 256-byte aligned.
+ * A row whose target lies outside [0, V) has a NaN loss, so its dZ row is NaN: its
+ * dH row and every entry of dW come out NaN.  dH and dW must not overlap the inputs,
+ * the workspace or each other (CE_ERR_ALIAS).  Requirements on N, D, V as in
+ * lce_forward, and N < 2^31.  A rocBLAS failure returns CE_ERR_LAUNCH.
+ */
+ce_status lce_backward(const void* H, const void* W, const int32_t* targets, const float* lse,
+                       const float* g, int64_t N, int64_t D, int64_t V, float* dH, float* dW,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* ce_status_string(ce_status status);

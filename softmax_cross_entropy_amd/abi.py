@@ -27,7 +27,7 @@ STATUS = {
 
 # every symbol include/ce_mi355x.h declares
 EXPORTS = ("ce_forward", "ce_forward_lanes", "ce_vjp", "ce_vjp_lanes", "lce_workspace_size",
-           "lce_forward", "ce_status_string")
+           "lce_forward", "lce_backward_workspace_size", "lce_backward", "ce_status_string")
 
 
 class CELayout(ctypes.Structure):
@@ -61,9 +61,12 @@ def lib() -> ctypes.CDLL:
         L.lce_workspace_size.argtypes = [_i64, _i64, _i64]
         L.lce_workspace_size.restype = _sz
         L.lce_forward.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _sz, _vp]
+        L.lce_backward_workspace_size.argtypes = [_i64, _i64, _i64]
+        L.lce_backward_workspace_size.restype = _sz
+        L.lce_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _sz, _vp]
         L.ce_status_string.argtypes = [ctypes.c_int]
         L.ce_status_string.restype = ctypes.c_char_p
-        for name in ("ce_forward", "ce_forward_lanes", "ce_vjp", "ce_vjp_lanes", "lce_forward"):
+        for name in ("ce_forward", "ce_forward_lanes", "ce_vjp", "ce_vjp_lanes", "lce_forward", "lce_backward"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -174,3 +177,34 @@ def lce_forward(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, loss=No
                            workspace.numel() * workspace.element_size(), _stream(H))
     _check(st, "lce_forward")
     return loss, lse
+
+
+def lce_backward_workspace_size(N: int, D: int, V: int) -> int:
+    return int(lib().lce_backward_workspace_size(N, D, V))
+
+
+def lce_backward(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: torch.Tensor, g: torch.Tensor,
+                 dH=None, dW=None, workspace=None):
+    """(dH [N, D], dW [V, D]) float32 of sum_i g_i loss_i, from lce_forward's lse [N, 2]."""
+    if H.dtype != torch.bfloat16 or W.dtype != torch.bfloat16 or H.dim() != 2 or W.dim() != 2:
+        raise ValueError("H and W must be 2-D bfloat16 tensors")
+    if not H.is_contiguous() or not W.is_contiguous() or H.shape[1] != W.shape[1]:
+        raise ValueError("H [N, D] and W [V, D] must be contiguous with the same D")
+    N, D = H.shape
+    V = W.shape[0]
+    _need(targets, torch.int32, N, "targets")
+    _need(g, torch.float32, N, "g")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (N, 2) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor of shape [N, 2]")
+    if dH is None:
+        dH = torch.empty(N, D, dtype=torch.float32, device=H.device)
+    if dW is None:
+        dW = torch.empty(V, D, dtype=torch.float32, device=H.device)
+    need = lce_backward_workspace_size(N, D, V)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=H.device)
+    st = lib().lce_backward(_ptr(H), _ptr(W), _ptr(targets), _ptr(lse), _ptr(g), N, D, V, _ptr(dH), _ptr(dW),
+                            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(H))
+    _check(st, "lce_backward")
+    return dH, dW
+

@@ -15,7 +15,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libce_mi355x.so")
-SOURCES = ["abi.cpp", "ce_kernels.hip", "lce_kernels.hip"]
+SOURCES = ["abi.cpp", "ce_kernels.hip", "lce_kernels.hip", "lce_backward.cpp"]
+# lce_backward runs its two plain GEMMs per vocabulary chunk on rocBLAS.
+LIBS = ["-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -53,7 +55,7 @@ def build(verbose: bool = False) -> str:
     if failed:
         raise RuntimeError(f"hipcc failed for {failed}")
     tmp = LIB + ".tmp"
-    rc, out = _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
+    rc, out = _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, *LIBS, "-o", tmp])
     if rc != 0:
         raise RuntimeError("link failed:\n" + out)
     os.replace(tmp, LIB)

@@ -273,6 +273,43 @@ ce_status lce_forward(const void* H, const void* W, const int32_t* targets, int6
     return from_hip(ce::launch_lce_forward(c));
 }
 
+size_t lce_backward_workspace_size(int64_t N, int64_t D, int64_t V) {
+    if (N < 0 || N > 0x7fffffff || D < 1 || D % 8 != 0 || V < 1 || V > kMaxV || D > (int64_t)1 << 22) return 0;
+    return ce::lce_backward_workspace_bytes(N, D, V);
+}
+
+ce_status lce_backward(const void* H, const void* W, const int32_t* targets, const float* lse, const float* g,
+                       int64_t N, int64_t D, int64_t V, float* dH, float* dW, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+    if (N < 0 || N > 0x7fffffff || D < 1 || D % 8 != 0 || V < 1 || V > kMaxV || D > (int64_t)1 << 22)
+        return CE_ERR_SHAPE;
+    if (!W || !dW) return CE_ERR_NULL;
+    if (N > 0 && (!H || !targets || !lse || !g || !dH)) return CE_ERR_NULL;
+    const size_t need = ce::lce_backward_workspace_bytes(N, D, V);
+    if (N > 0 && (!workspace || workspace_bytes < need)) return CE_ERR_WORKSPACE;
+    if (!aligned(W, 16) || !aligned(dW, 4)) return CE_ERR_LAYOUT;
+    if (N > 0 && (!aligned(H, 16) || !aligned(targets, 4) || !aligned(lse, 8) || !aligned(g, 4) ||
+                  !aligned(dH, 4) || !aligned(workspace, 256)))
+        return CE_ERR_LAYOUT;
+    const Extent ex_dW = flat_extent(dW, V * D * 4);
+    const Extent ex_W = flat_extent(W, V * D * 2);
+    if (overlaps(ex_dW, ex_W)) return CE_ERR_ALIAS;
+    if (N > 0) {
+        const Extent ex_dH = flat_extent(dH, N * D * 4);
+        const Extent ex_ws = flat_extent(workspace, (int64_t)need);
+        const Extent ins[5] = {flat_extent(H, N * D * 2), ex_W, flat_extent(targets, N * 4),
+                               flat_extent(lse, N * 8), flat_extent(g, N * 4)};
+        for (const Extent& e : ins)
+            if (overlaps(ex_dH, e) || overlaps(ex_dW, e) || overlaps(ex_ws, e)) return CE_ERR_ALIAS;
+        if (overlaps(ex_dH, ex_dW) || overlaps(ex_dH, ex_ws) || overlaps(ex_dW, ex_ws)) return CE_ERR_ALIAS;
+    }
+    int cus = 0;
+    if (ce_status s = device_cus(&cus)) return s;
+    if (N == 0) return from_hip(ce::launch_fill_zero_f32(dW, V * D, stream));
+    ce::LceBackwardCall c{H, W, targets, lse, g, N, D, V, dH, dW, workspace, stream};
+    return ce::run_lce_backward(c) == ce::LceBackwardStatus::kOk ? CE_OK : CE_ERR_LAUNCH;
+}
+
 const char* ce_status_string(ce_status s) {
     switch (s) {
         case CE_OK: return "CE_OK: success";

@@ -75,4 +75,46 @@ struct LceCall {
 size_t lce_workspace_bytes(int64_t N, int64_t D, int64_t V);
 hipError_t launch_lce_forward(const LceCall& c);
 
+// dZ for vocabulary columns [c0, c0 + width) of all N rows, bf16, row r at G + r * ldG.
+struct LceGradChunk {
+    const void* H;
+    const void* W;
+    const int32_t* targets;
+    const float* lse;
+    const float* g;
+    int64_t N;
+    int64_t D;
+    int64_t V;
+    int64_t c0;
+    int64_t width;
+    void* G;
+    int64_t ldG;
+    hipStream_t stream;
+};
+
+hipError_t launch_lce_grad_chunk(const LceGradChunk& c);
+
+// Writes n zeros (a kernel, not a memset, so a captured graph replays it safely).
+hipError_t launch_fill_zero_f32(float* p, int64_t n, hipStream_t stream);
+
+struct LceBackwardCall {
+    const void* H;
+    const void* W;
+    const int32_t* targets;
+    const float* lse;
+    const float* g;
+    int64_t N;
+    int64_t D;
+    int64_t V;
+    float* dH;
+    float* dW;
+    void* workspace;
+    hipStream_t stream;
+};
+
+enum class LceBackwardStatus { kOk, kHip, kBlas };
+
+size_t lce_backward_workspace_bytes(int64_t N, int64_t D, int64_t V);
+LceBackwardStatus run_lce_backward(const LceBackwardCall& c);
+
 }  // namespace ce

@@ -52,12 +52,19 @@ struct TileArgs {
     int64_t N;
     int64_t D;
     int64_t V;
+    int64_t c0, c_end;  // vocabulary columns [c0, c_end) this launch covers
     int n_row_tiles, n_col_tiles;
     int gr, gc;      // super-block shape in tiles (gr * gc == 32)
     int n_rg, n_sb;  // row groups, super-blocks
+    // forward
     int n_slabs;
     float2* partial;  // [N][n_slabs]
     float* zy;        // [N]
+    // gradient of the logits
+    const float2* lse;  // [N] saved (m, log s)
+    const float* g;     // [N]
+    __bf16* G;          // [N][ldG], column c at c - c0
+    int64_t ldG;
 };
 
 // LDS layout of one operand stage: 256 rows x 8 chunks of 16 bytes (8 bf16 along K).
@@ -65,6 +72,10 @@ struct TileArgs {
 // read touches at one K chunk land in 16 different 16-byte bank groups:
 //   byte offset of (row, chunk) = row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4).
 
+// kGrad = false: the forward epilogue ((m, s) per row per 128-column slab, target logit).
+// kGrad = true: the same tile of Z turned into dZ = g (exp((z - m) - log s) - [col = y])
+// with the saved (m, log s), stored in bf16 (the logits regenerated for the backward).
+template <bool kGrad>
 __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
     // One LDS object (the compiler then sees the DMA writes and the fragment reads as
     // one array and inserts no waits of its own): two stages of A and B, then targets.
@@ -95,7 +106,7 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int64_t row0 = (int64_t)row_tile * BM;
-    const int64_t col0 = (int64_t)col_tile * BN;
+    const int64_t col0 = a.c0 + (int64_t)col_tile * BN;
 
     // ---- global -> LDS loads: each wave fills 64 rows of A and of B per stage ----
     // One global_load_lds_dwordx4 writes 64 lanes x 16 bytes = 8 LDS rows; lane i lands
@@ -112,7 +123,7 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
     // Addresses: a wave-uniform base (the tile's first row at K offset k0) plus a 32-bit
     // per-lane byte offset; rows past N (or V) are clamped to the last valid row.
     const int64_t a_rows = a.N - row0 < BM ? a.N - row0 : BM;  // valid rows in this tile
-    const int64_t b_rows = a.V - col0 < BN ? a.V - col0 : BN;
+    const int64_t b_rows = a.c_end - col0 < BN ? a.c_end - col0 : BN;
     const uint32_t row_bytes = (uint32_t)(a.D * 2);
     const char* a_tile = reinterpret_cast<const char*>(a.H + row0 * a.D);
     const char* b_tile = reinterpret_cast<const char*>(a.W + col0 * a.D);
@@ -298,73 +309,125 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
     const int64_t wrow0 = row0 + wm * WT;
     auto col_of = [&](int j, int e) { return j * 32 + 8 * (e / 4) + 4 * h2 + (e % 4); };
 
-    // target logits: the lane holding the target column of a row stores it.  A row's
-    // target lies in this wave's columns for about one wave in ten, so the select runs
-    // rarely and only in those lanes: column c = j*32 + 8*(e/4) + 4*h2 + e%4 gives
-    // j = c / 32 and e = 4 * ((c / 8) % 4) + c % 4; pick j first, then e.
-#pragma unroll
-    for (int i = 0; i < FB; ++i) {
-        const int lr = wm * WT + i * 32 + l32;
-        const int64_t yrel = (int64_t)tile_targets[lr] - wcol0;
-        if (yrel >= 0 && yrel < WT && (((int)yrel >> 2) & 1) == h2) {
-            const int c = (int)yrel;
-            const int jj = c >> 5, ee = (((c >> 3) & 3) << 2) | (c & 3);
-            float v = 0.f;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float lo = (jj & 1) ? acc[i][1][e] : acc[i][0][e];
-                const float hi = (jj & 1) ? acc[i][3][e] : acc[i][2][e];
-                v = ee == e ? ((jj & 2) ? hi : lo) : v;
-            }
-            a.zy[row0 + lr] = v;  // a valid target implies a valid row
-        }
-    }
-
-    // Per row: the exact maximum over the 128 columns (this lane's 64, then lane ^ 32's),
-    // then sum exp(z - m) with one exponential per logit, and the partner's sum.  Both
-    // lanes of a pair end with the same (m, s); the lower one stores it.  Columns past V
-    // hold copies of the last W row and count as -inf: only the last column tile has
-    // any, so the masked form is a separate instance (the accumulators stay read-only).
-    const int64_t slab = (int64_t)col_tile * 2 + wn;
-    auto row_states = [&](auto mask_c) {
-        constexpr bool kMask = decltype(mask_c)::value;
-        auto z = [&](int i, int j, int e) {
-            if constexpr (kMask)
-                return wcol0 + col_of(j, e) < a.V ? acc[i][j][e] : kNegInf;
-            else
-                return acc[i][j][e];
-        };
+    if constexpr (kGrad) {
+        // dZ for this lane's 4 rows x 64 columns.  A row with an out-of-range target
+        // gets m = NaN, so its whole row of dZ is NaN (its loss is NaN too).
 #pragma unroll
         for (int i = 0; i < FB; ++i) {
-            float mj[FB];
+            const int lr = wm * WT + i * 32 + l32;
+            const int64_t row = row0 + lr;
+            if (row >= a.N) continue;
+            const int32_t y = tile_targets[lr];
+            const float2 l = a.lse[row];
+            const float m = (y >= 0 && (int64_t)y < a.V) ? l.x : __builtin_nanf("");
+            const float nlsl = -l.y * kLog2e;
+            const float gr = a.g[row];
+            __bf16* grow = a.G + row * a.ldG - a.c0;
+            auto dz = [&](float z) { return gr * __builtin_amdgcn_exp2f(__builtin_fmaf(z - m, kLog2e, nlsl)); };
 #pragma unroll
-            for (int j = 0; j < FB; ++j) {
-                float t = z(i, j, 0);
+            for (int j = 0; j < FB; ++j)
 #pragma unroll
-                for (int e = 1; e < 16; ++e) t = fmaxf(t, z(i, j, e));
-                mj[j] = t;
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t c = wcol0 + j * 32 + 8 * q + 4 * h2;  // 4 consecutive columns
+                    const float v0 = dz(acc[i][j][4 * q]), v1 = dz(acc[i][j][4 * q + 1]);
+                    const float v2 = dz(acc[i][j][4 * q + 2]), v3 = dz(acc[i][j][4 * q + 3]);
+                    if (c + 3 < a.c_end) {
+                        uint2 w;
+                        w.x = Elem<__bf16>::bits2(v0, v1);
+                        w.y = Elem<__bf16>::bits2(v2, v3);
+                        *reinterpret_cast<uint2*>(grow + c) = w;
+                    } else {
+                        const float v[4] = {v0, v1, v2, v3};
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            if (c + t < a.c_end) grow[c + t] = (__bf16)v[t];
+                    }
+                }
+            // the target column: stored again as g (p - 1) by the lane that stored it
+            // (same lane, same address, so the second store lands last)
+            const int64_t yrel = (int64_t)y - wcol0;
+            if (yrel >= 0 && yrel < WT && (((int)yrel >> 2) & 1) == h2) {
+                const int cc = (int)yrel;
+                const int jj = cc >> 5, ee = (((cc >> 3) & 3) << 2) | (cc & 3);
+                float z = 0.f;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const float lo = (jj & 1) ? acc[i][1][e] : acc[i][0][e];
+                    const float hi = (jj & 1) ? acc[i][3][e] : acc[i][2][e];
+                    z = ee == e ? ((jj & 2) ? hi : lo) : z;
+                }
+                grow[y] = (__bf16)(dz(z) - gr);
             }
-            float m = fmaxf(fmaxf(mj[0], mj[1]), fmaxf(mj[2], mj[3]));
-            m = fmaxf(m, __shfl_xor(m, 32));
-            const float r = ref_point(m);
-            float sj[FB];
-#pragma unroll
-            for (int j = 0; j < FB; ++j) {
-                float t = 0.f;
-#pragma unroll
-                for (int e = 0; e < 16; ++e) t += exp_e(z(i, j, e) - r);
-                sj[j] = t;
-            }
-            float s = (sj[0] + sj[1]) + (sj[2] + sj[3]);
-            s += __shfl_xor(s, 32);
-            const int64_t row = wrow0 + i * 32 + l32;
-            if (h2 == 0 && row < a.N) a.partial[row * a.n_slabs + slab] = make_float2(m, s);
         }
-    };
-    if (wcol0 + WT > a.V)
-        row_states(std::true_type{});
-    else
-        row_states(std::false_type{});
+    } else {
+        // target logits: the lane holding the target column of a row stores it.  A row's
+        // target lies in this wave's columns for about one wave in ten, so the select runs
+        // rarely and only in those lanes: column c = j*32 + 8*(e/4) + 4*h2 + e%4 gives
+        // j = c / 32 and e = 4 * ((c / 8) % 4) + c % 4; pick j first, then e.
+    #pragma unroll
+        for (int i = 0; i < FB; ++i) {
+            const int lr = wm * WT + i * 32 + l32;
+            const int64_t yrel = (int64_t)tile_targets[lr] - wcol0;
+            if (yrel >= 0 && yrel < WT && (((int)yrel >> 2) & 1) == h2) {
+                const int c = (int)yrel;
+                const int jj = c >> 5, ee = (((c >> 3) & 3) << 2) | (c & 3);
+                float v = 0.f;
+    #pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const float lo = (jj & 1) ? acc[i][1][e] : acc[i][0][e];
+                    const float hi = (jj & 1) ? acc[i][3][e] : acc[i][2][e];
+                    v = ee == e ? ((jj & 2) ? hi : lo) : v;
+                }
+                a.zy[row0 + lr] = v;  // a valid target implies a valid row
+            }
+        }
+
+        // Per row: the exact maximum over the 128 columns (this lane's 64, then lane ^ 32's),
+        // then sum exp(z - m) with one exponential per logit, and the partner's sum.  Both
+        // lanes of a pair end with the same (m, s); the lower one stores it.  Columns past V
+        // hold copies of the last W row and count as -inf: only the last column tile has
+        // any, so the masked form is a separate instance (the accumulators stay read-only).
+        const int64_t slab = (int64_t)col_tile * 2 + wn;
+        auto row_states = [&](auto mask_c) {
+            constexpr bool kMask = decltype(mask_c)::value;
+            auto z = [&](int i, int j, int e) {
+                if constexpr (kMask)
+                    return wcol0 + col_of(j, e) < a.c_end ? acc[i][j][e] : kNegInf;
+                else
+                    return acc[i][j][e];
+            };
+    #pragma unroll
+            for (int i = 0; i < FB; ++i) {
+                float mj[FB];
+    #pragma unroll
+                for (int j = 0; j < FB; ++j) {
+                    float t = z(i, j, 0);
+    #pragma unroll
+                    for (int e = 1; e < 16; ++e) t = fmaxf(t, z(i, j, e));
+                    mj[j] = t;
+                }
+                float m = fmaxf(fmaxf(mj[0], mj[1]), fmaxf(mj[2], mj[3]));
+                m = fmaxf(m, __shfl_xor(m, 32));
+                const float r = ref_point(m);
+                float sj[FB];
+    #pragma unroll
+                for (int j = 0; j < FB; ++j) {
+                    float t = 0.f;
+    #pragma unroll
+                    for (int e = 0; e < 16; ++e) t += exp_e(z(i, j, e) - r);
+                    sj[j] = t;
+                }
+                float s = (sj[0] + sj[1]) + (sj[2] + sj[3]);
+                s += __shfl_xor(s, 32);
+                const int64_t row = wrow0 + i * 32 + l32;
+                if (h2 == 0 && row < a.N) a.partial[row * a.n_slabs + slab] = make_float2(m, s);
+            }
+        };
+        if (wcol0 + WT > a.c_end)
+            row_states(std::true_type{});
+        else
+            row_states(std::false_type{});
+    }
 }
 
 constexpr int kMergeThreads = 256;
@@ -412,10 +475,11 @@ struct Geometry {
     int64_t blocks;
 };
 
-Geometry geometry(int64_t N, int64_t V) {
+// Tiles over N rows and `cols` vocabulary columns.
+Geometry geometry(int64_t N, int64_t cols) {
     Geometry g;
     g.n_row_tiles = (int)((N + BM - 1) / BM);
-    g.n_col_tiles = (int)((V + BN - 1) / BN);
+    g.n_col_tiles = (int)((cols + BN - 1) / BN);
     g.gr = g.n_row_tiles >= 4 ? 4 : (g.n_row_tiles >= 2 ? 2 : 1);
     g.gc = kTilesPerGroup / g.gr;
     g.n_rg = (g.n_row_tiles + g.gr - 1) / g.gr;
@@ -442,14 +506,38 @@ hipError_t launch_lce_forward(const LceCall& c) {
     float2* partial = reinterpret_cast<float2*>(ws);
     float* zy = reinterpret_cast<float*>(ws + align256((size_t)g.n_slabs * (size_t)c.N * sizeof(float2)));
     TileArgs a{static_cast<const __bf16*>(c.H), static_cast<const __bf16*>(c.W), c.targets, c.N, c.D, c.V,
-               g.n_row_tiles, g.n_col_tiles, g.gr, g.gc, g.n_rg, g.n_sb, g.n_slabs, partial, zy};
-    hipLaunchKernelGGL(lce_tile, dim3((unsigned)g.blocks), dim3(kThreads), 0, c.stream, a);
+               0, c.V, g.n_row_tiles, g.n_col_tiles, g.gr, g.gc, g.n_rg, g.n_sb, g.n_slabs, partial, zy,
+               nullptr, nullptr, nullptr, 0};
+    hipLaunchKernelGGL(lce_tile<false>, dim3((unsigned)g.blocks), dim3(kThreads), 0, c.stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     constexpr int kRowsPerBlock = kMergeThreads / kMergeLanes;
     const int64_t mblocks = (c.N + kRowsPerBlock - 1) / kRowsPerBlock;
     hipLaunchKernelGGL(lce_merge, dim3((unsigned)mblocks), dim3(kMergeThreads), 0, c.stream, partial, zy,
                        c.targets, c.N, g.n_slabs, c.V, c.loss, reinterpret_cast<float2*>(c.lse));
+    return hipGetLastError();
+}
+
+hipError_t launch_lce_grad_chunk(const LceGradChunk& c) {
+    const Geometry g = geometry(c.N, c.width);
+    TileArgs a{static_cast<const __bf16*>(c.H), static_cast<const __bf16*>(c.W), c.targets, c.N, c.D, c.V,
+               c.c0, c.c0 + c.width, g.n_row_tiles, g.n_col_tiles, g.gr, g.gc, g.n_rg, g.n_sb, 0, nullptr,
+               nullptr, reinterpret_cast<const float2*>(c.lse), c.g, static_cast<__bf16*>(c.G), c.ldG};
+    hipLaunchKernelGGL(lce_tile<true>, dim3((unsigned)g.blocks), dim3(kThreads), 0, c.stream, a);
+    return hipGetLastError();
+}
+
+namespace {
+__global__ __launch_bounds__(256) void fill_zero_f32(float* p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
+}
+}  // namespace
+
+hipError_t launch_fill_zero_f32(float* p, int64_t n, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    const int64_t want = (n + 255) / 256;
+    const unsigned blocks = (unsigned)(want < 16384 ? want : 16384);
+    hipLaunchKernelGGL(fill_zero_f32, dim3(blocks), dim3(256), 0, stream, p, n);
     return hipGetLastError();
 }
 

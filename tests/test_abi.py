@@ -135,8 +135,51 @@ def test_lce_rejects_bad_arguments():
     assert lce(ws=ctypes.c_void_p(7 * A + 256)) == ALIAS  # workspace inside W
 
 
+P_DH, P_DW = ctypes.c_void_p(A * 200), ctypes.c_void_p(A * 210)  # clear of the 64.5 MiB workspace
+
+
+def lbw(H=P_LOGITS, W=P_W, t=P_T, lse=P_LSE, g=P_G, N=32, D=64, V=1000, dH=P_DH, dW=P_DW, ws=P_WS, wsb=None):
+    if wsb is None:
+        wsb = abi.lce_backward_workspace_size(N, D, V)
+    return abi.lib().lce_backward(H, W, t, lse, g, N, D, V, dH, dW, ws, wsb, None)
+
+
+def test_lce_backward_rejects_bad_arguments():
+    need = abi.lce_backward_workspace_size(32, 64, 1000)
+    assert need == 32 * 8192 * 2 + (64 << 20)
+    assert abi.lce_backward_workspace_size(32, 60, 1000) == 0
+    assert abi.lce_backward_workspace_size(1 << 31, 64, 1000) == 0
+    assert lbw(D=60) == SHAPE
+    assert lbw(D=0) == SHAPE
+    assert lbw(V=0) == SHAPE
+    assert lbw(N=-1) == SHAPE
+    assert lbw(N=1 << 31, wsb=1 << 40) == SHAPE
+    assert lbw(D=(1 << 22) + 8) == SHAPE
+    for name in ("H", "W", "t", "lse", "g", "dH", "dW"):
+        assert lbw(**{name: None}) == NULL, name
+    assert lbw(ws=None) == WORKSPACE
+    assert lbw(wsb=need - 1) == WORKSPACE
+    assert lbw(H=ctypes.c_void_p(A + 8)) == LAYOUT
+    assert lbw(lse=ctypes.c_void_p(4 * A + 4)) == LAYOUT
+    assert lbw(ws=ctypes.c_void_p(8 * A + 64)) == LAYOUT
+    assert lbw(dW=ctypes.c_void_p(7 * A + 1024)) == ALIAS   # dW inside W
+    assert lbw(dH=ctypes.c_void_p(20 * A)) == ALIAS         # dH inside the workspace
+    assert lbw(dH=ctypes.c_void_p(210 * A + 4096)) == ALIAS  # dH inside dW
+    assert lbw(dW=ctypes.c_void_p(5 * A)) == ALIAS          # dW over g
+
+
+def test_lce_backward_empty_batch_needs_only_w_and_dw():
+    """N == 0 still writes dW (= 0); H, targets, lse, g, dH and the workspace may be NULL."""
+    st = lbw(H=None, t=None, lse=None, g=None, dH=None, ws=None, N=0, wsb=0)
+    assert st in (OK, DEVICE)
+    assert lbw(N=0, dW=None) == NULL
+
+
 @pytest.mark.skipif(os.environ.get("HIP_VISIBLE_DEVICES", None) is not None or os.path.exists("/dev/kfd"),
                     reason="only meaningful without a GPU")
 def test_valid_call_without_device_reports_device_error():
     assert fwd() == DEVICE
     assert vjp() == DEVICE
+    assert lce() == DEVICE
+    assert lbw() == DEVICE
+    assert lbw(H=None, t=None, lse=None, g=None, dH=None, ws=None, N=0, wsb=0) == DEVICE
