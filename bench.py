@@ -5,6 +5,9 @@ One step is one pass of the whole path over one batch of synthetic input:
     g = 1): the configuration the CE fwd+VJP figure is quoted on;
   * lce_forward on bf16 H [8192 x 4096] ~ N(0,1), W [151,936 x 4096] ~ N(0, 1/D),
     uniform targets: the linear-CE configuration.
+After the timed steps, lce_backward (dH, dW of the same linear-CE loss, upstream
+gradient U[0.25, 2)) is timed on its own loop and reported under parts/rooflines; it
+is not part of the step.
 Inputs are resident in HBM before the timed region.  Two copies of the logits
 alternate between steps (each copy is 622 MB, larger than the 256 MB Infinity Cache,
 so no step reads logits cached by the previous one).
@@ -109,6 +112,11 @@ def cpu_baseline(ce_batch, lce_inputs, lce_rows=32):
     t0 = time.perf_counter()
     olce.forward(H, W, y, rows=rows)
     lce_s = time.perf_counter() - t0
+    g_up = np.random.default_rng([5, 0]).uniform(0.25, 2.0, LCE_N)
+    W64 = olce.decode_bf16(W)
+    t0 = time.perf_counter()
+    olce.grad64(olce.decode_bf16(H[rows]), W64, y[rows], g_up[rows])
+    lbw_s = time.perf_counter() - t0
     blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     return {
         "value": (fwd_b + vjp_b) / ce_s / 1e9,
@@ -121,6 +129,10 @@ def cpu_baseline(ce_batch, lce_inputs, lce_rows=32):
                 "cores": blas, "seconds": lce_s,
                 "sample": f"lce oracle (float64 BLAS matmul + CE) on {lce_rows} of {LCE_N} rows, "
                           f"all {LCE_V} columns"},
+        "lce_backward": {"value": 3 * lce_flops(lce_rows, LCE_D, LCE_V) / lbw_s / 1e12, "unit": "TFLOP/s",
+                         "cores": blas, "seconds": lbw_s,
+                         "sample": f"lce gradient oracle (float64: logits, dZ, dZ W, dZ^T H) on {lce_rows} "
+                                   f"of {LCE_N} rows, all {LCE_V} columns"},
         "host_cores": len(os.sched_getaffinity(0)),
     }
 
@@ -131,7 +143,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--parts", default="ce,lce", help="comma list of ce, lce")
+    ap.add_argument("--parts", default="ce,lce,lbw", help="comma list of ce, lce, lbw (lce_backward)")
+    ap.add_argument("--bwd-steps", type=int, default=5, help="timed lce_backward calls")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run one elementwise copy (torch.neg) of MIB MiB fp32 first, so a counter "
                          "profile holds a kernel of known traffic")
@@ -214,6 +227,25 @@ def main():
     def ms(a, b):
         return [ev[i][a].elapsed_time(ev[i][b]) for i in range(K)]
 
+    bwd_ms = None
+    if "lbw" in parts and lce_in is not None:
+        G_up = torch.from_numpy(np.random.default_rng([5, 0]).uniform(0.25, 2.0, LCE_N).astype(np.float32)).to(dev)
+        dH = torch.empty(LCE_N, LCE_D, dtype=torch.float32, device=dev)
+        dW = torch.empty(LCE_V, LCE_D, dtype=torch.float32, device=dev)
+        bws = torch.empty(abi.lce_backward_workspace_size(LCE_N, LCE_D, LCE_V), dtype=torch.uint8, device=dev)
+        for _ in range(2):
+            abi.lce_backward(Hd, Wd, Yd, llse, G_up, dH=dH, dW=dW, workspace=bws)
+        torch.cuda.synchronize()
+        bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.bwd_steps)]
+        for e0, e1 in bev:
+            e0.record(stream)
+            abi.lce_backward(Hd, Wd, Yd, llse, G_up, dH=dH, dW=dW, workspace=bws)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        bwd_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in bev]))
+        del dH, dW, bws
+
     step_ms = float(np.mean(ms(0, 3)))
     out = {"metric": METRIC, "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": step_ms,
            "wall_ms_per_step": wall / K * 1e3, "higher_is_better": True, "scaling": "weak",
@@ -257,11 +289,22 @@ def main():
         if "value" not in out:
             out["value"] = tf
             out["unit"] = "TFLOP/s"
+    # the dominant kernel of the step by time (lce_backward is timed apart from the step)
+    dom = max(rooflines, key=lambda k: rooflines[k]["ms"])
+    if bwd_ms is not None:
+        fl = 3 * lce_flops(LCE_N, LCE_D, LCE_V)
+        tf = fl / (bwd_ms * 1e-3) / 1e12
+        parts_out["lce_backward"] = {"ms": bwd_ms, "TFLOP_s": tf, "frac_mfma_bf16_peak": tf / MFMA_BF16_PEAK_TFLOPS,
+                                     "flop": fl, "calls": args.bwd_steps, "in_step": False}
+        rooflines["lce_backward"] = {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS,
+                                     "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                                     "ms": bwd_ms, "algorithmic_flop": fl,
+                                     "kernels": "per 8192-column chunk: lce_tile (dZ epilogue) + two rocBLAS "
+                                                "GEMMs (one lce_backward call)"}
+        cfg["lce_backward"] = {"N": LCE_N, "D": LCE_D, "V": LCE_V, "out": "fp32 dH, dW", "timed": "apart"}
     cfg["workload"] = " + ".join(cfg["workload"])
     out["config"] = cfg
     out["parts"] = parts_out
-    # the dominant kernel of the step by time
-    dom = max(rooflines, key=lambda k: rooflines[k]["ms"])
     out["roofline"] = dict(rooflines[dom], kernel=dom)
     out["rooflines"] = rooflines
     if calib:
