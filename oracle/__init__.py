@@ -10,12 +10,14 @@ It writes out the plain definitions in float64 NumPy:
 
 * ``oracle.ce``: the per-row loss, the log-sum-exp and the gradient of
   softmax cross-entropy.
-* ``oracle.lce``: the linear cross-entropy forward.  It materialises the
-  logits H.W^T in float64 row blocks and applies ``oracle.ce``.
+* ``oracle.lce``: the linear cross-entropy forward and its gradients dH, dW.  It
+  materialises the logits H.W^T in float64 row blocks and applies ``oracle.ce``.
+* ``oracle.kl``: the row-wise KL divergence of a teacher row from a student row
+  and its gradient with respect to the student logits.
 
 Every function is pinned by ``tests/test_oracle.py`` against values the pages
 print, closed forms, invariants and brute force.  No function here is
 "parity unpinned".
 """
 
-from . import ce, lce  # noqa: F401
+from . import ce, kl, lce  # noqa: F401

@@ -18,6 +18,7 @@ import torch
 
 import oracle
 from oracle import ce as oce
+from oracle import kl as okl
 from oracle import lce as olce
 from softmax_cross_entropy_amd import inputs
 from tests import golden_io
@@ -444,6 +445,108 @@ def test_lce_grad_bounds_dominate():
     assert np.all(bH >= np.abs(dH) - 1e-15) and np.all(bW >= np.abs(dW) - 1e-15)
 
 
+# --- KL divergence ("One barrier short", Run it yourself) --------------------
+
+def kl_rows(rows=6, V=50, seed=0, scale=4.0):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((rows, V)) * scale, rng.standard_normal((rows, V)) * scale
+
+
+def test_kl_of_a_row_from_itself_is_zero():
+    q, _ = kl_rows()
+    kl, *_ = okl.forward(q, q)
+    assert np.all(kl == 0.0)
+    assert np.all(okl.grad(q, q, np.ones(q.shape[0])) == 0.0)
+
+
+def pin_kl_uniform_student(V=37):
+    """A uniform student row gives kl = log V - H(softmax(p)) (entropy from SciPy)."""
+    _, p = kl_rows(V=V, seed=3)
+    q = np.full_like(p, 2.5)
+    kl, *_ = okl.forward(q, p)
+    ent = scipy.special.entr(scipy.special.softmax(p, axis=1)).sum(axis=1)
+    np.testing.assert_allclose(kl, math.log(V) - ent, rtol=1e-13, atol=1e-13)
+
+
+def test_kl_uniform_student():
+    pin_kl_uniform_student()
+
+
+def kl_brute(q, p):
+    """50-digit KL and gradient without the max shift."""
+    out, grads = [], []
+    with mpmath.workdps(50):
+        for qr, pr in zip(q.tolist(), p.tolist()):
+            eq = [mpmath.exp(mpmath.mpf(v)) for v in qr]
+            ep = [mpmath.exp(mpmath.mpf(v)) for v in pr]
+            sq, sp = mpmath.fsum(eq), mpmath.fsum(ep)
+            P = [e / sp for e in ep]
+            Q = [e / sq for e in eq]
+            out.append(float(mpmath.fsum(Pj * (mpmath.log(Pj) - mpmath.log(Qj)) for Pj, Qj in zip(P, Q))))
+            grads.append([float(Qj - Pj) for Pj, Qj in zip(P, Q)])
+    return np.array(out), np.array(grads)
+
+
+def pin_kl_bruteforce():
+    for V in (1, 2, 3, 8, 17):
+        q, p = kl_rows(rows=5, V=V, seed=V, scale=6.0)
+        kl, *_ = okl.forward(q, p)
+        bk, bg = kl_brute(q, p)
+        np.testing.assert_allclose(kl, bk, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(okl.grad(q, p, np.ones(5)), bg, rtol=0, atol=1e-14)
+
+
+def test_kl_bruteforce():
+    pin_kl_bruteforce()
+
+
+def test_kl_matches_torch():
+    q, p = kl_rows(rows=9, V=300, seed=5)
+    g = np.random.default_rng(2).uniform(0.5, 2.0, 9)
+    kl, *_ = okl.forward(q, p)
+    tq = torch.tensor(q, dtype=torch.float64, requires_grad=True)
+    lq = torch.log_softmax(tq, dim=1)
+    lp = torch.log_softmax(torch.tensor(p, dtype=torch.float64), dim=1)
+    tk = torch.nn.functional.kl_div(lq, lp, log_target=True, reduction="none").sum(dim=1)
+    np.testing.assert_allclose(kl, tk.detach().numpy(), rtol=1e-12, atol=1e-13)
+    (tk * torch.from_numpy(g)).sum().backward()
+    np.testing.assert_allclose(okl.grad(q, p, g), tq.grad.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_kl_invariants():
+    q, p = kl_rows(rows=8, V=200, seed=7)
+    kl, mq, lsq, mp, lsp = okl.forward(q, p)
+    assert np.all(kl >= -1e-15)  # Gibbs
+    d = okl.grad(q, p, np.full(8, 1.5))
+    assert np.all(np.abs(d.sum(axis=1)) <= 1e-14)
+    shift_q, shift_p = np.arange(8)[:, None] * 3.0, -np.arange(8)[:, None] * 5.0
+    kl2, *_ = okl.forward(q + shift_q, p + shift_p)
+    np.testing.assert_allclose(kl2, kl, rtol=1e-12, atol=1e-13)
+    # the saved statistics reproduce the same gradient
+    np.testing.assert_array_equal(okl.grad(q, p, np.full(8, 1.5), (mq, lsq, mp, lsp)), d)
+
+
+def test_kl_infinite_entries():
+    q, p = kl_rows(rows=3, V=10, seed=9)
+    # a teacher entry of -inf has zero probability: the same as dropping that column
+    p2 = p.copy()
+    p2[:, 4] = -np.inf
+    kl2, *_ = okl.forward(q, p2)
+    kl_drop, *_ = okl.forward(np.delete(q, 4, axis=1), np.delete(p, 4, axis=1))
+    # dropping the column also removes it from the student's normaliser: compare with
+    # the student's own log-softmax kept over all 10 columns
+    lq = okl.log_softmax(q)
+    P = np.exp(okl.log_softmax(np.delete(p, 4, axis=1)))
+    expect = (P * (np.log(P) - np.delete(lq, 4, axis=1))).sum(axis=1)
+    np.testing.assert_allclose(kl2, expect, rtol=1e-13, atol=1e-14)
+    assert np.all(np.isfinite(kl_drop))
+    # a student entry of -inf where the teacher has mass makes the row +inf
+    q3 = q.copy()
+    q3[:, 2] = -np.inf
+    kl3, *_ = okl.forward(q3, p)
+    assert np.all(kl3 == np.inf)
+
+
 # --- planted mistakes: each must fail at least one pin ----------------------
 
 @contextlib.contextmanager
@@ -533,3 +636,20 @@ def test_planted_dropped_weight_scale_in_backward_is_caught():
         return (out[0] * 0.5,) + tuple(out[1:])
     with planted(olce, "grad64", half):
         assert fails(pin_lce_grad_zero_weights) or fails(pin_lce_grad_finite_differences)
+
+
+def test_planted_swapped_kl_direction_is_caught():
+    real = okl.forward
+    with planted(okl, "forward", lambda q, p: real(p, q)):
+        assert fails(pin_kl_bruteforce)
+
+
+def test_planted_missing_normaliser_in_kl_is_caught():
+    real = okl.log_softmax
+
+    def no_log_sum(z, m=None, ls=None):
+        if m is None or ls is None:
+            m, ls = okl.row_stats(z)
+        return real(z, m, np.zeros_like(ls))
+    with planted(okl, "log_softmax", no_log_sum):
+        assert fails(pin_kl_uniform_student)
