@@ -15,7 +15,9 @@ g_i (exp(lq_i) - exp(lp_i)) = g_i (softmax(q_i) - softmax(p_i)).
 The oracle is that definition written out in float64, with the row statistics of
 the softmax cross-entropy oracle (max shift, pairwise sums).  A teacher entry of
 -inf has zero probability and contributes nothing (0 log 0 = 0); a student entry of
--inf under a teacher entry with positive probability makes the row +inf.
+-inf under a teacher entry with positive probability makes the row +inf; a teacher
+row that is -inf throughout has no softmax (0 / 0), so its kl is NaN, as an all -inf
+logits row gives a NaN cross-entropy.
 """
 
 from __future__ import annotations
@@ -48,7 +50,10 @@ def forward(q: np.ndarray, p: np.ndarray):
     P = np.exp(lp)
     with np.errstate(invalid="ignore"):
         terms = np.where(P > 0, P * (lp - lq), 0.0)
-    return terms.sum(axis=1), mq, lsq, mp, lsp
+    kl = terms.sum(axis=1)
+    # a teacher row without mass (all -inf) has no softmax: 0 / 0
+    kl[mp == -np.inf] = np.nan
+    return kl, mq, lsq, mp, lsp
 
 
 def grad(q: np.ndarray, p: np.ndarray, g: np.ndarray, stats=None) -> np.ndarray:

@@ -545,6 +545,11 @@ def test_kl_infinite_entries():
     q3[:, 2] = -np.inf
     kl3, *_ = okl.forward(q3, p)
     assert np.all(kl3 == np.inf)
+    # a teacher row without mass has no softmax
+    p4 = p.copy()
+    p4[1, :] = -np.inf
+    kl4, *_ = okl.forward(q, p4)
+    assert np.isnan(kl4[1]) and np.all(np.isfinite(kl4[[0, 2]]))
 
 
 # --- planted mistakes: each must fail at least one pin ----------------------
