@@ -1,7 +1,7 @@
 /*
  * ce_mi355x.h: C ABI of the MI355X (gfx950) fused softmax cross-entropy library.
  *
- * Four operations, computed by hand-written HIP kernels in libce_mi355x.so:
+ * Six operations, computed by hand-written HIP kernels in libce_mi355x.so:
  *
  *   ce_forward    per-row loss and log-sum-exp of a [rows, V] logits view
  *   ce_vjp        dlogits = g_i * (softmax(z_i) - onehot(y_i)) from the saved log-sum-exp
@@ -10,6 +10,8 @@
  *   lce_backward  dH and dW of sum_i g_i loss_i for lce_forward's loss; the logits
  *                 are regenerated chunk by chunk, and the two products with the
  *                 regenerated gradient chunk run on rocBLAS
+ *   kl_forward    per-row KL divergence of a teacher logits row from a student row
+ *   kl_vjp        dq = g_i * (softmax(q_i) - softmax(p_i)) from the saved pairs
  *
  * Conventions shared by every call
  * --------------------------------
@@ -217,6 +219,55 @@ size_t lce_backward_workspace_size(int64_t N, int64_t D, int64_t V);
 ce_status lce_backward(const void* H, const void* W, const int32_t* targets, const float* lse,
                        const float* g, int64_t N, int64_t D, int64_t V, float* dH, float* dW,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * kl_forward: kl_i = sum_j softmax(p_i)_j (log softmax(p_i)_j - log softmax(q_i)_j), the
+ * KL divergence of the teacher row p_i from the student row q_i.
+ *
+ * Source: "One barrier short", section "Run it yourself" (the reference the fused
+ * kernel is checked against: kl = sum exp(lp) (lp - lq) with lq, lp the log-softmaxes
+ * of the student and teacher logits), and section "Sixty-four floats" (one pass per
+ * row with an online log-sum-exp per distribution, combined across waves through
+ * shared memory).  Each lane keeps (m_q, s_q), (m_p, s_p) and
+ * t = sum_j exp(p_j - m_p) (p_j - q_j); then kl = t / s_p - (m_p + log s_p) + (m_q + log s_q).
+ *
+ *   q, p     student and teacher logits, [n_rows rows of V] of dtype `dt`, each
+ *            addressed through its own layout (as the logits of ce_forward).
+ *   kl       float32 [n_rows] (written).
+ *   lse_q, lse_p  float32 [n_rows][2] (written): (m, log s) of q and of p, as
+ *            ce_forward's lse, kept for kl_vjp.
+ * A teacher entry of -inf has zero probability and adds nothing; a student entry of
+ * -inf where the teacher has mass makes kl_i = +inf; a row with +inf or NaN, or an
+ * all -inf teacher row, gives NaN.  Outputs must not overlap q, p or each other.
+ */
+ce_status kl_forward(const void* q, ce_layout q_layout, const void* p, ce_layout p_layout, ce_dtype dt,
+                     int64_t n_rows, int64_t V, float* kl, float* lse_q, float* lse_p, hipStream_t stream);
+
+/* kl_forward with lanes_per_row as in ce_forward_lanes (-1 is not accepted here). */
+ce_status kl_forward_lanes(const void* q, ce_layout q_layout, const void* p, ce_layout p_layout, ce_dtype dt,
+                           int64_t n_rows, int64_t V, float* kl, float* lse_q, float* lse_p,
+                           int32_t lanes_per_row, hipStream_t stream);
+
+/*
+ * kl_vjp: dq_ij = g_i * (exp((q_ij - m_q,i) - log s_q,i) - exp((p_ij - m_p,i) - log s_p,i)),
+ * the gradient of sum_i g_i kl_i with respect to the student logits (the page's
+ * reference gradient exp(lq) - exp(lp)).
+ *
+ *   q, p, dt, layouts  as in kl_forward; lse_q, lse_p as kl_forward wrote them.
+ *   g        float32 [n_rows].
+ *   dq       [n_rows rows of V] of dtype `dt`, through `dq_layout` (written); computed
+ *            in float32 and rounded to nearest, ties to even.
+ * dq may be q itself (same layout); otherwise it must not overlap q.  It must never
+ * overlap p, lse_q, lse_p or g (CE_ERR_ALIAS).
+ */
+ce_status kl_vjp(const void* q, ce_layout q_layout, const void* p, ce_layout p_layout, ce_dtype dt,
+                 const float* lse_q, const float* lse_p, const float* g, int64_t n_rows, int64_t V, void* dq,
+                 ce_layout dq_layout, hipStream_t stream);
+
+/* kl_vjp with lanes_per_row as in ce_vjp_lanes (-1 is not accepted here). */
+ce_status kl_vjp_lanes(const void* q, ce_layout q_layout, const void* p, ce_layout p_layout, ce_dtype dt,
+                       const float* lse_q, const float* lse_p, const float* g, int64_t n_rows, int64_t V,
+                       void* dq, ce_layout dq_layout, int32_t lanes_per_row, hipStream_t stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* ce_status_string(ce_status status);

@@ -27,7 +27,8 @@ STATUS = {
 
 # every symbol include/ce_mi355x.h declares
 EXPORTS = ("ce_forward", "ce_forward_lanes", "ce_vjp", "ce_vjp_lanes", "lce_workspace_size",
-           "lce_forward", "lce_backward_workspace_size", "lce_backward", "ce_status_string")
+           "lce_forward", "lce_backward_workspace_size", "lce_backward", "kl_forward", "kl_forward_lanes",
+           "kl_vjp", "kl_vjp_lanes", "ce_status_string")
 
 
 class CELayout(ctypes.Structure):
@@ -64,9 +65,17 @@ def lib() -> ctypes.CDLL:
         L.lce_backward_workspace_size.argtypes = [_i64, _i64, _i64]
         L.lce_backward_workspace_size.restype = _sz
         L.lce_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _sz, _vp]
+        L.kl_forward.argtypes = [_vp, CELayout, _vp, CELayout, ctypes.c_int, _i64, _i64, _vp, _vp, _vp, _vp]
+        L.kl_forward_lanes.argtypes = [_vp, CELayout, _vp, CELayout, ctypes.c_int, _i64, _i64, _vp, _vp, _vp,
+                                       _i32, _vp]
+        L.kl_vjp.argtypes = [_vp, CELayout, _vp, CELayout, ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _vp,
+                             CELayout, _vp]
+        L.kl_vjp_lanes.argtypes = [_vp, CELayout, _vp, CELayout, ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _vp,
+                                   CELayout, _i32, _vp]
         L.ce_status_string.argtypes = [ctypes.c_int]
         L.ce_status_string.restype = ctypes.c_char_p
-        for name in ("ce_forward", "ce_forward_lanes", "ce_vjp", "ce_vjp_lanes", "lce_forward", "lce_backward"):
+        for name in ("ce_forward", "ce_forward_lanes", "ce_vjp", "ce_vjp_lanes", "lce_forward", "lce_backward",
+                     "kl_forward", "kl_forward_lanes", "kl_vjp", "kl_vjp_lanes"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -207,4 +216,56 @@ def lce_backward(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: t
                             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(H))
     _check(st, "lce_backward")
     return dH, dW
+
+
+def _view(t: torch.Tensor, name: str):
+    if t.stride(-1) != 1 and t.shape[-1] > 1:
+        raise ValueError(f"{name} needs unit column stride")
+    return rows_layout(t)
+
+
+def kl_forward(q: torch.Tensor, p: torch.Tensor, kl=None, lse_q=None, lse_p=None, lanes_per_row: int = 0):
+    """Per-row (kl [n], lse_q [n, 2], lse_p [n, 2]) of the teacher p from the student q."""
+    if q.dtype != p.dtype or q.shape != p.shape:
+        raise ValueError("q and p must have the same dtype and shape")
+    ql, n, V = _view(q, "q")
+    pl, _, _ = _view(p, "p")
+    dev = q.device
+    kl = torch.empty(n, dtype=torch.float32, device=dev) if kl is None else kl
+    lse_q = torch.empty(n, 2, dtype=torch.float32, device=dev) if lse_q is None else lse_q
+    lse_p = torch.empty(n, 2, dtype=torch.float32, device=dev) if lse_p is None else lse_p
+    _need(kl, torch.float32, n, "kl")
+    _need(lse_q, torch.float32, 2 * n, "lse_q")
+    _need(lse_p, torch.float32, 2 * n, "lse_p")
+    args = (_ptr(q), ql, _ptr(p), pl, DTYPE_CODE[q.dtype], n, V, _ptr(kl), _ptr(lse_q), _ptr(lse_p))
+    if lanes_per_row == 0:
+        st = lib().kl_forward(*args, _stream(q))
+    else:
+        st = lib().kl_forward_lanes(*args, int(lanes_per_row), _stream(q))
+    _check(st, "kl_forward")
+    return kl, lse_q, lse_p
+
+
+def kl_vjp(q: torch.Tensor, p: torch.Tensor, lse_q: torch.Tensor, lse_p: torch.Tensor, g: torch.Tensor, dq=None,
+           lanes_per_row: int = 0):
+    """dq = g * (softmax(q) - softmax(p)) from the saved pairs; same shape and dtype as q."""
+    if q.dtype != p.dtype or q.shape != p.shape:
+        raise ValueError("q and p must have the same dtype and shape")
+    ql, n, V = _view(q, "q")
+    pl, _, _ = _view(p, "p")
+    _need(lse_q, torch.float32, 2 * n, "lse_q")
+    _need(lse_p, torch.float32, 2 * n, "lse_p")
+    _need(g, torch.float32, n, "g")
+    if dq is None:
+        dq = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if dq.dtype != q.dtype or dq.shape != q.shape:
+        raise ValueError("dq must match q in dtype and shape")
+    dl, _, _ = _view(dq, "dq")
+    args = (_ptr(q), ql, _ptr(p), pl, DTYPE_CODE[q.dtype], _ptr(lse_q), _ptr(lse_p), _ptr(g), n, V, _ptr(dq), dl)
+    if lanes_per_row == 0:
+        st = lib().kl_vjp(*args, _stream(q))
+    else:
+        st = lib().kl_vjp_lanes(*args, int(lanes_per_row), _stream(q))
+    _check(st, "kl_vjp")
+    return dq
 

@@ -220,6 +220,64 @@ ce_status vjp_impl(const void* logits, ce_layout in, ce_dtype dt, const int32_t*
     return from_hip(ce::launch_ce_vjp(c));
 }
 
+bool lanes_ok_kl(int32_t lanes) {
+    return lanes == 0 || (lanes >= 1 && lanes <= 1024 && (lanes & (lanes - 1)) == 0);
+}
+
+ce_status kl_forward_impl(const void* q, ce_layout ql, const void* p, ce_layout pl, ce_dtype dt, int64_t n_rows,
+                          int64_t V, float* kl, float* lse_q, float* lse_p, int32_t lanes, hipStream_t stream) {
+    if (!valid_dtype((int)dt)) return CE_ERR_DTYPE;
+    if (n_rows < 0 || V < 1 || V > kMaxV || !lanes_ok_kl(lanes)) return CE_ERR_SHAPE;
+    if (n_rows == 0) return CE_OK;
+    if (!q || !p || !kl || !lse_q || !lse_p) return CE_ERR_NULL;
+    const int es = esize(dt);
+    if (!layout_ok(ql, n_rows, V, false) || !layout_ok(pl, n_rows, V, false) || !aligned(q, es) ||
+        !aligned(p, es) || !aligned(kl, 4) || !aligned(lse_q, 8) || !aligned(lse_p, 8))
+        return CE_ERR_LAYOUT;
+    const Extent ins[2] = {view_extent(q, ql, n_rows, V, es), view_extent(p, pl, n_rows, V, es)};
+    const Extent outs[3] = {flat_extent(kl, n_rows * 4), flat_extent(lse_q, n_rows * 8),
+                            flat_extent(lse_p, n_rows * 8)};
+    for (const Extent& o : outs)
+        for (const Extent& i : ins)
+            if (overlaps(o, i)) return CE_ERR_ALIAS;
+    if (overlaps(outs[0], outs[1]) || overlaps(outs[0], outs[2]) || overlaps(outs[1], outs[2])) return CE_ERR_ALIAS;
+    int cus = 0;
+    if (ce_status s = device_cus(&cus)) return s;
+    Plan plan;
+    if (ce_status s = make_plan(false, V, es, n_rows, lanes, false, cus, &plan)) return s;
+    ce::KLFwdCall c{q, host_layout(ql, n_rows), p, host_layout(pl, n_rows), (Dt)dt, n_rows, V, kl, lse_q, lse_p,
+                    plan, stream};
+    return from_hip(ce::launch_kl_forward(c));
+}
+
+ce_status kl_vjp_impl(const void* q, ce_layout ql, const void* p, ce_layout pl, ce_dtype dt, const float* lse_q,
+                      const float* lse_p, const float* g, int64_t n_rows, int64_t V, void* dq, ce_layout dl,
+                      int32_t lanes, hipStream_t stream) {
+    if (!valid_dtype((int)dt)) return CE_ERR_DTYPE;
+    if (n_rows < 0 || V < 1 || V > kMaxV || !lanes_ok_kl(lanes)) return CE_ERR_SHAPE;
+    if (n_rows == 0) return CE_OK;
+    if (!q || !p || !lse_q || !lse_p || !g || !dq) return CE_ERR_NULL;
+    const int es = esize(dt);
+    if (!layout_ok(ql, n_rows, V, false) || !layout_ok(pl, n_rows, V, false) || !layout_ok(dl, n_rows, V, true) ||
+        !aligned(q, es) || !aligned(p, es) || !aligned(dq, es) || !aligned(lse_q, 8) || !aligned(lse_p, 8) ||
+        !aligned(g, 4))
+        return CE_ERR_LAYOUT;
+    const Extent ex_q = view_extent(q, ql, n_rows, V, es);
+    const Extent ex_d = view_extent(dq, dl, n_rows, V, es);
+    const bool in_place = q == dq && same_layout(ql, dl, n_rows);
+    if (!in_place && overlaps(ex_q, ex_d)) return CE_ERR_ALIAS;
+    if (overlaps(ex_d, view_extent(p, pl, n_rows, V, es)) || overlaps(ex_d, flat_extent(lse_q, n_rows * 8)) ||
+        overlaps(ex_d, flat_extent(lse_p, n_rows * 8)) || overlaps(ex_d, flat_extent(g, n_rows * 4)))
+        return CE_ERR_ALIAS;
+    int cus = 0;
+    if (ce_status s = device_cus(&cus)) return s;
+    Plan plan;
+    if (ce_status s = make_plan(false, V, es, n_rows, lanes, true, cus, &plan)) return s;
+    ce::KLVjpCall c{q,     host_layout(ql, n_rows), p, host_layout(pl, n_rows), (Dt)dt, lse_q, lse_p, g, n_rows,
+                    V,     dq, host_layout(dl, n_rows), plan, stream};
+    return from_hip(ce::launch_kl_vjp(c));
+}
+
 }  // namespace
 
 extern "C" {
@@ -308,6 +366,30 @@ ce_status lce_backward(const void* H, const void* W, const int32_t* targets, con
     if (N == 0) return from_hip(ce::launch_fill_zero_f32(dW, V * D, stream));
     ce::LceBackwardCall c{H, W, targets, lse, g, N, D, V, dH, dW, workspace, stream};
     return ce::run_lce_backward(c) == ce::LceBackwardStatus::kOk ? CE_OK : CE_ERR_LAUNCH;
+}
+
+ce_status kl_forward(const void* q, ce_layout q_layout, const void* p, ce_layout p_layout, ce_dtype dt,
+                     int64_t n_rows, int64_t V, float* kl, float* lse_q, float* lse_p, hipStream_t stream) {
+    return kl_forward_impl(q, q_layout, p, p_layout, dt, n_rows, V, kl, lse_q, lse_p, 0, stream);
+}
+
+ce_status kl_forward_lanes(const void* q, ce_layout q_layout, const void* p, ce_layout p_layout, ce_dtype dt,
+                           int64_t n_rows, int64_t V, float* kl, float* lse_q, float* lse_p, int32_t lanes_per_row,
+                           hipStream_t stream) {
+    return kl_forward_impl(q, q_layout, p, p_layout, dt, n_rows, V, kl, lse_q, lse_p, lanes_per_row, stream);
+}
+
+ce_status kl_vjp(const void* q, ce_layout q_layout, const void* p, ce_layout p_layout, ce_dtype dt,
+                 const float* lse_q, const float* lse_p, const float* g, int64_t n_rows, int64_t V, void* dq,
+                 ce_layout dq_layout, hipStream_t stream) {
+    return kl_vjp_impl(q, q_layout, p, p_layout, dt, lse_q, lse_p, g, n_rows, V, dq, dq_layout, 0, stream);
+}
+
+ce_status kl_vjp_lanes(const void* q, ce_layout q_layout, const void* p, ce_layout p_layout, ce_dtype dt,
+                       const float* lse_q, const float* lse_p, const float* g, int64_t n_rows, int64_t V, void* dq,
+                       ce_layout dq_layout, int32_t lanes_per_row, hipStream_t stream) {
+    return kl_vjp_impl(q, q_layout, p, p_layout, dt, lse_q, lse_p, g, n_rows, V, dq, dq_layout, lanes_per_row,
+                       stream);
 }
 
 const char* ce_status_string(ce_status s) {

@@ -22,7 +22,13 @@ constexpr float kNegInf = -__builtin_inff();
 // gap between two large logits is exact in that difference and would be lost in
 // z * log2(e) - m * log2(e).
 __device__ __forceinline__ float exp_e(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
-__device__ __forceinline__ float log_e(float x) { return __builtin_amdgcn_logf(x) * kLn2; }
+// log s is rounded on its own (the multiply is not fused into whatever consumes it), so
+// a stored log s is exactly the value the loss was assembled from, and two equal sums
+// give two equal logs wherever they are used.
+__device__ __forceinline__ float log_e(float x) {
+#pragma clang fp contract(off)
+    return __builtin_amdgcn_logf(x) * kLn2;
+}
 
 // Reference point for rescaling.  A state that has seen only -inf (or nothing) has
 // m = -inf and s = 0; rescaling against -inf would form exp(-inf - -inf) = NaN, so it
@@ -37,8 +43,10 @@ struct MS {
 __device__ __forceinline__ MS ms_empty() { return MS{kNegInf, 0.0f}; }
 
 // Merge two states.  Symmetric in its arguments bit for bit (the two products are
-// rounded separately before the add), so lanes exchanging states agree exactly.
+// rounded separately before the add: no fused multiply-add), so lanes exchanging
+// states agree exactly.
 __device__ __forceinline__ MS ms_merge(MS a, MS b) {
+#pragma clang fp contract(off)
     float m = fmaxf(a.m, b.m);
     float r = ref_point(m);
     float pa = __fmul_rn(a.s, exp_e(a.m - r));

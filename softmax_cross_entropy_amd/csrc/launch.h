@@ -57,6 +57,42 @@ struct VjpCall {
 hipError_t launch_ce_forward(const FwdCall& c);
 hipError_t launch_ce_vjp(const VjpCall& c);
 
+// KL divergence of the teacher rows p from the student rows q (same dtype, own views).
+struct KLFwdCall {
+    const void* q;
+    HostLayout ql;
+    const void* p;
+    HostLayout pl;
+    Dt dt;
+    int64_t n_rows;
+    int64_t V;
+    float* kl;
+    float* lse_q;
+    float* lse_p;
+    Plan plan;
+    hipStream_t stream;
+};
+
+struct KLVjpCall {
+    const void* q;
+    HostLayout ql;
+    const void* p;
+    HostLayout pl;
+    Dt dt;
+    const float* lse_q;
+    const float* lse_p;
+    const float* g;
+    int64_t n_rows;
+    int64_t V;
+    void* dq;
+    HostLayout dl;
+    Plan plan;
+    hipStream_t stream;
+};
+
+hipError_t launch_kl_forward(const KLFwdCall& c);
+hipError_t launch_kl_vjp(const KLVjpCall& c);
+
 // lce_forward.  Workspace layout is described in lce_kernels.hip.
 struct LceCall {
     const void* H;

@@ -269,3 +269,14 @@ def linear_ce(N: int, D: int, V: int, seed_stream: int = 0, w_scale: float | Non
         W[v0:v1] = f32_to_bf16_bits(normal_f32(g, (v1 - v0, D), scale))
     y = uniform_targets(g, (N,), V)
     return H, W, y
+
+
+# --- KL divergence: student and teacher logits --------------------------------
+
+def kl_pair(rows: int, V: int, dtype: str, scale: float = 4.0, workload: int = 20, stream: int = 0):
+    """(q, p, g): student and teacher logits [rows, V] ~ N(0, 1) * scale, stored in dtype,
+    and g = 1.  "One barrier short", Run it yourself, draws both at scale 4 with V = 151,936."""
+    gen = rng(workload, stream)
+    q = encode(normal_f32(gen, (rows, V), scale), dtype)
+    p = encode(normal_f32(gen, (rows, V), scale), dtype)
+    return q, p, np.ones(rows, np.float32)

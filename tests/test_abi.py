@@ -175,6 +175,38 @@ def test_lce_backward_empty_batch_needs_only_w_and_dw():
     assert lbw(N=0, dW=None) == NULL
 
 
+P_P, P_KL, P_LQ, P_LP, P_DQ = (ctypes.c_void_p(A * k) for k in (300, 310, 320, 330, 340))
+
+
+def klf(q=P_LOGITS, ql=None, p=P_P, pl=None, dt=0, n=16, V=8, kl=P_KL, lq=P_LQ, lp=P_LP, lanes=0):
+    return abi.lib().kl_forward_lanes(q, ql or lay(n, V), p, pl or lay(n, V), dt, n, V, kl, lq, lp, lanes, None)
+
+
+def klv(q=P_LOGITS, ql=None, p=P_P, pl=None, dt=0, lq=P_LQ, lp=P_LP, g=P_G, n=16, V=8, dq=P_DQ, dl=None, lanes=0):
+    return abi.lib().kl_vjp_lanes(q, ql or lay(n, V), p, pl or lay(n, V), dt, lq, lp, g, n, V, dq, dl or lay(n, V),
+                                  lanes, None)
+
+
+def test_kl_rejects_bad_arguments():
+    assert klf(dt=3) == DTYPE and klv(dt=-1) == DTYPE
+    assert klf(V=0) == SHAPE and klf(n=-1) == SHAPE
+    assert klf(lanes=-1) == SHAPE and klv(lanes=3) == SHAPE and klf(lanes=2048) == SHAPE
+    assert klf(n=0, q=None) == OK and klv(n=0, dq=None) == OK
+    for name in ("q", "p", "kl", "lq", "lp"):
+        assert klf(**{name: None}) == NULL, name
+    for name in ("q", "p", "lq", "lp", "g", "dq"):
+        assert klv(**{name: None}) == NULL, name
+    assert klf(p=ctypes.c_void_p(300 * A + 2)) == LAYOUT  # fp32 p not 4-byte aligned
+    assert klf(lq=ctypes.c_void_p(320 * A + 4)) == LAYOUT
+    assert klv(dl=abi.CELayout(16, 4, 64)) == LAYOUT  # output rows overlap
+    assert klf(kl=ctypes.c_void_p(300 * A + 16)) == ALIAS  # kl inside p
+    assert klf(lp=ctypes.c_void_p(310 * A)) == ALIAS  # lse_p over kl
+    assert klv(dq=ctypes.c_void_p(300 * A)) == ALIAS  # dq over p
+    assert klv(dq=ctypes.c_void_p(A + 64)) == ALIAS  # dq overlapping q, not in place
+    assert klv(dq=ctypes.c_void_p(5 * A)) == ALIAS  # dq over g
+    assert klv(dq=P_LOGITS) in (OK, DEVICE)  # in place, identical layout
+
+
 @pytest.mark.skipif(os.environ.get("HIP_VISIBLE_DEVICES", None) is not None or os.path.exists("/dev/kfd"),
                     reason="only meaningful without a GPU")
 def test_valid_call_without_device_reports_device_error():
@@ -183,3 +215,5 @@ def test_valid_call_without_device_reports_device_error():
     assert lce() == DEVICE
     assert lbw() == DEVICE
     assert lbw(H=None, t=None, lse=None, g=None, dH=None, ws=None, N=0, wsb=0) == DEVICE
+    assert klf() == DEVICE
+    assert klv() == DEVICE
