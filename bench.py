@@ -6,8 +6,10 @@ One step is one pass of the whole path over one batch of synthetic input:
   * lce_forward on bf16 H [8192 x 4096] ~ N(0,1), W [151,936 x 4096] ~ N(0, 1/D),
     uniform targets: the linear-CE configuration.
 After the timed steps, lce_backward (dH, dW of the same linear-CE loss, upstream
-gradient U[0.25, 2)) is timed on its own loop and reported under parts/rooflines; it
-is not part of the step.
+gradient U[0.25, 2)) and kl_forward + kl_vjp (fp32 student and teacher logits
+[512 x 151,936] ~ N(0, 16), the shape "One barrier short" reproduces its race on; two
+copies alternate) are timed on their own loops and reported under parts/rooflines;
+they are not part of the step.
 Inputs are resident in HBM before the timed region.  Two copies of the logits
 alternate between steps (each copy is 622 MB, larger than the 256 MB Infinity Cache,
 so no step reads logits cached by the previous one).
@@ -31,6 +33,7 @@ import time
 import numpy as np
 
 CE_ROWS, CE_V = 2048, 151936
+KL_ROWS, KL_V = 512, 151936
 LCE_N, LCE_D, LCE_V = 8192, 4096, 151936
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
@@ -63,7 +66,8 @@ TRAFFIC = {
 def source_sha(kernel):
     """sha256 (first 16 hex digits) of the kernel's source file and the device header it
     includes."""
-    fname = "lce_kernels.hip" if kernel.startswith("lce") else "ce_kernels.hip"
+    fname = ("lce_kernels.hip" if kernel.startswith("lce") else
+             "kl_kernels.hip" if kernel.startswith("kl") else "ce_kernels.hip")
     h = hashlib.sha256()
     for f in (fname, "device_common.h"):
         with open(os.path.join(CSRC, f), "rb") as fh:
@@ -87,6 +91,13 @@ def ce_bytes(rows, V, e):
     return fwd, vjp
 
 
+def kl_bytes(rows, V, e):
+    """Algorithmic HBM bytes per call: the forward reads both rows and writes kl (4)
+    and the two (m, log s) pairs (16); the VJP reads both rows, the pairs and g (20)
+    and writes the student gradient."""
+    return rows * (2 * V * e + 20), rows * (3 * V * e + 20)
+
+
 def lce_flops(N, D, V):
     return 2.0 * N * D * V
 
@@ -97,6 +108,7 @@ def cpu_baseline(ce_batch, lce_inputs, lce_rows=32):
 
     from oracle import ce as oce
     from oracle import lce as olce
+    from softmax_cross_entropy_amd import inputs
 
     b = ce_batch
     t0 = time.perf_counter()
@@ -117,6 +129,14 @@ def cpu_baseline(ce_batch, lce_inputs, lce_rows=32):
     t0 = time.perf_counter()
     olce.grad64(olce.decode_bf16(H[rows]), W64, y[rows], g_up[rows])
     lbw_s = time.perf_counter() - t0
+    from oracle import kl as okl
+    kq, kp, kg = inputs.kl_pair(32, KL_V, "f32", scale=4.0)
+    t0 = time.perf_counter()
+    zq, zp = kq.astype(np.float64), kp.astype(np.float64)
+    okl.forward(zq, zp)
+    okl.grad(zq, zp, kg)
+    kl_s = time.perf_counter() - t0
+    kf_b, kv_b = kl_bytes(32, KL_V, 4)
     blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     return {
         "value": (fwd_b + vjp_b) / ce_s / 1e9,
@@ -129,6 +149,8 @@ def cpu_baseline(ce_batch, lce_inputs, lce_rows=32):
                 "cores": blas, "seconds": lce_s,
                 "sample": f"lce oracle (float64 BLAS matmul + CE) on {lce_rows} of {LCE_N} rows, "
                           f"all {LCE_V} columns"},
+        "kl": {"value": (kf_b + kv_b) / kl_s / 1e9, "unit": "GB/s", "cores": 1, "seconds": kl_s,
+               "sample": f"KL fwd+grad oracle (float64 NumPy) on 32 of {KL_ROWS} rows, all {KL_V} columns"},
         "lce_backward": {"value": 3 * lce_flops(lce_rows, LCE_D, LCE_V) / lbw_s / 1e12, "unit": "TFLOP/s",
                          "cores": blas, "seconds": lbw_s,
                          "sample": f"lce gradient oracle (float64: logits, dZ, dZ W, dZ^T H) on {lce_rows} "
@@ -143,7 +165,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--parts", default="ce,lce,lbw", help="comma list of ce, lce, lbw (lce_backward)")
+    ap.add_argument("--parts", default="ce,lce,lbw,kl",
+                    help="comma list of ce, lce, lbw (lce_backward), kl (kl_forward + kl_vjp)")
     ap.add_argument("--bwd-steps", type=int, default=5, help="timed lce_backward calls")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run one elementwise copy (torch.neg) of MIB MiB fp32 first, so a counter "
@@ -227,6 +250,33 @@ def main():
     def ms(a, b):
         return [ev[i][a].elapsed_time(ev[i][b]) for i in range(K)]
 
+    kl_ms = None
+    if "kl" in parts:
+        kq, kp, kg = inputs.kl_pair(KL_ROWS, KL_V, "f32", scale=4.0)
+        kq2, kp2, _ = inputs.kl_pair(KL_ROWS, KL_V, "f32", scale=4.0, stream=1)
+        KQ = [torch.from_numpy(kq).to(dev), torch.from_numpy(kq2).to(dev)]
+        KP = [torch.from_numpy(kp).to(dev), torch.from_numpy(kp2).to(dev)]
+        KG = torch.from_numpy(kg).to(dev)
+        kl_o = torch.empty(KL_ROWS, device=dev)
+        lq_o = torch.empty(KL_ROWS, 2, device=dev)
+        lp_o = torch.empty(KL_ROWS, 2, device=dev)
+        dq_o = torch.empty_like(KQ[0])
+        for i in range(3):
+            abi.kl_forward(KQ[i % 2], KP[i % 2], kl=kl_o, lse_q=lq_o, lse_p=lp_o)
+            abi.kl_vjp(KQ[i % 2], KP[i % 2], lq_o, lp_o, KG, dq=dq_o)
+        torch.cuda.synchronize()
+        kev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+        for i in range(K):
+            kev[i][0].record(stream)
+            abi.kl_forward(KQ[i % 2], KP[i % 2], kl=kl_o, lse_q=lq_o, lse_p=lp_o)
+            kev[i][1].record(stream)
+            abi.kl_vjp(KQ[i % 2], KP[i % 2], lq_o, lp_o, KG, dq=dq_o)
+            kev[i][2].record(stream)
+        torch.cuda.synchronize()
+        kl_ms = (float(np.mean([e[0].elapsed_time(e[1]) for e in kev])),
+                 float(np.mean([e[1].elapsed_time(e[2]) for e in kev])))
+        del KQ, KP, dq_o
+
     bwd_ms = None
     if "lbw" in parts and lce_in is not None:
         G_up = torch.from_numpy(np.random.default_rng([5, 0]).uniform(0.25, 2.0, LCE_N).astype(np.float32)).to(dev)
@@ -302,6 +352,18 @@ def main():
                                      "kernels": "per 8192-column chunk: lce_tile (dZ epilogue) + two rocBLAS "
                                                 "GEMMs (one lce_backward call)"}
         cfg["lce_backward"] = {"N": LCE_N, "D": LCE_D, "V": LCE_V, "out": "fp32 dH, dW", "timed": "apart"}
+    if kl_ms is not None:
+        kf_b, kv_b = kl_bytes(KL_ROWS, KL_V, 4)
+        kf, kv = kl_ms
+        parts_out["kl_fwd_vjp"] = {"ms": kf + kv, "GB_s": (kf_b + kv_b) / ((kf + kv) * 1e-3) / 1e9,
+                                   "frac_hbm_peak": (kf_b + kv_b) / ((kf + kv) * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                   "algorithmic_bytes": kf_b + kv_b, "fwd_ms": kf, "vjp_ms": kv, "in_step": False}
+        for name, byts, t in (("kl_forward", kf_b, kf), ("kl_vjp", kv_b, kv)):
+            a = byts / (t * 1e-3) / 1e9
+            rooflines[name] = {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": a / HBM_PEAK_GBS, "traffic": traffic_for(name), "ms": t,
+                               "algorithmic_bytes": byts}
+        cfg["kl"] = {"rows": KL_ROWS, "V": KL_V, "dtype": "f32", "scale": 4.0, "timed": "apart"}
     cfg["workload"] = " + ".join(cfg["workload"])
     out["config"] = cfg
     out["parts"] = parts_out
