@@ -150,7 +150,13 @@ ce_status ce_vjp(const void* logits, ce_layout in, ce_dtype dt, const int32_t* t
                  const float* lse, const float* g, int64_t n_rows, int64_t V, void* dlogits,
                  ce_layout out, hipStream_t stream);
 
-/* ce_vjp_lanes: ce_vjp with lanes_per_row chosen as in ce_forward_lanes. */
+/*
+ * ce_vjp_lanes: ce_vjp with lanes_per_row chosen as in ce_forward_lanes.  With
+ * lanes_per_row = 0 a row spanning at least 2048 16-byte vectors is cut into chunks
+ * of 512 vectors, each handled by its own 256-thread workgroup (ce_vjp does the
+ * same); a power of two keeps whole rows on that many lanes.  Every layout computes
+ * each element with the same float32 operations, so all give identical bits.
+ */
 ce_status ce_vjp_lanes(const void* logits, ce_layout in, ce_dtype dt, const int32_t* targets,
                        const float* lse, const float* g, int64_t n_rows, int64_t V, void* dlogits,
                        ce_layout out, int32_t lanes_per_row, hipStream_t stream);

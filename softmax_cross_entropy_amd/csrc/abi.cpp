@@ -116,7 +116,7 @@ ce_status make_plan(bool narrow_ok, int64_t V, int es, int64_t n_rows, int32_t l
                     int cus, Plan* plan) {
     const int vec = 16 / es;
     const int64_t nvec = (V + vec - 1) / vec;
-    Plan p{0, 0, 0};
+    Plan p{0, 0, 0, 0};
     if (lanes_req == -1) {
         if (!narrow_ok) return CE_ERR_LAYOUT;
         p.narrow_nv = (int)(V / vec);
@@ -147,6 +147,24 @@ ce_status make_plan(bool narrow_ok, int64_t V, int es, int64_t n_rows, int32_t l
     if (p.blocks < 1) p.blocks = 1;
     *plan = p;
     return CE_OK;
+}
+
+// Chunked layout for the VJP of long rows: work items of one (row, chunk of
+// 256 * kChunkU vectors) pair each, on a grid of at most 256 workgroups per CU that
+// loops over the rest.  Taken when a row spans at least kChunkMinVec 16-byte vectors
+// (counting a partial one); shorter rows keep whole-row layouts.
+constexpr int64_t kChunkMinVec = 2048;
+
+bool chunk_plan(int64_t V, int es, int64_t n_rows, int cus, Plan* plan) {
+    const int vec = 16 / es;
+    const int64_t nvec = (V + vec - 1) / vec;
+    if (nvec < kChunkMinVec) return false;
+    const int64_t per_chunk = 256 * (int64_t)ce::kChunkU;
+    const int64_t chunks = (nvec + per_chunk - 1) / per_chunk;
+    const int64_t items = n_rows * chunks;
+    const int64_t cap = (int64_t)cus * 256;
+    *plan = Plan{0, 0, items < cap ? items : cap, chunks};
+    return true;
 }
 
 ce_status from_hip(hipError_t e) { return e == hipSuccess ? CE_OK : CE_ERR_LAUNCH; }
@@ -214,7 +232,8 @@ ce_status vjp_impl(const void* logits, ce_layout in, ce_dtype dt, const int32_t*
     const bool narrow_ok = rows_aligned16(logits, in, n_rows, es) && rows_aligned16(dlogits, out, n_rows, es) &&
                            V % vec == 0 && (V / vec == 1 || V / vec == 2 || V / vec == 4 || V / vec == 8);
     Plan plan;
-    if (ce_status s = make_plan(narrow_ok, V, es, n_rows, lanes, true, cus, &plan)) return s;
+    if (lanes != 0 || !chunk_plan(V, es, n_rows, cus, &plan))
+        if (ce_status s = make_plan(narrow_ok, V, es, n_rows, lanes, true, cus, &plan)) return s;
     ce::VjpCall c{logits, host_layout(in, n_rows), (Dt)dt, targets, lse, g, n_rows, V, dlogits,
                   host_layout(out, n_rows), plan, stream};
     return from_hip(ce::launch_ce_vjp(c));
@@ -272,7 +291,8 @@ ce_status kl_vjp_impl(const void* q, ce_layout ql, const void* p, ce_layout pl, 
     int cus = 0;
     if (ce_status s = device_cus(&cus)) return s;
     Plan plan;
-    if (ce_status s = make_plan(false, V, es, n_rows, lanes, true, cus, &plan)) return s;
+    if (lanes != 0 || !chunk_plan(V, es, n_rows, cus, &plan))
+        if (ce_status s = make_plan(false, V, es, n_rows, lanes, true, cus, &plan)) return s;
     ce::KLVjpCall c{q,     host_layout(ql, n_rows), p, host_layout(pl, n_rows), (Dt)dt, lse_q, lse_p, g, n_rows,
                     V,     dq, host_layout(dl, n_rows), plan, stream};
     return from_hip(ce::launch_kl_vjp(c));

@@ -329,6 +329,57 @@ __global__ __launch_bounds__(G > kBlock ? G : kBlock) void ce_vjp_lanes(VjpArgs 
     }
 }
 
+// Long rows: the VJP is elementwise, so each row is cut into chunks of 256 * U vectors
+// and every (row, chunk) pair is one work item of a 256-thread workgroup.  With few
+// rows, one workgroup per row leaves too few workgroups for the memory system; many
+// short work items keep it full.  The target column lies in exactly one chunk (or among
+// the row's unaligned head and tail elements, which chunk 0 takes), so it is stored
+// again exactly once, as in the row-wide layouts.
+template <typename T, int U>
+__global__ __launch_bounds__(kBlock) void ce_vjp_chunks(VjpArgs a, int64_t chunks_per_row) {
+    constexpr int kVec = Elem<T>::kVec;
+    constexpr int64_t kChunkVec = (int64_t)kBlock * U;
+    const int t = threadIdx.x;
+    const int64_t items = a.n_rows * chunks_per_row;
+    for (int64_t w = blockIdx.x; w < items; w += gridDim.x) {
+        const int64_t r = w / chunks_per_row;
+        const int64_t c = w - r * chunks_per_row;
+        const T* row = static_cast<const T*>(a.logits) + row_offset(r, a.in);
+        T* orow = static_cast<T*>(a.dlogits) + row_offset(r, a.out);
+        const RowGrad rg = load_row_grad(a, r);
+        if (((((uintptr_t)row) ^ ((uintptr_t)orow)) & 15u) == 0) {
+            RowSplit<T> sp(row, a.V);
+            const char* vb = reinterpret_cast<const char*>(row + sp.head);
+            char* ob = reinterpret_cast<char*>(orow + sp.head);
+            const int64_t v0 = c * kChunkVec + t;
+            if (c * kChunkVec + kChunkVec <= sp.nvec) {
+                U4 buf[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) buf[u] = load_u4_stream(vb + (v0 + (int64_t)u * kBlock) * 16);
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    grad_store_vec<T>(buf[u], rg, sp.head + (v0 + (int64_t)u * kBlock) * kVec,
+                                      ob + (v0 + (int64_t)u * kBlock) * 16, orow);
+            } else {
+                for (int64_t j = v0; j < sp.nvec; j += kBlock)
+                    grad_store_vec<T>(load_u4_stream(vb + j * 16), rg, sp.head + j * kVec, ob + j * 16, orow);
+            }
+            if (c == 0) {
+                const int64_t ns = sp.n_scalar(a.V);
+                for (int64_t k = t; k < ns; k += kBlock) {
+                    const int64_t idx = sp.scalar_index(k);
+                    Elem<T>::store1(orow + idx, grad_elem(Elem<T>::load1(row + idx), rg, idx == rg.y));
+                }
+            }
+        } else {
+            const int64_t e0 = c * kChunkVec * kVec;
+            const int64_t e1 = e0 + kChunkVec * kVec < a.V ? e0 + kChunkVec * kVec : a.V;
+            for (int64_t idx = e0 + t; idx < e1; idx += kBlock)
+                Elem<T>::store1(orow + idx, grad_elem(Elem<T>::load1(row + idx), rg, idx == rg.y));
+        }
+    }
+}
+
 // ---- dispatch -------------------------------------------------------------------
 
 RowLayout dev_layout(const HostLayout& h) {
@@ -373,6 +424,10 @@ hipError_t vjp_typed(const VjpCall& c) {
               c.n_rows, c.V, c.dlogits, dev_layout(c.out)};
     const dim3 grid((unsigned)c.plan.blocks);
     constexpr int kU = Elem<T>::kVec == 8 ? 4 : 8;
+    if (c.plan.chunks > 0) {
+        hipLaunchKernelGGL((ce_vjp_chunks<T, kChunkU>), grid, dim3(kBlock), 0, c.stream, a, c.plan.chunks);
+        return hipGetLastError();
+    }
     if (c.plan.narrow_nv > 0) {
         switch (c.plan.narrow_nv) {
             case 1: hipLaunchKernelGGL((ce_vjp_narrow<T, 1, 4>), grid, dim3(kBlock), 0, c.stream, a); break;

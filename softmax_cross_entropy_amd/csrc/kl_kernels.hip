@@ -292,6 +292,74 @@ __global__ __launch_bounds__(G > kBlock ? G : kBlock) void kl_vjp_lanes(KLVjpArg
     }
 }
 
+// Long rows: the VJP is elementwise, so each row is cut into chunks of kChunkVec vectors
+// and every (row, chunk) pair is one work item of a 256-thread workgroup.  With few rows,
+// one workgroup per row leaves too few workgroups for the memory system; many short
+// work items keep it full.  Chunk 0 of a row also takes the row's unaligned head and
+// tail elements.
+template <typename T, int U>
+__global__ __launch_bounds__(kBlock) void kl_vjp_chunks(KLVjpArgs a, int64_t chunks_per_row) {
+    constexpr int kVec = Elem<T>::kVec;
+    constexpr int64_t kChunkVec = (int64_t)kBlock * U;
+    const int t = threadIdx.x;
+    const int64_t items = a.n_rows * chunks_per_row;
+    for (int64_t w = blockIdx.x; w < items; w += gridDim.x) {
+        const int64_t r = w / chunks_per_row;
+        const int64_t c = w - r * chunks_per_row;
+        const T* q = static_cast<const T*>(a.q) + row_offset(r, a.ql);
+        const T* p = static_cast<const T*>(a.p) + row_offset(r, a.pl);
+        T* d = static_cast<T*>(a.dq) + row_offset(r, a.dl);
+        const float2 lq = a.lse_q[r], lp = a.lse_p[r];
+        const KLRow rw{lq.x, lq.y * kLog2e, lp.x, lp.y * kLog2e, a.g[r]};
+        const uintptr_t aq = (uintptr_t)q, ap = (uintptr_t)p, ad = (uintptr_t)d;
+        if (((aq ^ ap) & 15u) == 0 && ((aq ^ ad) & 15u) == 0) {
+            RowSplit<T> sp(q, a.V);
+            const char* qb = reinterpret_cast<const char*>(q + sp.head);
+            const char* pb = reinterpret_cast<const char*>(p + sp.head);
+            char* db = reinterpret_cast<char*>(d + sp.head);
+            const int64_t v0 = c * kChunkVec + t;
+            if (c * kChunkVec + kChunkVec <= sp.nvec) {
+                U4 bq[U], bp[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    bq[u] = load_u4_stream(qb + (v0 + (int64_t)u * kBlock) * 16);
+                    bp[u] = load_u4_stream(pb + (v0 + (int64_t)u * kBlock) * 16);
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    float fq[kVec], fp[kVec], o[kVec];
+                    Elem<T>::unpack(bq[u], fq);
+                    Elem<T>::unpack(bp[u], fp);
+#pragma unroll
+                    for (int k = 0; k < kVec; ++k) o[k] = kl_grad(fq[k], fp[k], rw);
+                    store_u4(db + (v0 + (int64_t)u * kBlock) * 16, Elem<T>::pack(o));
+                }
+            } else {
+                for (int64_t j = v0; j < sp.nvec; j += kBlock) {
+                    float fq[kVec], fp[kVec], o[kVec];
+                    Elem<T>::unpack(load_u4_stream(qb + j * 16), fq);
+                    Elem<T>::unpack(load_u4_stream(pb + j * 16), fp);
+#pragma unroll
+                    for (int k = 0; k < kVec; ++k) o[k] = kl_grad(fq[k], fp[k], rw);
+                    store_u4(db + j * 16, Elem<T>::pack(o));
+                }
+            }
+            if (c == 0) {
+                const int64_t ns = sp.n_scalar(a.V);
+                for (int64_t k = t; k < ns; k += kBlock) {
+                    const int64_t i = sp.scalar_index(k);
+                    Elem<T>::store1(d + i, kl_grad(Elem<T>::load1(q + i), Elem<T>::load1(p + i), rw));
+                }
+            }
+        } else {
+            const int64_t e0 = c * kChunkVec * kVec;
+            const int64_t e1 = e0 + kChunkVec * kVec < a.V ? e0 + kChunkVec * kVec : a.V;
+            for (int64_t i = e0 + t; i < e1; i += kBlock)
+                Elem<T>::store1(d + i, kl_grad(Elem<T>::load1(q + i), Elem<T>::load1(p + i), rw));
+        }
+    }
+}
+
 RowLayout kl_layout(const HostLayout& h) {
     return RowLayout{h.rows_per_batch, h.row_stride, h.batch_stride, h.uniform};
 }
@@ -324,6 +392,10 @@ hipError_t kl_vjp_typed(const KLVjpCall& c) {
     KLVjpArgs a{c.q, kl_layout(c.ql), c.p, kl_layout(c.pl), reinterpret_cast<const float2*>(c.lse_q),
                 reinterpret_cast<const float2*>(c.lse_p), c.g, c.n_rows, c.V, c.dq, kl_layout(c.dl)};
     const dim3 grid((unsigned)c.plan.blocks);
+    if (c.plan.chunks > 0) {
+        hipLaunchKernelGGL((kl_vjp_chunks<T, kChunkU>), grid, dim3(kBlock), 0, c.stream, a, c.plan.chunks);
+        return hipGetLastError();
+    }
     constexpr int kU = Elem<T>::kVec == 8 ? 1 : 2;
     switch (c.plan.lanes) {
         case 1: hipLaunchKernelGGL((kl_vjp_lanes<T, 1, 1>), grid, dim3(kBlock), 0, c.stream, a); break;

@@ -24,7 +24,11 @@ struct Plan {
     int narrow_nv;
     int lanes;
     int64_t blocks;
+    int64_t chunks;  // VJP only: > 0 cuts each row into this many chunks of kChunkU * 256 vectors
 };
+
+// Vectors per thread in one chunk of the chunked VJP layout.
+constexpr int kChunkU = 2;
 
 struct FwdCall {
     const void* logits;

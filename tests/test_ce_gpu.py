@@ -257,6 +257,72 @@ def test_misaligned_rows(dtype, shift):
             check_grad(from_dev(d2), rd, dtype)
 
 
+# --- chunked VJP layout: rows of at least 2048 16-byte vectors ---------------
+
+CHUNK_ELEMS = {"f32": 2048, "f16": 4096, "bf16": 4096}  # 512 vectors of 16 bytes
+CHUNK_V = {"f32": [8189, 10243, 16384], "f16": [16377], "bf16": [16377, 20483, 32768]}
+
+
+def edge_targets(V, dtype):
+    """Targets at both row ends and within 8 elements of every chunk edge, so that for
+    any 16-byte phase of the row start some target falls in the unaligned head, the
+    tail, and the first and last vector of each chunk."""
+    c = CHUNK_ELEMS[dtype]
+    pos = [0, 1, 2, 3, V - 1, V - 2, V - 3, V - 4]
+    pos += [k * c + d for k in range(1, V // c + 1) for d in range(-8, 9)]
+    return np.array(sorted({q for q in pos if 0 <= q < V}), np.int32)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_chunked_vjp_edges(dtype):
+    """The default VJP layout for long rows against the oracle and, bit for bit, against
+    one workgroup per row: contiguous rows, views starting 1 and 3 elements off a
+    16-byte boundary, and an output in another 16-byte phase than the input."""
+    for V in CHUNK_V[dtype]:
+        y = edge_targets(V, dtype)
+        n = len(y)
+        for shift in (0, 1, 3):
+            b = inputs.normal_rows(n, V + shift + 2, dtype, workload=30, stream=V + shift)
+            full = to_dev(b.logits, dtype)
+            view = full[:, shift:shift + V]
+            z = decode(b.logits[:, shift:shift + V], dtype)
+            g = np.linspace(-1.5, 2.0, n).astype(np.float32)
+            rl, rm, rls = oce.forward(z, y)
+            rd = oce.grad(z, y, g, rm, rls)
+            t = torch.from_numpy(y).cuda()
+            gd = torch.from_numpy(g).cuda()
+            loss, lse = abi.ce_forward(view, t)
+            d = abi.ce_vjp(view, t, lse, gd)
+            rows = abi.ce_vjp(view, t, lse, gd, lanes_per_row=1024)
+            out = torch.empty(n, V + 1, dtype=TORCH_DT[dtype], device="cuda")[:, 1:]
+            d2 = abi.ce_vjp(view, t, lse, gd, dlogits=out)
+            torch.cuda.synchronize()
+            check_loss(from_dev(loss), rl, dtype)
+            check_grad(from_dev(d), rd, dtype, f"dlogits V={V} shift={shift}")
+            check_grad(from_dev(d2), rd, dtype, f"dlogits (other phase) V={V} shift={shift}")
+            assert np.array_equal(from_dev(d), from_dev(rows))
+            assert np.array_equal(from_dev(d2), from_dev(rows))
+
+
+def test_chunked_vjp_in_place_strided():
+    """In place on a [B, L - 1, V] view with V past the chunking threshold."""
+    x, y = inputs.strided_view_source(3, 7, 9001)
+    yv = inputs.shifted_targets(y)
+    X = torch.from_numpy(x).cuda()
+    view = X[:, :-1]
+    t = torch.from_numpy(yv).cuda()
+    g = torch.linspace(-2, 2, len(yv), dtype=torch.float32, device="cuda")
+    loss, lse = abi.ce_forward(view, t)
+    expect = abi.ce_vjp(view, t, lse, g, lanes_per_row=1024)
+    abi.ce_vjp(view, t, lse, g, dlogits=view)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(view), from_dev(expect))
+    assert np.array_equal(from_dev(X[:, -1]), x[:, -1])
+    z = decode(np.ascontiguousarray(x[:, :-1]).reshape(-1, 9001), "f32")
+    rl, rm, rls = oce.forward(z, yv)
+    check_grad(from_dev(view).reshape(-1, 9001), oce.grad(z, yv, from_dev(g), rm, rls), "f32")
+
+
 def test_degenerate_rows():
     """Out-of-range targets, all -inf, +inf and NaN entries: NaN loss and gradient rows."""
     V = 300

@@ -18,7 +18,7 @@ import torch
 
 from oracle import kl as okl
 from softmax_cross_entropy_amd import abi, inputs
-from tests.gpu_util import decode, from_dev, to_dev, ulp16
+from tests.gpu_util import TORCH_DT, decode, from_dev, to_dev, ulp16
 
 pytestmark = pytest.mark.gpu
 
@@ -159,3 +159,53 @@ def test_misaligned_rows_take_the_scalar_path():
     rk, *_ = okl.forward(zq, zp)
     check_kl(kl.cpu().numpy(), rk, "bf16")
     check_dq(from_dev(dq), zq, zp, np.ones(33), "bf16")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunked_vjp_phases(dtype):
+    """Rows of at least 2048 16-byte vectors take the chunked VJP layout by default:
+    against the oracle and, bit for bit, against one workgroup per row, with q starting
+    0, 1 or 3 elements off a 16-byte boundary, p and dq in the same or another phase."""
+    Vs = [8189, 10243] if dtype == "f32" else [16377, 20483]
+    for V in Vs:
+        for shift in (0, 1, 3):
+            q, p, g = inputs.kl_pair(19, V + 4, dtype, workload=27, stream=V + shift)
+            g = np.linspace(-1.0, 2.0, 19).astype(np.float32)
+            qd = to_dev(q, dtype)[:, shift:shift + V]
+            zq = decode(q, dtype)[:, shift:shift + V]
+            for pshift in (shift, 2):
+                pd = to_dev(p, dtype)[:, pshift:pshift + V]
+                zp = decode(p, dtype)[:, pshift:pshift + V]
+                kl, lq, lp = abi.kl_forward(qd, pd)
+                gd = torch.from_numpy(g).cuda()
+                dq = abi.kl_vjp(qd, pd, lq, lp, gd)
+                rows = abi.kl_vjp(qd, pd, lq, lp, gd, lanes_per_row=1024)
+                out = torch.empty(19, V + 1, dtype=TORCH_DT[dtype], device="cuda")[:, 1:]
+                dq2 = abi.kl_vjp(qd, pd, lq, lp, gd, dq=out)
+                torch.cuda.synchronize()
+                rk, *_ = okl.forward(zq, zp)
+                check_kl(kl.cpu().numpy(), rk, dtype)
+                check_dq(from_dev(dq), zq, zp, g, dtype)
+                check_dq(from_dev(dq2), zq, zp, g, dtype)
+                assert np.array_equal(from_dev(dq), from_dev(rows))
+                assert np.array_equal(from_dev(dq2), from_dev(rows))
+
+
+def test_chunked_vjp_in_place_strided():
+    B, L, V = 3, 7, 9001
+    q, p, g = inputs.kl_pair(B * L, V, "f32", workload=28)
+    qd = to_dev(q, "f32").view(B, L, V)
+    pd = to_dev(p, "f32").view(B, L, V)
+    qv, pv = qd[:, :-1], pd[:, 1:]
+    n = B * (L - 1)
+    gd = torch.from_numpy(np.linspace(0.5, 1.5, n).astype(np.float32)).cuda()
+    kl, lq, lp = abi.kl_forward(qv, pv)
+    expect = abi.kl_vjp(qv, pv, lq, lp, gd, lanes_per_row=1024)
+    before = qd.clone()
+    abi.kl_vjp(qv, pv, lq, lp, gd, dq=qv)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(qv), from_dev(expect))
+    assert torch.equal(qd[:, -1], before[:, -1])
+    ref_q = decode(q, "f32").reshape(B, L, V)[:, :-1].reshape(n, V)
+    ref_p = decode(p, "f32").reshape(B, L, V)[:, 1:].reshape(n, V)
+    check_dq(from_dev(qv).reshape(n, V), ref_q, ref_p, gd.cpu().numpy(), "f32")
