@@ -46,30 +46,38 @@ CSRC = os.path.join(ROOT, "softmax_cross_entropy_amd", "csrc")
 # HBM traffic per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this script
 # (--steps 1 --warmup 0 --calibrate-copy 1024), each scaled by the same counter on a
 # copy of known size; see profiles/.  Keyed by the sha256 of the kernel's source file
-# and device header at measurement time: a changed kernel reports traffic null until it is measured again.
+# and headers at measurement time: a changed kernel reports traffic null until it is measured again.
 TRAFFIC = {
     "ce_forward": {
-        "source_sha": "e0eaeaabbba34d72",
-        "bytes": 622629720
+        "source_sha": "120aeb018d6702d9",
+        "bytes": 622636909
     },
     "ce_vjp": {
-        "source_sha": "e0eaeaabbba34d72",
-        "bytes": 1245124781
+        "source_sha": "120aeb018d6702d9",
+        "bytes": 1245006280
     },
     "lce_forward": {
-        "source_sha": "910ab9952babd6d2",
-        "bytes": 15154197279
+        "source_sha": "bb8c98d7ddae9d41",
+        "bytes": 15153683711
+    },
+    "kl_forward": {
+        "source_sha": "caaaf15903e43c73",
+        "bytes": 622516558
+    },
+    "kl_vjp": {
+        "source_sha": "caaaf15903e43c73",
+        "bytes": 933640781
     },
 }
 
 
 def source_sha(kernel):
-    """sha256 (first 16 hex digits) of the kernel's source file and the device header it
-    includes."""
+    """sha256 (first 16 hex digits) of the kernel's source file and the two headers it
+    includes (device helpers; launch plans and shared constants)."""
     fname = ("lce_kernels.hip" if kernel.startswith("lce") else
              "kl_kernels.hip" if kernel.startswith("kl") else "ce_kernels.hip")
     h = hashlib.sha256()
-    for f in (fname, "device_common.h"):
+    for f in (fname, "device_common.h", "launch.h"):
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
