@@ -12,12 +12,14 @@ It writes out the plain definitions in float64 NumPy:
   softmax cross-entropy.
 * ``oracle.lce``: the linear cross-entropy forward and its gradients dH, dW.  It
   materialises the logits H.W^T in float64 row blocks and applies ``oracle.ce``.
+* ``oracle.ce_options``: label smoothing, probability targets, ignore_index and
+  the sum / mean reductions of the cross-entropy, with their gradients.
 * ``oracle.kl``: the row-wise KL divergence of a teacher row from a student row
   and its gradient with respect to the student logits.
 
-Every function is pinned by ``tests/test_oracle.py`` against values the pages
+Every function is pinned by ``tests/test_oracle*.py`` against values the pages
 print, closed forms, invariants and brute force.  No function here is
 "parity unpinned".
 """
 
-from . import ce, kl, lce  # noqa: F401
+from . import ce, ce_options, kl, lce  # noqa: F401
