@@ -1,7 +1,7 @@
 /*
  * ce_mi355x.h: C ABI of the MI355X (gfx950) fused softmax cross-entropy library.
  *
- * Six operations, computed by hand-written HIP kernels in libce_mi355x.so:
+ * The operations, computed by hand-written HIP kernels in libce_mi355x.so:
  *
  *   ce_forward    per-row loss and log-sum-exp of a [rows, V] logits view
  *   ce_vjp        dlogits = g_i * (softmax(z_i) - onehot(y_i)) from the saved log-sum-exp
@@ -12,6 +12,9 @@
  *                 regenerated gradient chunk run on rocBLAS
  *   kl_forward    per-row KL divergence of a teacher logits row from a student row
  *   kl_vjp        dq = g_i * (softmax(q_i) - softmax(p_i)) from the saved pairs
+ *   ce_forward_ex / ce_vjp_ex        ce_forward / ce_vjp with label smoothing,
+ *                                    ignore_index and an in-library sum or mean
+ *   ce_forward_probs / ce_vjp_probs  the same with probability targets
  *
  * Conventions shared by every call
  * --------------------------------
@@ -33,9 +36,10 @@
  *   skips rows when the Metal grid gets too large", Issue: a 32-bit grid of
  *   rows x threads-per-row silently dropped rows past 2^32 threads.)
  * - Targets are contiguous int32 [n_rows].  A target outside [0, V) never causes an
- *   out-of-bounds read: that row's loss, and its dlogits row, are written as NaN.
- *   There is no ignore_index.
- * - Only per-row outputs are produced; a mean or sum over rows is the caller's.
+ *   out-of-bounds read: that row's loss, and its dlogits row, are written as NaN
+ *   (unless it is the ignore_index of a ce_forward_ex / ce_vjp_ex call).
+ * - ce_forward and ce_vjp produce per-row outputs only; the _ex and _probs calls can
+ *   also reduce the losses to their sum or mean on the device.
  */
 #ifndef CE_MI355X_H
 #define CE_MI355X_H
@@ -87,7 +91,8 @@ typedef enum {
     CE_ERR_WORKSPACE = -5, /* lce workspace NULL or smaller than the *_workspace_size()    */
     CE_ERR_LAUNCH = -6,    /* the HIP runtime rejected a kernel launch                     */
     CE_ERR_ALIAS = -7,     /* an output overlaps an input it may not overlap               */
-    CE_ERR_DEVICE = -8     /* no usable HIP device, or the device is not gfx950            */
+    CE_ERR_DEVICE = -8,    /* no usable HIP device, or the device is not gfx950            */
+    CE_ERR_OPTION = -9     /* a ce_options field out of range (see ce_options)             */
 } ce_status;
 
 /*
@@ -274,6 +279,100 @@ ce_status kl_vjp(const void* q, ce_layout q_layout, const void* p, ce_layout p_l
 ce_status kl_vjp_lanes(const void* q, ce_layout q_layout, const void* p, ce_layout p_layout, ce_dtype dt,
                        const float* lse_q, const float* lse_p, const float* g, int64_t n_rows, int64_t V,
                        void* dq, ce_layout dq_layout, int32_t lanes_per_row, hipStream_t stream);
+
+/*
+ * ---- Cross-entropy options --------------------------------------------------------
+ *
+ * Source: MLX PR #4188 "Shift by the max in cross_entropy", Proposed changes: the
+ * cross-entropy takes class-index or probability targets, a label smoothing whose
+ * term subtracts the mean logit, and the reductions 'none', 'sum' and 'mean', all
+ * checked against PyTorch; the max shift serves every one of these paths.  With target
+ * weights w_j the loss of a row is -sum_j w_j log p_j, where
+ *     class index y:   w = (1 - eps) onehot(y) + eps / V
+ *     probabilities t: w = (1 - eps) t + eps / V,
+ * and the gradient of sum_i g_i loss_i is g_i (W_i p_ij - w_ij), W_i = sum_j w_ij.
+ * A zero weight contributes nothing even where p_j = 0 (0 log 0 = 0).
+ */
+typedef enum { CE_REDUCE_NONE = 0, CE_REDUCE_SUM = 1, CE_REDUCE_MEAN = 2 } ce_reduction;
+
+/* ignore_index value that ignores nothing. */
+#define CE_NO_IGNORE ((int32_t)INT32_MIN)
+
+/*
+ * label_smoothing  eps in [0, 1].
+ * ignore_index     class-index targets only: a row whose target equals it has loss 0
+ *                  and gradient 0 and does not count towards a mean (PyTorch's
+ *                  convention).  Any value may be given, also one inside [0, V).  Must be
+ *                  CE_NO_IGNORE for probability targets.
+ * reduction        a ce_reduction.  'sum' adds the losses of the rows that count,
+ *                  'mean' divides that sum by their number (NaN when none counts).
+ * Anything else returns CE_ERR_OPTION.
+ */
+typedef struct {
+    float label_smoothing;
+    int32_t ignore_index;
+    int32_t reduction;
+} ce_options;
+
+/* Bytes of device workspace a CE_REDUCE_SUM or CE_REDUCE_MEAN forward needs (a constant). */
+size_t ce_reduce_workspace_size(void);
+
+/*
+ * ce_forward_ex: ce_forward with options.
+ *
+ *   logits, in, dt, targets, n_rows, V, loss, lse  as in ce_forward.  loss holds the
+ *           per-row losses whatever the reduction (0 on ignored rows); lse is the pair
+ *           (m, log s) of every row.
+ *   total   float32 [1]: the sum or mean (written; may be NULL with CE_REDUCE_NONE).
+ *   count   int64 [1]: the number of rows that count (written; may be NULL with
+ *           CE_REDUCE_NONE).  ce_vjp_ex reads it for a mean.
+ *   workspace, workspace_bytes  device scratch of at least ce_reduce_workspace_size()
+ *           bytes, 8-byte aligned, for a sum or mean (may be NULL otherwise).
+ * The sum is formed in float64 over a fixed split of the rows that depends on n_rows
+ * alone, so results are bitwise reproducible.  With n_rows == 0 and a reduction, total
+ * is 0 (sum) or NaN (mean) and count is 0.  Outputs, the workspace included, must not
+ * overlap the inputs or each other (CE_ERR_ALIAS).
+ */
+ce_status ce_forward_ex(const void* logits, ce_layout in, ce_dtype dt, const int32_t* targets, int64_t n_rows,
+                        int64_t V, ce_options opt, float* loss, float* lse, float* total, int64_t* count,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * ce_vjp_ex: dlogits_ij = g_i ((1 - eps) (p_ij - [j == y_i]) + eps (p_ij - 1 / V)), the
+ * gradient of ce_forward_ex's loss, from the saved lse.
+ *
+ *   g       float32: [n_rows] per-row upstream gradients for CE_REDUCE_NONE; [1], the
+ *           gradient of the total, for a sum or mean.
+ *   count   int64 [1] as ce_forward_ex wrote it; read for CE_REDUCE_MEAN (g / count per
+ *           row), otherwise may be NULL.
+ *   The rest as in ce_vjp.  Ignored rows get dlogits 0.
+ */
+ce_status ce_vjp_ex(const void* logits, ce_layout in, ce_dtype dt, const int32_t* targets, const float* lse,
+                    const float* g, int64_t n_rows, int64_t V, ce_options opt, const int64_t* count, void* dlogits,
+                    ce_layout out, hipStream_t stream);
+
+/*
+ * ce_forward_probs: loss_i = -sum_j w_ij log p_ij with probability targets.
+ *
+ *   probs        [n_rows rows of V] of dtype `dt` (the logits' type), read through
+ *                `probs_layout` (a ce_layout like `in`).  Rows need not sum to 1.
+ *   wsum         float32 [n_rows] (written): W_i = sum_j w_ij, which ce_vjp_probs needs.
+ *   The rest as in ce_forward_ex; opt.ignore_index must be CE_NO_IGNORE, and a mean
+ *   divides by n_rows.
+ */
+ce_status ce_forward_probs(const void* logits, ce_layout in, ce_dtype dt, const void* probs, ce_layout probs_layout,
+                           int64_t n_rows, int64_t V, ce_options opt, float* loss, float* lse, float* wsum,
+                           float* total, int64_t* count, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/*
+ * ce_vjp_probs: dlogits_ij = g_i (W_i p_ij - w_ij), from ce_forward_probs's lse and wsum.
+ * g and count as in ce_vjp_ex; dlogits as in ce_vjp (it may be the logits, in place,
+ * and must not overlap probs).
+ */
+ce_status ce_vjp_probs(const void* logits, ce_layout in, ce_dtype dt, const void* probs, ce_layout probs_layout,
+                       const float* lse, const float* wsum, const float* g, int64_t n_rows, int64_t V, ce_options opt,
+                       const int64_t* count, void* dlogits, ce_layout out, hipStream_t stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* ce_status_string(ce_status status);

@@ -22,18 +22,31 @@ DTYPE_CODE = {torch.float32: CE_F32, torch.float16: CE_F16, torch.bfloat16: CE_B
 
 STATUS = {
     0: "CE_OK", -1: "CE_ERR_NULL", -2: "CE_ERR_SHAPE", -3: "CE_ERR_DTYPE", -4: "CE_ERR_LAYOUT",
-    -5: "CE_ERR_WORKSPACE", -6: "CE_ERR_LAUNCH", -7: "CE_ERR_ALIAS", -8: "CE_ERR_DEVICE",
+    -5: "CE_ERR_WORKSPACE", -6: "CE_ERR_LAUNCH", -7: "CE_ERR_ALIAS", -8: "CE_ERR_DEVICE", -9: "CE_ERR_OPTION",
 }
+
+CE_REDUCE = {"none": 0, "sum": 1, "mean": 2}
+CE_NO_IGNORE = -(2 ** 31)
 
 # every symbol include/ce_mi355x.h declares
 EXPORTS = ("ce_forward", "ce_forward_lanes", "ce_vjp", "ce_vjp_lanes", "lce_workspace_size",
            "lce_forward", "lce_backward_workspace_size", "lce_backward", "kl_forward", "kl_forward_lanes",
-           "kl_vjp", "kl_vjp_lanes", "ce_status_string")
+           "kl_vjp", "kl_vjp_lanes", "ce_reduce_workspace_size", "ce_forward_ex", "ce_vjp_ex", "ce_forward_probs",
+           "ce_vjp_probs", "ce_status_string")
 
 
 class CELayout(ctypes.Structure):
     _fields_ = [("rows_per_batch", ctypes.c_int64), ("row_stride", ctypes.c_int64),
                 ("batch_stride", ctypes.c_int64)]
+
+
+class CEOptions(ctypes.Structure):
+    _fields_ = [("label_smoothing", ctypes.c_float), ("ignore_index", ctypes.c_int32), ("reduction", ctypes.c_int32)]
+
+
+def options(label_smoothing: float = 0.0, ignore_index=None, reduction: str = "none") -> CEOptions:
+    return CEOptions(float(label_smoothing), CE_NO_IGNORE if ignore_index is None else int(ignore_index),
+                     CE_REDUCE[reduction] if isinstance(reduction, str) else int(reduction))
 
 
 class CEError(RuntimeError):
@@ -72,10 +85,21 @@ def lib() -> ctypes.CDLL:
                              CELayout, _vp]
         L.kl_vjp_lanes.argtypes = [_vp, CELayout, _vp, CELayout, ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _vp,
                                    CELayout, _i32, _vp]
+        L.ce_reduce_workspace_size.argtypes = []
+        L.ce_reduce_workspace_size.restype = _sz
+        L.ce_forward_ex.argtypes = [_vp, CELayout, ctypes.c_int, _vp, _i64, _i64, CEOptions, _vp, _vp, _vp, _vp, _vp,
+                                    _sz, _vp]
+        L.ce_vjp_ex.argtypes = [_vp, CELayout, ctypes.c_int, _vp, _vp, _vp, _i64, _i64, CEOptions, _vp, _vp, CELayout,
+                                _vp]
+        L.ce_forward_probs.argtypes = [_vp, CELayout, ctypes.c_int, _vp, CELayout, _i64, _i64, CEOptions, _vp, _vp,
+                                       _vp, _vp, _vp, _vp, _sz, _vp]
+        L.ce_vjp_probs.argtypes = [_vp, CELayout, ctypes.c_int, _vp, CELayout, _vp, _vp, _vp, _i64, _i64, CEOptions,
+                                   _vp, _vp, CELayout, _vp]
         L.ce_status_string.argtypes = [ctypes.c_int]
         L.ce_status_string.restype = ctypes.c_char_p
         for name in ("ce_forward", "ce_forward_lanes", "ce_vjp", "ce_vjp_lanes", "lce_forward", "lce_backward",
-                     "kl_forward", "kl_forward_lanes", "kl_vjp", "kl_vjp_lanes"):
+                     "kl_forward", "kl_forward_lanes", "kl_vjp", "kl_vjp_lanes", "ce_forward_ex", "ce_vjp_ex",
+                     "ce_forward_probs", "ce_vjp_probs"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -159,6 +183,118 @@ def ce_vjp(logits: torch.Tensor, targets: torch.Tensor, lse: torch.Tensor, g: to
     else:
         st = lib().ce_vjp_lanes(*args, int(lanes_per_row), _stream(logits))
     _check(st, "ce_vjp")
+    return dlogits
+
+
+def ce_reduce_workspace_size() -> int:
+    return int(lib().ce_reduce_workspace_size())
+
+
+def _rows_view(t: torch.Tensor, name: str):
+    if t.stride(-1) != 1 and t.shape[-1] > 1:
+        raise ValueError(f"{name} needs unit column stride")
+    return rows_layout(t)
+
+
+def _reduce_outputs(dev, reduction, total, count, workspace):
+    if reduction == "none":
+        return total, count, workspace
+    if total is None:
+        total = torch.empty(1, dtype=torch.float32, device=dev)
+    if count is None:
+        count = torch.empty(1, dtype=torch.int64, device=dev)
+    if workspace is None:
+        workspace = torch.empty(ce_reduce_workspace_size(), dtype=torch.uint8, device=dev)
+    _need(total, torch.float32, 1, "total")
+    _need(count, torch.int64, 1, "count")
+    return total, count, workspace
+
+
+def _upstream(g, n, reduction):
+    _need(g, torch.float32, n if reduction == "none" else 1, "g")
+
+
+def ce_forward_ex(logits: torch.Tensor, targets: torch.Tensor, label_smoothing: float = 0.0, ignore_index=None,
+                  reduction: str = "none", loss=None, lse=None, total=None, count=None, workspace=None):
+    """(loss [n], lse [n, 2], total [1] or None, count [1] or None) with the cross-entropy options."""
+    lay, n, V = _rows_view(logits, "logits")
+    _need(targets, torch.int32, n, "targets")
+    dev = logits.device
+    loss = torch.empty(n, dtype=torch.float32, device=dev) if loss is None else loss
+    lse = torch.empty(n, 2, dtype=torch.float32, device=dev) if lse is None else lse
+    _need(loss, torch.float32, n, "loss")
+    _need(lse, torch.float32, 2 * n, "lse")
+    total, count, workspace = _reduce_outputs(dev, reduction, total, count, workspace)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().ce_forward_ex(_ptr(logits), lay, DTYPE_CODE[logits.dtype], _ptr(targets), n, V,
+                             options(label_smoothing, ignore_index, reduction), _ptr(loss), _ptr(lse), _ptr(total),
+                             _ptr(count), _ptr(workspace), ws_bytes, _stream(logits))
+    _check(st, "ce_forward_ex")
+    return loss, lse, total, count
+
+
+def ce_vjp_ex(logits: torch.Tensor, targets: torch.Tensor, lse: torch.Tensor, g: torch.Tensor,
+              label_smoothing: float = 0.0, ignore_index=None, reduction: str = "none", count=None, dlogits=None):
+    """Gradient of ce_forward_ex's loss: g per row ('none') or g [1] of the total."""
+    lay, n, V = _rows_view(logits, "logits")
+    _need(targets, torch.int32, n, "targets")
+    _need(lse, torch.float32, 2 * n, "lse")
+    _upstream(g, n, reduction)
+    if dlogits is None:
+        dlogits = torch.empty(logits.shape, dtype=logits.dtype, device=logits.device)
+    if dlogits.dtype != logits.dtype or dlogits.shape != logits.shape:
+        raise ValueError("dlogits must match logits in dtype and shape")
+    olay, _, _ = _rows_view(dlogits, "dlogits")
+    st = lib().ce_vjp_ex(_ptr(logits), lay, DTYPE_CODE[logits.dtype], _ptr(targets), _ptr(lse), _ptr(g), n, V,
+                         options(label_smoothing, ignore_index, reduction), _ptr(count), _ptr(dlogits), olay,
+                         _stream(logits))
+    _check(st, "ce_vjp_ex")
+    return dlogits
+
+
+def ce_forward_probs(logits: torch.Tensor, probs: torch.Tensor, label_smoothing: float = 0.0,
+                     reduction: str = "none", loss=None, lse=None, wsum=None, total=None, count=None,
+                     workspace=None):
+    """(loss [n], lse [n, 2], wsum [n], total, count) with probability targets of the logits' dtype."""
+    lay, n, V = _rows_view(logits, "logits")
+    if probs.dtype != logits.dtype or probs.shape != logits.shape:
+        raise ValueError("probs must match logits in dtype and shape")
+    play, _, _ = _rows_view(probs, "probs")
+    dev = logits.device
+    loss = torch.empty(n, dtype=torch.float32, device=dev) if loss is None else loss
+    lse = torch.empty(n, 2, dtype=torch.float32, device=dev) if lse is None else lse
+    wsum = torch.empty(n, dtype=torch.float32, device=dev) if wsum is None else wsum
+    _need(loss, torch.float32, n, "loss")
+    _need(lse, torch.float32, 2 * n, "lse")
+    _need(wsum, torch.float32, n, "wsum")
+    total, count, workspace = _reduce_outputs(dev, reduction, total, count, workspace)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().ce_forward_probs(_ptr(logits), lay, DTYPE_CODE[logits.dtype], _ptr(probs), play, n, V,
+                                options(label_smoothing, None, reduction), _ptr(loss), _ptr(lse), _ptr(wsum),
+                                _ptr(total), _ptr(count), _ptr(workspace), ws_bytes, _stream(logits))
+    _check(st, "ce_forward_probs")
+    return loss, lse, wsum, total, count
+
+
+def ce_vjp_probs(logits: torch.Tensor, probs: torch.Tensor, lse: torch.Tensor, wsum: torch.Tensor, g: torch.Tensor,
+                 label_smoothing: float = 0.0, reduction: str = "none", count=None, dlogits=None):
+    """Gradient of ce_forward_probs's loss: g (W p - w)."""
+    lay, n, V = _rows_view(logits, "logits")
+    if probs.dtype != logits.dtype or probs.shape != logits.shape:
+        raise ValueError("probs must match logits in dtype and shape")
+    play, _, _ = _rows_view(probs, "probs")
+    _need(lse, torch.float32, 2 * n, "lse")
+    _need(wsum, torch.float32, n, "wsum")
+    _upstream(g, n, reduction)
+    if dlogits is None:
+        dlogits = torch.empty(logits.shape, dtype=logits.dtype, device=logits.device)
+    if dlogits.dtype != logits.dtype or dlogits.shape != logits.shape:
+        raise ValueError("dlogits must match logits in dtype and shape")
+    olay, _, _ = _rows_view(dlogits, "dlogits")
+    st = lib().ce_vjp_probs(_ptr(logits), lay, DTYPE_CODE[logits.dtype], _ptr(probs), play, _ptr(lse), _ptr(wsum),
+                            _ptr(g), n, V, options(label_smoothing, None, reduction), _ptr(count), _ptr(dlogits),
+                            olay, _stream(logits))
+    _check(st, "ce_vjp_probs")
     return dlogits
 
 

@@ -239,6 +239,128 @@ ce_status vjp_impl(const void* logits, ce_layout in, ce_dtype dt, const int32_t*
     return from_hip(ce::launch_ce_vjp(c));
 }
 
+// ---- cross-entropy options ------------------------------------------------------
+
+bool options_ok(const ce_options& o, bool probs) {
+    // NaN fails both comparisons
+    if (!(o.label_smoothing >= 0.0f && o.label_smoothing <= 1.0f)) return false;
+    if (o.reduction != CE_REDUCE_NONE && o.reduction != CE_REDUCE_SUM && o.reduction != CE_REDUCE_MEAN)
+        return false;
+    return !probs || o.ignore_index == CE_NO_IGNORE;
+}
+
+// True when some output range overlaps an input range or another output range.
+bool alias_any(const Extent* outs, int n_out, const Extent* ins, int n_in) {
+    for (int i = 0; i < n_out; ++i) {
+        for (int j = 0; j < n_in; ++j)
+            if (overlaps(outs[i], ins[j])) return true;
+        for (int j = i + 1; j < n_out; ++j)
+            if (overlaps(outs[i], outs[j])) return true;
+    }
+    return false;
+}
+
+// The two option forwards: class-index targets (use_probs false, `targets`) or
+// probability targets (use_probs true, the `probs` view).
+ce_status options_forward(const void* logits, ce_layout in, ce_dtype dt, const int32_t* targets, bool use_probs,
+                          const void* probs, ce_layout pl, int64_t n_rows, int64_t V, ce_options opt, float* loss, float* lse,
+                          float* wsum, float* total, int64_t* count, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+    if (!valid_dtype((int)dt)) return CE_ERR_DTYPE;
+    if (n_rows < 0 || V < 1 || V > kMaxV) return CE_ERR_SHAPE;
+    if (!options_ok(opt, use_probs)) return CE_ERR_OPTION;
+    const bool reduce = opt.reduction != CE_REDUCE_NONE;
+    const bool has_ignore = !use_probs && opt.ignore_index != CE_NO_IGNORE;
+    if (reduce) {
+        if (!total || !count || !workspace) return CE_ERR_NULL;
+        if (workspace_bytes < ce::kReduceWorkspaceBytes) return CE_ERR_WORKSPACE;
+        if (!aligned(total, 4) || !aligned(count, 8) || !aligned(workspace, 8)) return CE_ERR_LAYOUT;
+    }
+    const Extent ex_tot = flat_extent(total, reduce ? 4 : 0);
+    const Extent ex_cnt = flat_extent(count, reduce ? 8 : 0);
+    const Extent ex_ws = flat_extent(workspace, reduce ? (int64_t)ce::kReduceWorkspaceBytes : 0);
+    if (n_rows == 0) {
+        if (!reduce) return CE_OK;
+        const Extent outs[3] = {ex_tot, ex_cnt, ex_ws};
+        if (alias_any(outs, 3, nullptr, 0)) return CE_ERR_ALIAS;
+        int cus = 0;
+        if (ce_status s = device_cus(&cus)) return s;
+        ce::ReduceCall rc{nullptr, nullptr, 0, opt.ignore_index, false, opt.reduction, total, count, workspace, stream};
+        return from_hip(ce::launch_loss_reduce(rc));
+    }
+    if (!logits || !loss || !lse) return CE_ERR_NULL;
+    if (use_probs ? (!probs || !wsum) : !targets) return CE_ERR_NULL;
+    const int es = esize(dt);
+    if (!layout_ok(in, n_rows, V, false) || !aligned(logits, es) || !aligned(loss, 4) || !aligned(lse, 8))
+        return CE_ERR_LAYOUT;
+    if (use_probs ? (!layout_ok(pl, n_rows, V, false) || !aligned(probs, es) || !aligned(wsum, 4))
+                  : !aligned(targets, 4))
+        return CE_ERR_LAYOUT;
+    const Extent ins[2] = {view_extent(logits, in, n_rows, V, es),
+                           use_probs ? view_extent(probs, pl, n_rows, V, es) : flat_extent(targets, n_rows * 4)};
+    const Extent outs[6] = {flat_extent(loss, n_rows * 4), flat_extent(lse, n_rows * 8),
+                            flat_extent(wsum, use_probs ? n_rows * 4 : 0), ex_tot, ex_cnt, ex_ws};
+    if (alias_any(outs, 6, ins, 2)) return CE_ERR_ALIAS;
+    int cus = 0;
+    if (ce_status s = device_cus(&cus)) return s;
+    if (!use_probs && opt.label_smoothing == 0.0f) {
+        if (ce_status s = forward_impl(logits, in, dt, targets, n_rows, V, loss, lse, 0, stream)) return s;
+    } else {
+        Plan plan;
+        if (ce_status s = make_plan(false, V, es, n_rows, 0, false, cus, &plan)) return s;
+        ce::OptFwdCall c{logits, host_layout(in, n_rows), use_probs ? probs : nullptr,
+                         host_layout(use_probs ? pl : in, n_rows), (Dt)dt, targets, n_rows, V, opt.label_smoothing,
+                         loss, lse, wsum, plan, stream};
+        if (hipError_t e = ce::launch_opt_forward(c)) return from_hip(e);
+    }
+    if (!reduce && !has_ignore) return CE_OK;
+    ce::ReduceCall rc{loss, use_probs ? nullptr : targets, n_rows, opt.ignore_index, has_ignore, opt.reduction,
+                      total, count, workspace, stream};
+    return from_hip(ce::launch_loss_reduce(rc));
+}
+
+ce_status options_vjp(const void* logits, ce_layout in, ce_dtype dt, const int32_t* targets, bool use_probs,
+                      const void* probs, ce_layout pl, const float* lse, const float* wsum, const float* g, int64_t n_rows, int64_t V,
+                      ce_options opt, const int64_t* count, void* dlogits, ce_layout out, hipStream_t stream) {
+    if (!valid_dtype((int)dt)) return CE_ERR_DTYPE;
+    if (n_rows < 0 || V < 1 || V > kMaxV) return CE_ERR_SHAPE;
+    if (!options_ok(opt, use_probs)) return CE_ERR_OPTION;
+    if (n_rows == 0) return CE_OK;
+    const bool has_ignore = !use_probs && opt.ignore_index != CE_NO_IGNORE;
+    if (!use_probs && opt.label_smoothing == 0.0f && !has_ignore && opt.reduction == CE_REDUCE_NONE)
+        return vjp_impl(logits, in, dt, targets, lse, g, n_rows, V, dlogits, out, 0, stream);
+    if (!logits || !lse || !g || !dlogits) return CE_ERR_NULL;
+    if (use_probs ? (!probs || !wsum) : !targets) return CE_ERR_NULL;
+    if (opt.reduction == CE_REDUCE_MEAN && !count) return CE_ERR_NULL;
+    const int es = esize(dt);
+    if (!layout_ok(in, n_rows, V, false) || !layout_ok(out, n_rows, V, true) || !aligned(logits, es) ||
+        !aligned(dlogits, es) || !aligned(lse, 8) || !aligned(g, 4) || !aligned(count, 8))
+        return CE_ERR_LAYOUT;
+    if (use_probs ? (!layout_ok(pl, n_rows, V, false) || !aligned(probs, es) || !aligned(wsum, 4))
+                  : !aligned(targets, 4))
+        return CE_ERR_LAYOUT;
+    const Extent ex_in = view_extent(logits, in, n_rows, V, es);
+    const Extent ex_out = view_extent(dlogits, out, n_rows, V, es);
+    const bool in_place = logits == dlogits && same_layout(in, out, n_rows);
+    if (!in_place && overlaps(ex_in, ex_out)) return CE_ERR_ALIAS;
+    const int64_t g_bytes = opt.reduction == CE_REDUCE_NONE ? n_rows * 4 : 4;
+    const Extent ins[5] = {use_probs ? view_extent(probs, pl, n_rows, V, es) : flat_extent(targets, n_rows * 4),
+                           flat_extent(lse, n_rows * 8), flat_extent(g, g_bytes),
+                           flat_extent(wsum, use_probs ? n_rows * 4 : 0),
+                           flat_extent(count, opt.reduction == CE_REDUCE_MEAN ? 8 : 0)};
+    if (alias_any(&ex_out, 1, ins, 5)) return CE_ERR_ALIAS;
+    int cus = 0;
+    if (ce_status s = device_cus(&cus)) return s;
+    Plan plan;
+    if (!chunk_plan(V, es, n_rows, cus, &plan))
+        if (ce_status s = make_plan(false, V, es, n_rows, 0, true, cus, &plan)) return s;
+    ce::OptVjpCall c{logits, host_layout(in, n_rows), use_probs ? probs : nullptr,
+                     host_layout(use_probs ? pl : in, n_rows), (Dt)dt, targets,
+                     lse, wsum, g, count, n_rows, V, opt.reduction, opt.ignore_index, has_ignore ? 1 : 0,
+                     opt.label_smoothing, dlogits, host_layout(out, n_rows), plan, stream};
+    return from_hip(ce::launch_opt_vjp(c));
+}
+
 bool lanes_ok_kl(int32_t lanes) {
     return lanes == 0 || (lanes >= 1 && lanes <= 1024 && (lanes & (lanes - 1)) == 0);
 }
@@ -412,6 +534,37 @@ ce_status kl_vjp_lanes(const void* q, ce_layout q_layout, const void* p, ce_layo
                        stream);
 }
 
+size_t ce_reduce_workspace_size(void) { return ce::kReduceWorkspaceBytes; }
+
+ce_status ce_forward_ex(const void* logits, ce_layout in, ce_dtype dt, const int32_t* targets, int64_t n_rows,
+                        int64_t V, ce_options opt, float* loss, float* lse, float* total, int64_t* count,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return options_forward(logits, in, dt, targets, false, nullptr, in, n_rows, V, opt, loss, lse, nullptr, total,
+                           count, workspace, workspace_bytes, stream);
+}
+
+ce_status ce_vjp_ex(const void* logits, ce_layout in, ce_dtype dt, const int32_t* targets, const float* lse,
+                    const float* g, int64_t n_rows, int64_t V, ce_options opt, const int64_t* count, void* dlogits,
+                    ce_layout out, hipStream_t stream) {
+    return options_vjp(logits, in, dt, targets, false, nullptr, in, lse, nullptr, g, n_rows, V, opt, count, dlogits,
+                       out, stream);
+}
+
+ce_status ce_forward_probs(const void* logits, ce_layout in, ce_dtype dt, const void* probs, ce_layout probs_layout,
+                           int64_t n_rows, int64_t V, ce_options opt, float* loss, float* lse, float* wsum,
+                           float* total, int64_t* count, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+    return options_forward(logits, in, dt, nullptr, true, probs, probs_layout, n_rows, V, opt, loss, lse, wsum, total,
+                           count, workspace, workspace_bytes, stream);
+}
+
+ce_status ce_vjp_probs(const void* logits, ce_layout in, ce_dtype dt, const void* probs, ce_layout probs_layout,
+                       const float* lse, const float* wsum, const float* g, int64_t n_rows, int64_t V, ce_options opt,
+                       const int64_t* count, void* dlogits, ce_layout out, hipStream_t stream) {
+    return options_vjp(logits, in, dt, nullptr, true, probs, probs_layout, lse, wsum, g, n_rows, V, opt, count,
+                       dlogits, out, stream);
+}
+
 const char* ce_status_string(ce_status s) {
     switch (s) {
         case CE_OK: return "CE_OK: success";
@@ -423,6 +576,7 @@ const char* ce_status_string(ce_status s) {
         case CE_ERR_LAUNCH: return "CE_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
         case CE_ERR_ALIAS: return "CE_ERR_ALIAS: an output overlaps an input";
         case CE_ERR_DEVICE: return "CE_ERR_DEVICE: no gfx950 HIP device is current";
+        case CE_ERR_OPTION: return "CE_ERR_OPTION: label_smoothing outside [0, 1], an unknown reduction, or an ignore_index with probability targets";
     }
     return "unknown ce_status";
 }

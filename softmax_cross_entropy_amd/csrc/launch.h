@@ -94,6 +94,74 @@ struct KLVjpCall {
     hipStream_t stream;
 };
 
+// Cross-entropy options (ce_options.hip).  t != NULL selects probability targets;
+// otherwise y holds class-index targets.
+struct OptFwdCall {
+    const void* z;
+    HostLayout zl;
+    const void* t;
+    HostLayout tl;
+    Dt dt;
+    const int32_t* y;
+    int64_t n_rows;
+    int64_t V;
+    float eps;
+    float* loss;
+    float* lse;
+    float* wsum;
+    Plan plan;
+    hipStream_t stream;
+};
+
+struct OptVjpCall {
+    const void* z;
+    HostLayout zl;
+    const void* t;
+    HostLayout tl;
+    Dt dt;
+    const int32_t* y;
+    const float* lse;
+    const float* wsum;
+    const float* g;
+    const int64_t* count;
+    int64_t n_rows;
+    int64_t V;
+    int32_t reduction;
+    int32_t ignore_index;
+    int32_t has_ignore;
+    float eps;
+    void* d;
+    HostLayout dl;
+    Plan plan;
+    hipStream_t stream;
+};
+
+// Sum / mean of the per-row losses: float64 partial sums over at most kReduceMaxParts
+// blocks of at least kReduceRowsMin rows (a split that depends on n_rows alone), then one
+// fixed-order fold.  The workspace holds the partials: kReduceMaxParts doubles, then as
+// many int64 counts.
+constexpr int64_t kReduceMaxParts = 1024;
+constexpr int64_t kReduceRowsMin = 4096;
+constexpr size_t kReduceWorkspaceBytes = (size_t)kReduceMaxParts * 16;
+
+struct ReduceCall {
+    float* loss;
+    const int32_t* y;  // NULL: every row counts
+    int64_t n_rows;
+    int32_t ignore_index;
+    bool has_ignore;
+    int32_t reduction;  // 0 none (ignore_index fix-up only), 1 sum, 2 mean
+    float* total;
+    int64_t* count;
+    void* workspace;
+    hipStream_t stream;
+};
+
+int64_t reduce_parts(int64_t n_rows);
+hipError_t launch_opt_forward(const OptFwdCall& c);
+hipError_t launch_opt_vjp(const OptVjpCall& c);
+hipError_t launch_loss_reduce(const ReduceCall& c);
+
 hipError_t launch_kl_forward(const KLFwdCall& c);
 hipError_t launch_kl_vjp(const KLVjpCall& c);
 

@@ -92,6 +92,17 @@ def normal_rows(rows: int, V: int, dtype: str, workload: int, stream: int = 0) -
     return CEBatch(encode(x, dtype), y, np.ones(rows, np.float32), dtype)
 
 
+def prob_targets(rows: int, V: int, dtype: str, workload: int, stream: int = 0, normalised_rows: int = None):
+    """[rows, V] probability targets stored in ``dtype``: U[0, 1) entries, the first
+    ``normalised_rows`` rows (default all) divided by their sums, the rest left
+    unnormalised."""
+    g = rng(workload, stream)
+    t = g.uniform(0.0, 1.0, size=(rows, V))
+    k = rows if normalised_rows is None else normalised_rows
+    t[:k] /= t[:k].sum(axis=1, keepdims=True)
+    return encode(t.astype(np.float32), dtype)
+
+
 # --- small-V rows: 1,048,576 x 8 fp32 --------------------------------------
 
 def small_v_rows(rows: int = 1 << 20, V: int = 8) -> CEBatch:

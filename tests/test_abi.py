@@ -16,7 +16,7 @@ from softmax_cross_entropy_amd import abi
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ce_mi355x.h")
 
-OK, NULL, SHAPE, DTYPE, LAYOUT, WORKSPACE, LAUNCH, ALIAS, DEVICE = 0, -1, -2, -3, -4, -5, -6, -7, -8
+OK, NULL, SHAPE, DTYPE, LAYOUT, WORKSPACE, LAUNCH, ALIAS, DEVICE, OPTION = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 
 pytestmark = pytest.mark.skipif(not os.path.exists(abi.LIB_PATH), reason="library not built")
 
@@ -207,6 +207,67 @@ def test_kl_rejects_bad_arguments():
     assert klv(dq=P_LOGITS) in (OK, DEVICE)  # in place, identical layout
 
 
+P_TOT, P_CNT, P_RWS, P_PR, P_WSUM, P_GR = (ctypes.c_void_p(A * k) for k in (400, 401, 402, 410, 420, 421))
+WSB = 1 << 14
+
+
+def opts(eps=0.1, ign=None, red="mean"):
+    return abi.options(eps, ign, red)
+
+
+def fex(logits=P_LOGITS, dt=0, t=P_T, n=16, V=8, o=None, loss=P_LOSS, lse=P_LSE, tot=P_TOT, cnt=P_CNT, ws=P_RWS,
+        wsb=WSB):
+    return abi.lib().ce_forward_ex(logits, lay(n, V), dt, t, n, V, o or opts(), loss, lse, tot, cnt, ws, wsb, None)
+
+
+def vex(logits=P_LOGITS, dt=0, t=P_T, lse=P_LSE, g=P_GR, n=16, V=8, o=None, cnt=P_CNT, d=P_OUT, dl=None):
+    return abi.lib().ce_vjp_ex(logits, lay(n, V), dt, t, lse, g, n, V, o or opts(), cnt, d, dl or lay(n, V), None)
+
+
+def fpr(logits=P_LOGITS, dt=0, pr=P_PR, n=16, V=8, o=None, loss=P_LOSS, lse=P_LSE, ws_=P_WSUM, tot=P_TOT,
+        cnt=P_CNT, ws=P_RWS, wsb=WSB):
+    return abi.lib().ce_forward_probs(logits, lay(n, V), dt, pr, lay(n, V), n, V, o or opts(), loss, lse, ws_, tot,
+                                      cnt, ws, wsb, None)
+
+
+def vpr(logits=P_LOGITS, dt=0, pr=P_PR, lse=P_LSE, ws_=P_WSUM, g=P_GR, n=16, V=8, o=None, cnt=P_CNT, d=P_OUT):
+    return abi.lib().ce_vjp_probs(logits, lay(n, V), dt, pr, lay(n, V), lse, ws_, g, n, V, o or opts(), cnt, d,
+                                  lay(n, V), None)
+
+
+def test_reduce_workspace_size():
+    assert abi.ce_reduce_workspace_size() == WSB
+
+
+def test_options_reject_bad_arguments():
+    for f in (fex, vex, fpr, vpr):
+        assert f(o=opts(eps=-0.01)) == OPTION and f(o=opts(eps=1.5)) == OPTION
+        assert f(o=opts(eps=float("nan"))) == OPTION and f(o=abi.options(0.1, None, 3)) == OPTION
+        assert f(dt=5) == DTYPE and f(V=0) == SHAPE and f(n=-1) == SHAPE
+    # ignore_index has no meaning for probability targets
+    assert fpr(o=opts(ign=-100)) == OPTION and vpr(o=opts(ign=-100)) == OPTION
+    # a reduction needs its outputs and the workspace
+    assert fex(tot=None) == NULL and fex(cnt=None) == NULL and fex(ws=None) == NULL
+    assert fex(wsb=WSB - 1) == WORKSPACE
+    assert fex(cnt=ctypes.c_void_p(400 * A + 4)) == LAYOUT
+    assert fex(o=opts(red="none"), tot=None, cnt=None, ws=None, wsb=0) in (OK, DEVICE)
+    for name in ("logits", "t", "loss", "lse"):
+        assert fex(**{name: None}) == NULL, name
+    assert fpr(pr=None) == NULL and fpr(ws_=None) == NULL
+    assert vex(cnt=None) == NULL and vex(o=opts(red="sum"), cnt=None) in (OK, DEVICE)
+    assert vpr(ws_=None) == NULL and vpr(pr=None) == NULL
+    # aliasing among the outputs and with the inputs
+    assert fex(tot=P_LOSS) == ALIAS and fex(ws=ctypes.c_void_p(A + 8)) == ALIAS and fex(cnt=P_RWS) == ALIAS
+    assert fpr(ws_=P_PR) == ALIAS and fpr(loss=P_WSUM) == ALIAS
+    assert vex(d=P_GR) == ALIAS and vex(d=P_CNT) == ALIAS and vpr(d=P_PR) == ALIAS and vpr(d=P_WSUM) == ALIAS
+    assert vex(d=P_LOGITS) in (OK, DEVICE)  # in place
+    # an empty batch with a reduction still writes total and count; without one it is a no-op
+    assert fex(n=0, logits=None, t=None, loss=None, lse=None) in (OK, DEVICE)
+    assert fex(n=0, tot=P_RWS) == ALIAS
+    assert fex(n=0, logits=None, o=opts(red="none"), tot=None, cnt=None, ws=None) == OK
+    assert vex(n=0, logits=None, d=None) == OK and vpr(n=0, pr=None, d=None) == OK
+
+
 @pytest.mark.skipif(os.environ.get("HIP_VISIBLE_DEVICES", None) is not None or os.path.exists("/dev/kfd"),
                     reason="only meaningful without a GPU")
 def test_valid_call_without_device_reports_device_error():
@@ -217,3 +278,5 @@ def test_valid_call_without_device_reports_device_error():
     assert lbw(H=None, t=None, lse=None, g=None, dH=None, ws=None, N=0, wsb=0) == DEVICE
     assert klf() == DEVICE
     assert klv() == DEVICE
+    assert fex() == DEVICE and vex() == DEVICE and fpr() == DEVICE and vpr() == DEVICE
+    assert fex(n=0, logits=None, t=None, loss=None, lse=None) == DEVICE
