@@ -75,7 +75,8 @@ def source_sha(kernel):
     """sha256 (first 16 hex digits) of the kernel's source file and the two headers it
     includes (device helpers; launch plans and shared constants)."""
     fname = ("lce_kernels.hip" if kernel.startswith("lce") else
-             "kl_kernels.hip" if kernel.startswith("kl") else "ce_kernels.hip")
+             "kl_kernels.hip" if kernel.startswith("kl") else
+             "ce_options.hip" if kernel.endswith(("_ex", "_probs")) else "ce_kernels.hip")
     h = hashlib.sha256()
     for f in (fname, "device_common.h", "launch.h"):
         with open(os.path.join(CSRC, f), "rb") as fh:
@@ -104,6 +105,21 @@ def kl_bytes(rows, V, e):
     and the two (m, log s) pairs (16); the VJP reads both rows, the pairs and g (20)
     and writes the student gradient."""
     return rows * (2 * V * e + 20), rows * (3 * V * e + 20)
+
+
+def opt_bytes(rows, V, e):
+    """Algorithmic HBM bytes per call of the index-target options (smoothing, ignore_index,
+    mean): the forward reads the logits and the target and writes loss and lse (16 per
+    row); the VJP reads the logits, lse and target (12) and writes the gradient.  The
+    reduction's second read of loss and targets is not counted."""
+    return rows * (V * e + 16), rows * (2 * V * e + 12)
+
+
+def probs_bytes(rows, V, e):
+    """Probability targets: the forward reads logits and targets and writes loss, lse and
+    the weight sum (16 per row); the VJP reads both rows, lse and the weight sum (12) and
+    writes the gradient."""
+    return rows * (2 * V * e + 16), rows * (3 * V * e + 12)
 
 
 def lce_flops(N, D, V):
@@ -145,6 +161,15 @@ def cpu_baseline(ce_batch, lce_inputs, lce_rows=32):
     okl.grad(zq, zp, kg)
     kl_s = time.perf_counter() - t0
     kf_b, kv_b = kl_bytes(32, KL_V, 4)
+    from oracle import ce_options as oco
+    y_ign = b.targets[:32].copy()
+    y_ign[::16] = -100
+    z = oce.decode(b.logits[:32], "bf16")
+    t0 = time.perf_counter()
+    oco.forward_index(z, y_ign, 0.1, -100, "mean")
+    oco.grad_index(z, y_ign, 1.0, 0.1, -100, "mean")
+    opt_s = time.perf_counter() - t0
+    of_b, ov_b = opt_bytes(32, b.V, 2)
     blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     return {
         "value": (fwd_b + vjp_b) / ce_s / 1e9,
@@ -157,6 +182,9 @@ def cpu_baseline(ce_batch, lce_inputs, lce_rows=32):
                 "cores": blas, "seconds": lce_s,
                 "sample": f"lce oracle (float64 BLAS matmul + CE) on {lce_rows} of {LCE_N} rows, "
                           f"all {LCE_V} columns"},
+        "ce_options": {"value": (of_b + ov_b) / opt_s / 1e9, "unit": "GB/s", "cores": 1, "seconds": opt_s,
+                       "sample": f"options oracle (eps 0.1, ignore_index, mean; float64 NumPy) on 32 of "
+                                 f"{b.rows} rows, all {b.V} columns"},
         "kl": {"value": (kf_b + kv_b) / kl_s / 1e9, "unit": "GB/s", "cores": 1, "seconds": kl_s,
                "sample": f"KL fwd+grad oracle (float64 NumPy) on 32 of {KL_ROWS} rows, all {KL_V} columns"},
         "lce_backward": {"value": 3 * lce_flops(lce_rows, LCE_D, LCE_V) / lbw_s / 1e12, "unit": "TFLOP/s",
@@ -173,8 +201,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--parts", default="ce,lce,lbw,kl",
-                    help="comma list of ce, lce, lbw (lce_backward), kl (kl_forward + kl_vjp)")
+    ap.add_argument("--parts", default="ce,lce,lbw,kl,opt,probs",
+                    help="comma list of ce, lce, lbw (lce_backward), kl (kl_forward + kl_vjp), opt "
+                         "(ce_forward_ex + ce_vjp_ex), probs (ce_forward_probs + ce_vjp_probs)")
     ap.add_argument("--bwd-steps", type=int, default=5, help="timed lce_backward calls")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run one elementwise copy (torch.neg) of MIB MiB fp32 first, so a counter "
@@ -285,6 +314,55 @@ def main():
                  float(np.mean([e[1].elapsed_time(e[2]) for e in kev])))
         del KQ, KP, dq_o
 
+    def timed_pair(fwd, vjp, reps=K):
+        for i in range(3):
+            fwd(i)
+            vjp(i)
+        torch.cuda.synchronize()
+        pev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+        for i in range(reps):
+            pev[i][0].record(stream)
+            fwd(i)
+            pev[i][1].record(stream)
+            vjp(i)
+            pev[i][2].record(stream)
+        torch.cuda.synchronize()
+        return (float(np.mean([e[0].elapsed_time(e[1]) for e in pev])),
+                float(np.mean([e[1].elapsed_time(e[2]) for e in pev])))
+
+    opt_ms = None
+    if "opt" in parts and ce_batch is not None:
+        y_ign = ce_batch.targets.copy()
+        y_ign[::16] = -100
+        TI = up(y_ign)
+        o_tot = torch.empty(1, device=dev)
+        o_cnt = torch.empty(1, dtype=torch.int64, device=dev)
+        o_ws = torch.empty(abi.ce_reduce_workspace_size(), dtype=torch.uint8, device=dev)
+        o_g = torch.ones(1, device=dev)
+        opt_ms = timed_pair(
+            lambda i: abi.ce_forward_ex(X[i % 2], TI, 0.1, -100, "mean", loss=loss, lse=lse, total=o_tot,
+                                        count=o_cnt, workspace=o_ws),
+            lambda i: abi.ce_vjp_ex(X[i % 2], TI, lse, o_g, 0.1, -100, "mean", count=o_cnt, dlogits=dX))
+
+    probs_ms = None
+    if "probs" in parts:
+        pz = inputs.kl_pair(KL_ROWS, KL_V, "f32", scale=4.0, stream=2)[0]
+        PZ = torch.from_numpy(pz).to(dev)
+        PT = torch.from_numpy(inputs.prob_targets(KL_ROWS, KL_V, "f32", workload=20, stream=3)).to(dev)
+        p_loss = torch.empty(KL_ROWS, device=dev)
+        p_lse = torch.empty(KL_ROWS, 2, device=dev)
+        p_w = torch.empty(KL_ROWS, device=dev)
+        p_tot = torch.empty(1, device=dev)
+        p_cnt = torch.empty(1, dtype=torch.int64, device=dev)
+        p_ws = torch.empty(abi.ce_reduce_workspace_size(), dtype=torch.uint8, device=dev)
+        p_g = torch.ones(1, device=dev)
+        p_d = torch.empty_like(PZ)
+        probs_ms = timed_pair(
+            lambda i: abi.ce_forward_probs(PZ, PT, 0.1, "mean", loss=p_loss, lse=p_lse, wsum=p_w, total=p_tot,
+                                           count=p_cnt, workspace=p_ws),
+            lambda i: abi.ce_vjp_probs(PZ, PT, p_lse, p_w, p_g, 0.1, "mean", count=p_cnt, dlogits=p_d))
+        del PZ, PT, p_d
+
     bwd_ms = None
     if "lbw" in parts and lce_in is not None:
         G_up = torch.from_numpy(np.random.default_rng([5, 0]).uniform(0.25, 2.0, LCE_N).astype(np.float32)).to(dev)
@@ -372,6 +450,25 @@ def main():
                                "frac": a / HBM_PEAK_GBS, "traffic": traffic_for(name), "ms": t,
                                "algorithmic_bytes": byts}
         cfg["kl"] = {"rows": KL_ROWS, "V": KL_V, "dtype": "f32", "scale": 4.0, "timed": "apart"}
+    for key, tms, (fb, vb), names, cfgv in (
+            ("ce_options", opt_ms, opt_bytes(CE_ROWS, CE_V, 2), ("ce_forward_ex", "ce_vjp_ex"),
+             {"rows": CE_ROWS, "V": CE_V, "dtype": "bf16", "label_smoothing": 0.1, "ignore_index": "every 16th row",
+              "reduction": "mean", "timed": "apart"}),
+            ("ce_probs", probs_ms, probs_bytes(KL_ROWS, KL_V, 4), ("ce_forward_probs", "ce_vjp_probs"),
+             {"rows": KL_ROWS, "V": KL_V, "dtype": "f32", "targets": "U[0,1) rows normalised to 1",
+              "label_smoothing": 0.1, "reduction": "mean", "timed": "apart"})):
+        if tms is None:
+            continue
+        f, v = tms
+        parts_out[key] = {"ms": f + v, "GB_s": (fb + vb) / ((f + v) * 1e-3) / 1e9,
+                          "frac_hbm_peak": (fb + vb) / ((f + v) * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                          "algorithmic_bytes": fb + vb, "fwd_ms": f, "vjp_ms": v, "in_step": False}
+        for name, byts, t in ((names[0], fb, f), (names[1], vb, v)):
+            a = byts / (t * 1e-3) / 1e9
+            rooflines[name] = {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": a / HBM_PEAK_GBS, "traffic": traffic_for(name), "ms": t,
+                               "algorithmic_bytes": byts}
+        cfg[key] = cfgv
     cfg["workload"] = " + ".join(cfg["workload"])
     out["config"] = cfg
     out["parts"] = parts_out

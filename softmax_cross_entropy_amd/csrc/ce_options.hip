@@ -250,8 +250,9 @@ __global__ __launch_bounds__(64 * NW, 8) void ceo_fwd_rowwg(OFwdArgs a) {
 
 // ---- reduction of the per-row losses ---------------------------------------------
 
-// Stage 1: partial sums over fixed blocks of rows, in float64, in a fixed order.  With
-// ignore_index it also writes loss 0 for the ignored rows and leaves them out of the count.
+// Stage 1: partial sums over fixed blocks of rows, in float64, in a fixed order; a single
+// block writes the result itself.  With ignore_index it also writes loss 0 for the
+// ignored rows and leaves them out of the count.
 struct RedArgs {
     float* loss;
     const int32_t* y;  // NULL: every row counts
@@ -262,7 +263,17 @@ struct RedArgs {
     int32_t reduce;  // 0: only the ignore_index fix-up
     double* part_sum;
     int64_t* part_cnt;
+    // one part covers every row: write the result here directly
+    int32_t single;
+    int32_t mean;
+    float* total;
+    int64_t* count;
 };
+
+__device__ __forceinline__ void write_total(double s, int64_t c, int32_t mean, float* total, int64_t* count) {
+    total[0] = (float)(mean ? s / (double)c : s);
+    count[0] = c;
+}
 
 __global__ __launch_bounds__(kBlock) void ceo_reduce_parts(RedArgs a) {
     __shared__ double ssum[kBlock];
@@ -292,8 +303,12 @@ __global__ __launch_bounds__(kBlock) void ceo_reduce_parts(RedArgs a) {
         __syncthreads();
     }
     if (threadIdx.x == 0) {
-        a.part_sum[blockIdx.x] = ssum[0];
-        a.part_cnt[blockIdx.x] = scnt[0];
+        if (a.single) {
+            write_total(ssum[0], scnt[0], a.mean, a.total, a.count);
+        } else {
+            a.part_sum[blockIdx.x] = ssum[0];
+            a.part_cnt[blockIdx.x] = scnt[0];
+        }
     }
 }
 
@@ -320,12 +335,7 @@ __global__ __launch_bounds__(kBlock) void ceo_reduce_final(const double* part_su
         }
         __syncthreads();
     }
-    if (threadIdx.x == 0) {
-        const double s = ssum[0];
-        const int64_t c = scnt[0];
-        total[0] = (float)(mean ? s / (double)c : s);
-        count[0] = c;
-    }
+    if (threadIdx.x == 0) write_total(ssum[0], scnt[0], mean, total, count);
 }
 
 // ---- VJP --------------------------------------------------------------------------
@@ -406,20 +416,11 @@ __device__ __forceinline__ float ograd(float z, float t, const ORow& o, const OV
     return o.zero ? 0.f : v;
 }
 
-// Index targets: the one lane whose vector holds the target stores that element again
-// with the target weight, g (p - ((1 - eps) + eps / V)); same lane, same address.
-template <typename T>
-__device__ __forceinline__ void otarget_fix(const float (&f)[Elem<T>::kVec], int64_t first, const ORow& o, T* drow) {
-    constexpr int kVec = Elem<T>::kVec;
-    const int64_t rel = (int64_t)o.y - first;
-    if ((uint64_t)rel < (uint64_t)kVec) {
-        float zy = f[0];
-#pragma unroll
-        for (int k = 1; k < kVec; ++k) zy = rel == k ? f[k] : zy;
-        Elem<T>::store1(drow + o.y, o.zero ? 0.f : o.g * (oprob(zy, o) - o.cy));
-    }
-}
-
+// One 16-byte vector of gradients.  Index targets: the one lane whose vector holds the
+// target stores that element again with the target weight, g (p - ((1 - eps) + eps / V));
+// same lane, same address.  The target logit is picked from registers by a bitwise
+// select chain: an indexed read of the vector would make the compiler stage every
+// vector through LDS.
 template <typename T, bool kProbs>
 __device__ __forceinline__ void ovec(const U4& bz, const U4& bt, const ORow& o, const OVjpArgs& a, int64_t first,
                                      char* dst, T* drow) {
@@ -430,7 +431,17 @@ __device__ __forceinline__ void ovec(const U4& bz, const U4& bt, const ORow& o, 
 #pragma unroll
     for (int k = 0; k < kVec; ++k) out[k] = ograd<kProbs>(fz[k], kProbs ? ft[k] : 0.f, o, a);
     store_u4(dst, Elem<T>::pack(out));
-    if constexpr (!kProbs) otarget_fix<T>(fz, first, o, drow);
+    if constexpr (!kProbs) {
+        const int64_t rel = (int64_t)o.y - first;
+        if ((uint64_t)rel < (uint64_t)kVec) {
+            const uint32_t r = (uint32_t)rel;
+            uint32_t bits = 0;
+#pragma unroll
+            for (int k = 0; k < kVec; ++k) bits |= (r == (uint32_t)k ? 0xffffffffu : 0u) & __float_as_uint(fz[k]);
+            const float zy = __uint_as_float(bits);
+            Elem<T>::store1(drow + o.y, o.zero ? 0.f : o.g * (oprob(zy, o) - o.cy));
+        }
+    }
 }
 
 template <typename T, bool kProbs>
@@ -644,13 +655,14 @@ hipError_t launch_loss_reduce(const ReduceCall& c) {
     double* part_sum = static_cast<double*>(c.workspace);
     int64_t* part_cnt = reinterpret_cast<int64_t*>(part_sum + kReduceMaxParts);
     const bool reduce = c.reduction != 0;
+    const bool single = reduce && parts == 1;
     if (parts > 0 && (reduce || c.has_ignore)) {
-        RedArgs a{c.loss, c.y, c.n_rows, (c.n_rows + parts - 1) / parts, c.ignore_index, c.has_ignore ? 1 : 0,
-                  reduce ? 1 : 0, part_sum, part_cnt};
+        RedArgs a{c.loss,    c.y,         c.n_rows, (c.n_rows + parts - 1) / parts, c.ignore_index, c.has_ignore ? 1 : 0,
+                  reduce ? 1 : 0, part_sum, part_cnt, single ? 1 : 0, c.reduction == 2 ? 1 : 0, c.total, c.count};
         hipLaunchKernelGGL(ceo_reduce_parts, dim3((unsigned)parts), dim3(kBlock), 0, c.stream, a);
         if (hipError_t e = hipGetLastError()) return e;
     }
-    if (reduce) {
+    if (reduce && !single) {
         hipLaunchKernelGGL(ceo_reduce_final, dim3(1), dim3(kBlock), 0, c.stream, part_sum, part_cnt, parts,
                            c.reduction == 2 ? 1 : 0, c.total, c.count);
         return hipGetLastError();
