@@ -72,13 +72,14 @@ TRAFFIC = {
 
 
 def source_sha(kernel):
-    """sha256 (first 16 hex digits) of the kernel's source file and the two headers it
-    includes (device helpers; launch plans and shared constants)."""
+    """sha256 (first 16 hex digits) of the kernel's source file and the two headers its
+    code depends on (device helpers; launch plans and the constants kernels are built
+    around)."""
     fname = ("lce_kernels.hip" if kernel.startswith("lce") else
              "kl_kernels.hip" if kernel.startswith("kl") else
              "ce_options.hip" if kernel.endswith(("_ex", "_probs")) else "ce_kernels.hip")
     h = hashlib.sha256()
-    for f in (fname, "device_common.h", "launch.h"):
+    for f in (fname, "device_common.h", "plan.h"):
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "plan.h"
+
 namespace ce {
 
 enum class Dt : int { F32 = 0, F16 = 1, BF16 = 2 };
@@ -16,19 +18,6 @@ struct HostLayout {
     int64_t batch_stride;
     int32_t uniform;
 };
-
-// How rows map onto lanes.  narrow_nv > 0: one lane per row, each row exactly
-// narrow_nv aligned 16-byte vectors.  Otherwise `lanes` lanes per row (a power of two
-// in [1, 1024]); above 64 one workgroup of `lanes` threads holds each row.
-struct Plan {
-    int narrow_nv;
-    int lanes;
-    int64_t blocks;
-    int64_t chunks;  // VJP only: > 0 cuts each row into this many chunks of kChunkU * 256 vectors
-};
-
-// Vectors per thread in one chunk of the chunked VJP layout.
-constexpr int kChunkU = 2;
 
 struct FwdCall {
     const void* logits;
@@ -136,13 +125,6 @@ struct OptVjpCall {
     hipStream_t stream;
 };
 
-// Sum / mean of the per-row losses: float64 partial sums over at most kReduceMaxParts
-// blocks of at least kReduceRowsMin rows (a split that depends on n_rows alone), then one
-// fixed-order fold.  The workspace holds the partials: kReduceMaxParts doubles, then as
-// many int64 counts.
-constexpr int64_t kReduceMaxParts = 1024;
-constexpr int64_t kReduceRowsMin = 4096;
-constexpr size_t kReduceWorkspaceBytes = (size_t)kReduceMaxParts * 16;
 
 struct ReduceCall {
     float* loss;
