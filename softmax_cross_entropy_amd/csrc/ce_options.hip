@@ -371,19 +371,20 @@ struct ORow {
     int32_t zero;  // ignored row: the gradient is 0 whatever the logits hold
 };
 
+// The upstream gradient shared by every row of a reduced loss: g, or g / count for a
+// mean (formed once per thread, not per work item).
+__device__ __forceinline__ float shared_upstream(const OVjpArgs& a) {
+    if (a.reduction == 0) return 0.f;
+    if (a.reduction == 1) return a.g[0];
+    return (float)((double)a.g[0] / (double)a.count[0]);
+}
+
 template <bool kProbs>
-__device__ __forceinline__ ORow load_orow(const OVjpArgs& a, int64_t r) {
+__device__ __forceinline__ ORow load_orow(const OVjpArgs& a, int64_t r, float gs) {
     ORow o;
-    float g;
-    if (a.reduction == 0)
-        g = a.g[r];
-    else if (a.reduction == 1)
-        g = a.g[0];
-    else
-        g = (float)((double)a.g[0] / (double)a.count[0]);
     const float2 l = a.lse[r];
     o.lsl = l.y * kLog2e;
-    o.g = g;
+    o.g = a.reduction == 0 ? a.g[r] : gs;
     o.cy = a.keep + a.eps_v;
     o.zero = 0;
     o.W = 0.f;
@@ -472,11 +473,12 @@ __global__ __launch_bounds__(G > kBlock ? G : kBlock) void ceo_vjp_lanes(OVjpArg
     constexpr int kRowsPerBlock = kThreads / G;
     const int lane = threadIdx.x % G;
     const int64_t stride = (int64_t)gridDim.x * kRowsPerBlock;
+    const float gs = shared_upstream(a);
     for (int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / G; r < a.n_rows; r += stride) {
         const T* z = static_cast<const T*>(a.z) + row_offset(r, a.zl);
         const T* t = kProbs ? static_cast<const T*>(a.t) + row_offset(r, a.tl) : nullptr;
         T* d = static_cast<T*>(a.d) + row_offset(r, a.dl);
-        const ORow o = load_orow<kProbs>(a, r);
+        const ORow o = load_orow<kProbs>(a, r, gs);
         if (ophases<T, kProbs>(z, t, d)) {
             RowSplit<T> sp(z, a.V);
             const char* zb = reinterpret_cast<const char*>(z + sp.head);
@@ -515,13 +517,14 @@ __global__ __launch_bounds__(kBlock) void ceo_vjp_chunks(OVjpArgs a, int64_t chu
     constexpr int64_t kChunkVec = (int64_t)kBlock * U;
     const int tid = threadIdx.x;
     const int64_t items = a.n_rows * chunks_per_row;
+    const float gs = shared_upstream(a);
     for (int64_t w = blockIdx.x; w < items; w += gridDim.x) {
         const int64_t r = w / chunks_per_row;
         const int64_t c = w - r * chunks_per_row;
         const T* z = static_cast<const T*>(a.z) + row_offset(r, a.zl);
         const T* t = kProbs ? static_cast<const T*>(a.t) + row_offset(r, a.tl) : nullptr;
         T* d = static_cast<T*>(a.d) + row_offset(r, a.dl);
-        const ORow o = load_orow<kProbs>(a, r);
+        const ORow o = load_orow<kProbs>(a, r, gs);
         if (ophases<T, kProbs>(z, t, d)) {
             RowSplit<T> sp(z, a.V);
             const char* zb = reinterpret_cast<const char*>(z + sp.head);
