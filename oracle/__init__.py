@@ -16,10 +16,12 @@ It writes out the plain definitions in float64 NumPy:
   the sum / mean reductions of the cross-entropy, with their gradients.
 * ``oracle.kl``: the row-wise KL divergence of a teacher row from a student row
   and its gradient with respect to the student logits.
+* ``oracle.js``: the row-wise Jensen-Shannon divergence of the two rows and its
+  gradient with respect to the student logits.
 
 Every function is pinned by ``tests/test_oracle*.py`` against values the pages
 print, closed forms, invariants and brute force.  No function here is
 "parity unpinned".
 """
 
-from . import ce, ce_options, kl, lce  # noqa: F401
+from . import ce, ce_options, js, kl, lce  # noqa: F401
