@@ -12,6 +12,8 @@
  *                 regenerated gradient chunk run on rocBLAS
  *   kl_forward    per-row KL divergence of a teacher logits row from a student row
  *   kl_vjp        dq = g_i * (softmax(q_i) - softmax(p_i)) from the saved pairs
+ *   js_forward    per-row Jensen-Shannon divergence of a student row and a teacher row
+ *   js_vjp        its gradient with respect to the student logits
  *   ce_forward_ex / ce_vjp_ex        ce_forward / ce_vjp with label smoothing,
  *                                    ignore_index and an in-library sum or mean
  *   ce_forward_probs / ce_vjp_probs  the same with probability targets
@@ -279,6 +281,51 @@ ce_status kl_vjp(const void* q, ce_layout q_layout, const void* p, ce_layout p_l
 ce_status kl_vjp_lanes(const void* q, ce_layout q_layout, const void* p, ce_layout p_layout, ce_dtype dt,
                        const float* lse_q, const float* lse_p, const float* g, int64_t n_rows, int64_t V,
                        void* dq, ce_layout dq_layout, int32_t lanes_per_row, hipStream_t stream);
+
+/*
+ * js_forward: js_i = 1/2 KL(P_i || M_i) + 1/2 KL(Q_i || M_i), M = (P + Q) / 2, with
+ * P = softmax(p_i) (teacher) and Q = softmax(q_i) (student).
+ *
+ * Source: "One barrier short", first section: mlx-lm fuses the Jensen-Shannon divergence
+ * of a student and a teacher the way it fuses the KL one; section "The fix": at a logit
+ * scale of 20 the loss overflowed to non-finite values until a numerically stable
+ * softplus was used.  log M is formed as log Q + softplus(log P - log Q) - log 2 with
+ * softplus(x) = max(x, 0) + log(1 + e^-|x|), which cannot overflow.
+ *
+ *   q, q_layout, p, p_layout, dt, n_rows, V  as in kl_forward.
+ *   js     float32 [n_rows] (written).
+ *   lse_q, lse_p  float32 [n_rows][2] (written): (m, log s) of q and p.
+ *   hq     float32 [n_rows] (written): H = 1/2 KL(Q || M), the student's half, which
+ *          js_vjp needs.
+ * Each row is read twice: the terms need both normalisers first.  A row pair where either
+ * row has no softmax (all -inf, or a +inf / NaN entry) gives NaN.  Zero probabilities
+ * contribute nothing (0 log 0 = 0); js is always finite otherwise, in [0, ln 2].
+ * Outputs must not overlap the inputs or each other (CE_ERR_ALIAS).
+ */
+ce_status js_forward(const void* q, ce_layout q_layout, const void* p, ce_layout p_layout, ce_dtype dt,
+                     int64_t n_rows, int64_t V, float* js, float* lse_q, float* lse_p, float* hq,
+                     hipStream_t stream);
+
+/* js_forward with lanes_per_row as in kl_forward_lanes. */
+ce_status js_forward_lanes(const void* q, ce_layout q_layout, const void* p, ce_layout p_layout, ce_dtype dt,
+                           int64_t n_rows, int64_t V, float* js, float* lse_q, float* lse_p, float* hq,
+                           int32_t lanes_per_row, hipStream_t stream);
+
+/*
+ * js_vjp: dq_ik = g_i Q_ik (h_ik - H_i), h_ik = (log Q_ik - log M_ik) / 2, the gradient of
+ * sum_i g_i js_i with respect to the student logits, from js_forward's lse_q, lse_p, hq.
+ *   g   float32 [n_rows].  dq  [n_rows rows of V] of dtype `dt` through `dq_layout`
+ *       (written; may be q itself with an identical layout, must not overlap p, lse_q,
+ *       lse_p, hq or g).
+ */
+ce_status js_vjp(const void* q, ce_layout q_layout, const void* p, ce_layout p_layout, ce_dtype dt,
+                 const float* lse_q, const float* lse_p, const float* hq, const float* g, int64_t n_rows, int64_t V,
+                 void* dq, ce_layout dq_layout, hipStream_t stream);
+
+/* js_vjp with lanes_per_row as in kl_vjp_lanes. */
+ce_status js_vjp_lanes(const void* q, ce_layout q_layout, const void* p, ce_layout p_layout, ce_dtype dt,
+                       const float* lse_q, const float* lse_p, const float* hq, const float* g, int64_t n_rows,
+                       int64_t V, void* dq, ce_layout dq_layout, int32_t lanes_per_row, hipStream_t stream);
 
 /*
  * ---- Cross-entropy options --------------------------------------------------------

@@ -31,7 +31,8 @@ CE_NO_IGNORE = -(2 ** 31)
 # every symbol include/ce_mi355x.h declares
 EXPORTS = ("ce_forward", "ce_forward_lanes", "ce_vjp", "ce_vjp_lanes", "lce_workspace_size",
            "lce_forward", "lce_backward_workspace_size", "lce_backward", "kl_forward", "kl_forward_lanes",
-           "kl_vjp", "kl_vjp_lanes", "ce_reduce_workspace_size", "ce_forward_ex", "ce_vjp_ex", "ce_forward_probs",
+           "kl_vjp", "kl_vjp_lanes", "js_forward", "js_forward_lanes", "js_vjp", "js_vjp_lanes",
+           "ce_reduce_workspace_size", "ce_forward_ex", "ce_vjp_ex", "ce_forward_probs",
            "ce_vjp_probs", "ce_status_string")
 
 
@@ -85,6 +86,13 @@ def lib() -> ctypes.CDLL:
                              CELayout, _vp]
         L.kl_vjp_lanes.argtypes = [_vp, CELayout, _vp, CELayout, ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _vp,
                                    CELayout, _i32, _vp]
+        L.js_forward.argtypes = [_vp, CELayout, _vp, CELayout, ctypes.c_int, _i64, _i64, _vp, _vp, _vp, _vp, _vp]
+        L.js_forward_lanes.argtypes = [_vp, CELayout, _vp, CELayout, ctypes.c_int, _i64, _i64, _vp, _vp, _vp, _vp,
+                                       _i32, _vp]
+        L.js_vjp.argtypes = [_vp, CELayout, _vp, CELayout, ctypes.c_int, _vp, _vp, _vp, _vp, _i64, _i64, _vp,
+                             CELayout, _vp]
+        L.js_vjp_lanes.argtypes = [_vp, CELayout, _vp, CELayout, ctypes.c_int, _vp, _vp, _vp, _vp, _i64, _i64, _vp,
+                                   CELayout, _i32, _vp]
         L.ce_reduce_workspace_size.argtypes = []
         L.ce_reduce_workspace_size.restype = _sz
         L.ce_forward_ex.argtypes = [_vp, CELayout, ctypes.c_int, _vp, _i64, _i64, CEOptions, _vp, _vp, _vp, _vp, _vp,
@@ -98,7 +106,8 @@ def lib() -> ctypes.CDLL:
         L.ce_status_string.argtypes = [ctypes.c_int]
         L.ce_status_string.restype = ctypes.c_char_p
         for name in ("ce_forward", "ce_forward_lanes", "ce_vjp", "ce_vjp_lanes", "lce_forward", "lce_backward",
-                     "kl_forward", "kl_forward_lanes", "kl_vjp", "kl_vjp_lanes", "ce_forward_ex", "ce_vjp_ex",
+                     "kl_forward", "kl_forward_lanes", "kl_vjp", "kl_vjp_lanes", "js_forward", "js_forward_lanes",
+                     "js_vjp", "js_vjp_lanes", "ce_forward_ex", "ce_vjp_ex",
                      "ce_forward_probs", "ce_vjp_probs"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -184,6 +193,56 @@ def ce_vjp(logits: torch.Tensor, targets: torch.Tensor, lse: torch.Tensor, g: to
         st = lib().ce_vjp_lanes(*args, int(lanes_per_row), _stream(logits))
     _check(st, "ce_vjp")
     return dlogits
+
+
+def js_forward(q: torch.Tensor, p: torch.Tensor, js=None, lse_q=None, lse_p=None, hq=None, lanes_per_row: int = 0):
+    """Per-row (js [n], lse_q [n, 2], lse_p [n, 2], hq [n]) of the student q and teacher p."""
+    if q.dtype != p.dtype or q.shape != p.shape:
+        raise ValueError("q and p must have the same dtype and shape")
+    ql, n, V = _view(q, "q")
+    pl, _, _ = _view(p, "p")
+    dev = q.device
+    js = torch.empty(n, dtype=torch.float32, device=dev) if js is None else js
+    lse_q = torch.empty(n, 2, dtype=torch.float32, device=dev) if lse_q is None else lse_q
+    lse_p = torch.empty(n, 2, dtype=torch.float32, device=dev) if lse_p is None else lse_p
+    hq = torch.empty(n, dtype=torch.float32, device=dev) if hq is None else hq
+    _need(js, torch.float32, n, "js")
+    _need(lse_q, torch.float32, 2 * n, "lse_q")
+    _need(lse_p, torch.float32, 2 * n, "lse_p")
+    _need(hq, torch.float32, n, "hq")
+    args = (_ptr(q), ql, _ptr(p), pl, DTYPE_CODE[q.dtype], n, V, _ptr(js), _ptr(lse_q), _ptr(lse_p), _ptr(hq))
+    if lanes_per_row == 0:
+        st = lib().js_forward(*args, _stream(q))
+    else:
+        st = lib().js_forward_lanes(*args, int(lanes_per_row), _stream(q))
+    _check(st, "js_forward")
+    return js, lse_q, lse_p, hq
+
+
+def js_vjp(q: torch.Tensor, p: torch.Tensor, lse_q: torch.Tensor, lse_p: torch.Tensor, hq: torch.Tensor,
+           g: torch.Tensor, dq=None, lanes_per_row: int = 0):
+    """dq = g * Q * (h - H) from js_forward's outputs; same shape and dtype as q."""
+    if q.dtype != p.dtype or q.shape != p.shape:
+        raise ValueError("q and p must have the same dtype and shape")
+    ql, n, V = _view(q, "q")
+    pl, _, _ = _view(p, "p")
+    _need(lse_q, torch.float32, 2 * n, "lse_q")
+    _need(lse_p, torch.float32, 2 * n, "lse_p")
+    _need(hq, torch.float32, n, "hq")
+    _need(g, torch.float32, n, "g")
+    if dq is None:
+        dq = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if dq.dtype != q.dtype or dq.shape != q.shape:
+        raise ValueError("dq must match q in dtype and shape")
+    dl, _, _ = _view(dq, "dq")
+    args = (_ptr(q), ql, _ptr(p), pl, DTYPE_CODE[q.dtype], _ptr(lse_q), _ptr(lse_p), _ptr(hq), _ptr(g), n, V,
+            _ptr(dq), dl)
+    if lanes_per_row == 0:
+        st = lib().js_vjp(*args, _stream(q))
+    else:
+        st = lib().js_vjp_lanes(*args, int(lanes_per_row), _stream(q))
+    _check(st, "js_vjp")
+    return dq
 
 
 def ce_reduce_workspace_size() -> int:

@@ -365,56 +365,72 @@ bool lanes_ok_kl(int32_t lanes) {
     return lanes == 0 || (lanes >= 1 && lanes <= 1024 && (lanes & (lanes - 1)) == 0);
 }
 
-ce_status kl_forward_impl(const void* q, ce_layout ql, const void* p, ce_layout pl, ce_dtype dt, int64_t n_rows,
-                          int64_t V, float* kl, float* lse_q, float* lse_p, int32_t lanes, hipStream_t stream) {
+// The two row-pair divergences share their checks and layouts: the KL forward writes
+// (kl, lse_q, lse_p), the Jensen-Shannon forward also the student's half H (`hq`), which
+// its VJP reads back.
+enum class Div { KL, JS };
+
+ce_status div_forward_impl(Div div, const void* q, ce_layout ql, const void* p, ce_layout pl, ce_dtype dt,
+                           int64_t n_rows, int64_t V, float* out, float* lse_q, float* lse_p, float* hq,
+                           int32_t lanes, hipStream_t stream) {
     if (!valid_dtype((int)dt)) return CE_ERR_DTYPE;
     if (n_rows < 0 || V < 1 || V > kMaxV || !lanes_ok_kl(lanes)) return CE_ERR_SHAPE;
     if (n_rows == 0) return CE_OK;
-    if (!q || !p || !kl || !lse_q || !lse_p) return CE_ERR_NULL;
+    const bool js = div == Div::JS;
+    if (!q || !p || !out || !lse_q || !lse_p || (js && !hq)) return CE_ERR_NULL;
     const int es = esize(dt);
     if (!layout_ok(ql, n_rows, V, false) || !layout_ok(pl, n_rows, V, false) || !aligned(q, es) ||
-        !aligned(p, es) || !aligned(kl, 4) || !aligned(lse_q, 8) || !aligned(lse_p, 8))
+        !aligned(p, es) || !aligned(out, 4) || !aligned(lse_q, 8) || !aligned(lse_p, 8) || !aligned(hq, 4))
         return CE_ERR_LAYOUT;
     const Extent ins[2] = {view_extent(q, ql, n_rows, V, es), view_extent(p, pl, n_rows, V, es)};
-    const Extent outs[3] = {flat_extent(kl, n_rows * 4), flat_extent(lse_q, n_rows * 8),
-                            flat_extent(lse_p, n_rows * 8)};
-    for (const Extent& o : outs)
-        for (const Extent& i : ins)
-            if (overlaps(o, i)) return CE_ERR_ALIAS;
-    if (overlaps(outs[0], outs[1]) || overlaps(outs[0], outs[2]) || overlaps(outs[1], outs[2])) return CE_ERR_ALIAS;
+    const Extent outs[4] = {flat_extent(out, n_rows * 4), flat_extent(lse_q, n_rows * 8),
+                            flat_extent(lse_p, n_rows * 8), flat_extent(hq, js ? n_rows * 4 : 0)};
+    if (alias_any(outs, 4, ins, 2)) return CE_ERR_ALIAS;
     int cus = 0;
     if (ce_status s = device_cus(&cus)) return s;
     Plan plan;
     if (ce_status s = make_plan(false, V, es, n_rows, lanes, false, cus, &plan)) return s;
-    ce::KLFwdCall c{q, host_layout(ql, n_rows), p, host_layout(pl, n_rows), (Dt)dt, n_rows, V, kl, lse_q, lse_p,
+    if (js) {
+        ce::JSFwdCall c{q,   host_layout(ql, n_rows), p,     host_layout(pl, n_rows), (Dt)dt, n_rows, V,
+                        out, lse_q,                   lse_p, hq,                      plan,   stream};
+        return from_hip(ce::launch_js_forward(c));
+    }
+    ce::KLFwdCall c{q, host_layout(ql, n_rows), p, host_layout(pl, n_rows), (Dt)dt, n_rows, V, out, lse_q, lse_p,
                     plan, stream};
     return from_hip(ce::launch_kl_forward(c));
 }
 
-ce_status kl_vjp_impl(const void* q, ce_layout ql, const void* p, ce_layout pl, ce_dtype dt, const float* lse_q,
-                      const float* lse_p, const float* g, int64_t n_rows, int64_t V, void* dq, ce_layout dl,
-                      int32_t lanes, hipStream_t stream) {
+ce_status div_vjp_impl(Div div, const void* q, ce_layout ql, const void* p, ce_layout pl, ce_dtype dt,
+                       const float* lse_q, const float* lse_p, const float* hq, const float* g, int64_t n_rows,
+                       int64_t V, void* dq, ce_layout dl, int32_t lanes, hipStream_t stream) {
     if (!valid_dtype((int)dt)) return CE_ERR_DTYPE;
     if (n_rows < 0 || V < 1 || V > kMaxV || !lanes_ok_kl(lanes)) return CE_ERR_SHAPE;
     if (n_rows == 0) return CE_OK;
-    if (!q || !p || !lse_q || !lse_p || !g || !dq) return CE_ERR_NULL;
+    const bool js = div == Div::JS;
+    if (!q || !p || !lse_q || !lse_p || !g || !dq || (js && !hq)) return CE_ERR_NULL;
     const int es = esize(dt);
     if (!layout_ok(ql, n_rows, V, false) || !layout_ok(pl, n_rows, V, false) || !layout_ok(dl, n_rows, V, true) ||
         !aligned(q, es) || !aligned(p, es) || !aligned(dq, es) || !aligned(lse_q, 8) || !aligned(lse_p, 8) ||
-        !aligned(g, 4))
+        !aligned(g, 4) || !aligned(hq, 4))
         return CE_ERR_LAYOUT;
     const Extent ex_q = view_extent(q, ql, n_rows, V, es);
     const Extent ex_d = view_extent(dq, dl, n_rows, V, es);
     const bool in_place = q == dq && same_layout(ql, dl, n_rows);
     if (!in_place && overlaps(ex_q, ex_d)) return CE_ERR_ALIAS;
-    if (overlaps(ex_d, view_extent(p, pl, n_rows, V, es)) || overlaps(ex_d, flat_extent(lse_q, n_rows * 8)) ||
-        overlaps(ex_d, flat_extent(lse_p, n_rows * 8)) || overlaps(ex_d, flat_extent(g, n_rows * 4)))
-        return CE_ERR_ALIAS;
+    const Extent ins[5] = {view_extent(p, pl, n_rows, V, es), flat_extent(lse_q, n_rows * 8),
+                           flat_extent(lse_p, n_rows * 8), flat_extent(g, n_rows * 4),
+                           flat_extent(hq, js ? n_rows * 4 : 0)};
+    if (alias_any(&ex_d, 1, ins, 5)) return CE_ERR_ALIAS;
     int cus = 0;
     if (ce_status s = device_cus(&cus)) return s;
     Plan plan;
     if (lanes != 0 || !chunk_plan(V, es, n_rows, cus, &plan))
         if (ce_status s = make_plan(false, V, es, n_rows, lanes, true, cus, &plan)) return s;
+    if (js) {
+        ce::JSVjpCall c{q, host_layout(ql, n_rows), p, host_layout(pl, n_rows), (Dt)dt, lse_q, lse_p, hq, g,
+                        n_rows, V, dq, host_layout(dl, n_rows), plan, stream};
+        return from_hip(ce::launch_js_vjp(c));
+    }
     ce::KLVjpCall c{q,     host_layout(ql, n_rows), p, host_layout(pl, n_rows), (Dt)dt, lse_q, lse_p, g, n_rows,
                     V,     dq, host_layout(dl, n_rows), plan, stream};
     return from_hip(ce::launch_kl_vjp(c));
@@ -512,26 +528,56 @@ ce_status lce_backward(const void* H, const void* W, const int32_t* targets, con
 
 ce_status kl_forward(const void* q, ce_layout q_layout, const void* p, ce_layout p_layout, ce_dtype dt,
                      int64_t n_rows, int64_t V, float* kl, float* lse_q, float* lse_p, hipStream_t stream) {
-    return kl_forward_impl(q, q_layout, p, p_layout, dt, n_rows, V, kl, lse_q, lse_p, 0, stream);
+    return div_forward_impl(Div::KL, q, q_layout, p, p_layout, dt, n_rows, V, kl, lse_q, lse_p, nullptr, 0,
+                            stream);
 }
 
 ce_status kl_forward_lanes(const void* q, ce_layout q_layout, const void* p, ce_layout p_layout, ce_dtype dt,
                            int64_t n_rows, int64_t V, float* kl, float* lse_q, float* lse_p, int32_t lanes_per_row,
                            hipStream_t stream) {
-    return kl_forward_impl(q, q_layout, p, p_layout, dt, n_rows, V, kl, lse_q, lse_p, lanes_per_row, stream);
+    return div_forward_impl(Div::KL, q, q_layout, p, p_layout, dt, n_rows, V, kl, lse_q, lse_p, nullptr,
+                            lanes_per_row, stream);
 }
 
 ce_status kl_vjp(const void* q, ce_layout q_layout, const void* p, ce_layout p_layout, ce_dtype dt,
                  const float* lse_q, const float* lse_p, const float* g, int64_t n_rows, int64_t V, void* dq,
                  ce_layout dq_layout, hipStream_t stream) {
-    return kl_vjp_impl(q, q_layout, p, p_layout, dt, lse_q, lse_p, g, n_rows, V, dq, dq_layout, 0, stream);
+    return div_vjp_impl(Div::KL, q, q_layout, p, p_layout, dt, lse_q, lse_p, nullptr, g, n_rows, V, dq, dq_layout,
+                        0, stream);
 }
 
 ce_status kl_vjp_lanes(const void* q, ce_layout q_layout, const void* p, ce_layout p_layout, ce_dtype dt,
                        const float* lse_q, const float* lse_p, const float* g, int64_t n_rows, int64_t V, void* dq,
                        ce_layout dq_layout, int32_t lanes_per_row, hipStream_t stream) {
-    return kl_vjp_impl(q, q_layout, p, p_layout, dt, lse_q, lse_p, g, n_rows, V, dq, dq_layout, lanes_per_row,
-                       stream);
+    return div_vjp_impl(Div::KL, q, q_layout, p, p_layout, dt, lse_q, lse_p, nullptr, g, n_rows, V, dq, dq_layout,
+                        lanes_per_row, stream);
+}
+
+ce_status js_forward(const void* q, ce_layout q_layout, const void* p, ce_layout p_layout, ce_dtype dt,
+                     int64_t n_rows, int64_t V, float* js, float* lse_q, float* lse_p, float* hq,
+                     hipStream_t stream) {
+    return div_forward_impl(Div::JS, q, q_layout, p, p_layout, dt, n_rows, V, js, lse_q, lse_p, hq, 0, stream);
+}
+
+ce_status js_forward_lanes(const void* q, ce_layout q_layout, const void* p, ce_layout p_layout, ce_dtype dt,
+                           int64_t n_rows, int64_t V, float* js, float* lse_q, float* lse_p, float* hq,
+                           int32_t lanes_per_row, hipStream_t stream) {
+    return div_forward_impl(Div::JS, q, q_layout, p, p_layout, dt, n_rows, V, js, lse_q, lse_p, hq, lanes_per_row,
+                            stream);
+}
+
+ce_status js_vjp(const void* q, ce_layout q_layout, const void* p, ce_layout p_layout, ce_dtype dt,
+                 const float* lse_q, const float* lse_p, const float* hq, const float* g, int64_t n_rows, int64_t V,
+                 void* dq, ce_layout dq_layout, hipStream_t stream) {
+    return div_vjp_impl(Div::JS, q, q_layout, p, p_layout, dt, lse_q, lse_p, hq, g, n_rows, V, dq, dq_layout, 0,
+                        stream);
+}
+
+ce_status js_vjp_lanes(const void* q, ce_layout q_layout, const void* p, ce_layout p_layout, ce_dtype dt,
+                       const float* lse_q, const float* lse_p, const float* hq, const float* g, int64_t n_rows,
+                       int64_t V, void* dq, ce_layout dq_layout, int32_t lanes_per_row, hipStream_t stream) {
+    return div_vjp_impl(Div::JS, q, q_layout, p, p_layout, dt, lse_q, lse_p, hq, g, n_rows, V, dq, dq_layout,
+                        lanes_per_row, stream);
 }
 
 size_t ce_reduce_workspace_size(void) { return ce::kReduceWorkspaceBytes; }

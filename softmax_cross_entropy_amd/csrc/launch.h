@@ -83,6 +83,44 @@ struct KLVjpCall {
     hipStream_t stream;
 };
 
+// Jensen-Shannon (js_kernels.hip): hq is the student's half H per row.
+struct JSFwdCall {
+    const void* q;
+    HostLayout ql;
+    const void* p;
+    HostLayout pl;
+    Dt dt;
+    int64_t n_rows;
+    int64_t V;
+    float* js;
+    float* lse_q;
+    float* lse_p;
+    float* hq;
+    Plan plan;
+    hipStream_t stream;
+};
+
+struct JSVjpCall {
+    const void* q;
+    HostLayout ql;
+    const void* p;
+    HostLayout pl;
+    Dt dt;
+    const float* lse_q;
+    const float* lse_p;
+    const float* hq;
+    const float* g;
+    int64_t n_rows;
+    int64_t V;
+    void* dq;
+    HostLayout dl;
+    Plan plan;
+    hipStream_t stream;
+};
+
+hipError_t launch_js_forward(const JSFwdCall& c);
+hipError_t launch_js_vjp(const JSVjpCall& c);
+
 // Cross-entropy options (ce_options.hip).  t != NULL selects probability targets;
 // otherwise y holds class-index targets.
 struct OptFwdCall {

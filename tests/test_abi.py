@@ -207,6 +207,31 @@ def test_kl_rejects_bad_arguments():
     assert klv(dq=P_LOGITS) in (OK, DEVICE)  # in place, identical layout
 
 
+P_HQ = ctypes.c_void_p(A * 350)
+
+
+def jsf(q=P_LOGITS, dt=0, p=P_P, n=16, V=8, js=P_KL, lq=P_LQ, lp=P_LP, hq=P_HQ, lanes=0):
+    return abi.lib().js_forward_lanes(q, lay(n, V), p, lay(n, V), dt, n, V, js, lq, lp, hq, lanes, None)
+
+
+def jsv(q=P_LOGITS, dt=0, p=P_P, lq=P_LQ, lp=P_LP, hq=P_HQ, g=P_G, n=16, V=8, dq=P_DQ, lanes=0):
+    return abi.lib().js_vjp_lanes(q, lay(n, V), p, lay(n, V), dt, lq, lp, hq, g, n, V, dq, lay(n, V), lanes, None)
+
+
+def test_js_rejects_bad_arguments():
+    assert jsf(dt=3) == DTYPE and jsv(dt=-1) == DTYPE
+    assert jsf(V=0) == SHAPE and jsv(n=-1) == SHAPE and jsf(lanes=3) == SHAPE
+    assert jsf(n=0, q=None) == OK and jsv(n=0, dq=None) == OK
+    for name in ("q", "p", "js", "lq", "lp", "hq"):
+        assert jsf(**{name: None}) == NULL, name
+    for name in ("q", "p", "lq", "lp", "hq", "g", "dq"):
+        assert jsv(**{name: None}) == NULL, name
+    assert jsf(hq=ctypes.c_void_p(350 * A + 2)) == LAYOUT
+    assert jsf(hq=P_KL) == ALIAS and jsf(hq=P_P) == ALIAS
+    assert jsv(dq=P_HQ) == ALIAS and jsv(dq=P_P) == ALIAS
+    assert jsv(dq=P_LOGITS) in (OK, DEVICE)
+
+
 P_TOT, P_CNT, P_RWS, P_PR, P_WSUM, P_GR = (ctypes.c_void_p(A * k) for k in (400, 401, 402, 410, 420, 421))
 WSB = 1 << 14
 
@@ -279,4 +304,5 @@ def test_valid_call_without_device_reports_device_error():
     assert klf() == DEVICE
     assert klv() == DEVICE
     assert fex() == DEVICE and vex() == DEVICE and fpr() == DEVICE and vpr() == DEVICE
+    assert jsf() == DEVICE and jsv() == DEVICE
     assert fex(n=0, logits=None, t=None, loss=None, lse=None) == DEVICE
