@@ -77,6 +77,7 @@ def source_sha(kernel):
     around)."""
     fname = ("lce_kernels.hip" if kernel.startswith("lce") else
              "kl_kernels.hip" if kernel.startswith("kl") else
+             "js_kernels.hip" if kernel.startswith("js") else
              "ce_options.hip" if kernel.endswith(("_ex", "_probs")) else "ce_kernels.hip")
     h = hashlib.sha256()
     for f in (fname, "device_common.h", "plan.h"):
@@ -106,6 +107,14 @@ def kl_bytes(rows, V, e):
     and the two (m, log s) pairs (16); the VJP reads both rows, the pairs and g (20)
     and writes the student gradient."""
     return rows * (2 * V * e + 20), rows * (3 * V * e + 20)
+
+
+def js_bytes(rows, V, e):
+    """Jensen-Shannon: the terms need both row normalisers first, so the forward reads both
+    rows twice (a 1.2 MB fp32 row pair does not stay on chip) and writes js, the two pairs
+    and H (24 per row); the VJP reads both rows, the pairs, H and g (24) and writes the
+    gradient."""
+    return rows * (4 * V * e + 24), rows * (3 * V * e + 24)
 
 
 def opt_bytes(rows, V, e):
@@ -162,6 +171,12 @@ def cpu_baseline(ce_batch, lce_inputs, lce_rows=32):
     okl.grad(zq, zp, kg)
     kl_s = time.perf_counter() - t0
     kf_b, kv_b = kl_bytes(32, KL_V, 4)
+    from oracle import js as ojs
+    t0 = time.perf_counter()
+    ojs.forward(zq, zp)
+    ojs.grad(zq, zp, kg)
+    js_s = time.perf_counter() - t0
+    jf_b, jv_b = js_bytes(32, KL_V, 4)
     from oracle import ce_options as oco
     y_ign = b.targets[:32].copy()
     y_ign[::16] = -100
@@ -186,6 +201,8 @@ def cpu_baseline(ce_batch, lce_inputs, lce_rows=32):
         "ce_options": {"value": (of_b + ov_b) / opt_s / 1e9, "unit": "GB/s", "cores": 1, "seconds": opt_s,
                        "sample": f"options oracle (eps 0.1, ignore_index, mean; float64 NumPy) on 32 of "
                                  f"{b.rows} rows, all {b.V} columns"},
+        "js": {"value": (jf_b + jv_b) / js_s / 1e9, "unit": "GB/s", "cores": 1, "seconds": js_s,
+               "sample": f"JS fwd+grad oracle (float64 NumPy) on 32 of {KL_ROWS} rows, all {KL_V} columns"},
         "kl": {"value": (kf_b + kv_b) / kl_s / 1e9, "unit": "GB/s", "cores": 1, "seconds": kl_s,
                "sample": f"KL fwd+grad oracle (float64 NumPy) on 32 of {KL_ROWS} rows, all {KL_V} columns"},
         "lce_backward": {"value": 3 * lce_flops(lce_rows, LCE_D, LCE_V) / lbw_s / 1e12, "unit": "TFLOP/s",
@@ -202,9 +219,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--parts", default="ce,lce,lbw,kl,opt,probs",
-                    help="comma list of ce, lce, lbw (lce_backward), kl (kl_forward + kl_vjp), opt "
-                         "(ce_forward_ex + ce_vjp_ex), probs (ce_forward_probs + ce_vjp_probs)")
+    ap.add_argument("--parts", default="ce,lce,lbw,kl,js,opt,probs",
+                    help="comma list of ce, lce, lbw (lce_backward), kl (kl_forward + kl_vjp), js (js_forward + "
+                         "js_vjp), opt (ce_forward_ex + ce_vjp_ex), probs (ce_forward_probs + ce_vjp_probs)")
     ap.add_argument("--bwd-steps", type=int, default=5, help="timed lce_backward calls")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run one elementwise copy (torch.neg) of MIB MiB fp32 first, so a counter "
@@ -331,6 +348,23 @@ def main():
         return (float(np.mean([e[0].elapsed_time(e[1]) for e in pev])),
                 float(np.mean([e[1].elapsed_time(e[2]) for e in pev])))
 
+    js_ms = None
+    if "js" in parts:
+        jq, jp, jg = inputs.kl_pair(KL_ROWS, KL_V, "f32", scale=4.0, stream=4)
+        jq2, jp2, _ = inputs.kl_pair(KL_ROWS, KL_V, "f32", scale=4.0, stream=5)
+        JQ = [torch.from_numpy(jq).to(dev), torch.from_numpy(jq2).to(dev)]
+        JP = [torch.from_numpy(jp).to(dev), torch.from_numpy(jp2).to(dev)]
+        JG = torch.from_numpy(jg).to(dev)
+        j_o = torch.empty(KL_ROWS, device=dev)
+        jlq = torch.empty(KL_ROWS, 2, device=dev)
+        jlp = torch.empty(KL_ROWS, 2, device=dev)
+        jh = torch.empty(KL_ROWS, device=dev)
+        jd = torch.empty_like(JQ[0])
+        js_ms = timed_pair(
+            lambda i: abi.js_forward(JQ[i % 2], JP[i % 2], js=j_o, lse_q=jlq, lse_p=jlp, hq=jh),
+            lambda i: abi.js_vjp(JQ[i % 2], JP[i % 2], jlq, jlp, jh, JG, dq=jd))
+        del JQ, JP, jd
+
     opt_ms = None
     if "opt" in parts and ce_batch is not None:
         y_ign = ce_batch.targets.copy()
@@ -426,8 +460,7 @@ def main():
         if "value" not in out:
             out["value"] = tf
             out["unit"] = "TFLOP/s"
-    # the dominant kernel of the step by time (lce_backward is timed apart from the step)
-    dom = max(rooflines, key=lambda k: rooflines[k]["ms"])
+    step_kernels = list(rooflines)  # ce_forward, ce_vjp, lce_forward: the kernels of the timed step
     if bwd_ms is not None:
         fl = 3 * lce_flops(LCE_N, LCE_D, LCE_V)
         tf = fl / (bwd_ms * 1e-3) / 1e12
@@ -452,6 +485,8 @@ def main():
                                "algorithmic_bytes": byts}
         cfg["kl"] = {"rows": KL_ROWS, "V": KL_V, "dtype": "f32", "scale": 4.0, "timed": "apart"}
     for key, tms, (fb, vb), names, cfgv in (
+            ("js_fwd_vjp", js_ms, js_bytes(KL_ROWS, KL_V, 4), ("js_forward", "js_vjp"),
+             {"rows": KL_ROWS, "V": KL_V, "dtype": "f32", "scale": 4.0, "timed": "apart"}),
             ("ce_options", opt_ms, opt_bytes(CE_ROWS, CE_V, 2), ("ce_forward_ex", "ce_vjp_ex"),
              {"rows": CE_ROWS, "V": CE_V, "dtype": "bf16", "label_smoothing": 0.1, "ignore_index": "every 16th row",
               "reduction": "mean", "timed": "apart"}),
@@ -473,7 +508,12 @@ def main():
     cfg["workload"] = " + ".join(cfg["workload"])
     out["config"] = cfg
     out["parts"] = parts_out
+    # the dominant kernel of the step by time (the parts timed apart count only without a step)
+    pool = step_kernels or list(rooflines)
+    dom = max(pool, key=lambda k: rooflines[k]["ms"])
     out["roofline"] = dict(rooflines[dom], kernel=dom)
+    out.setdefault("value", None)
+    out.setdefault("unit", None)
     out["rooflines"] = rooflines
     if calib:
         out["calibration"] = calib
