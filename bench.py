@@ -49,24 +49,48 @@ CSRC = os.path.join(ROOT, "softmax_cross_entropy_amd", "csrc")
 # and headers at measurement time: a changed kernel reports traffic null until it is measured again.
 TRAFFIC = {
     "ce_forward": {
-        "source_sha": "120aeb018d6702d9",
-        "bytes": 622636909
+        "source_sha": "5909a33a1b8df273",
+        "bytes": 622639540
     },
     "ce_vjp": {
-        "source_sha": "120aeb018d6702d9",
-        "bytes": 1245006280
+        "source_sha": "5909a33a1b8df273",
+        "bytes": 1245005391
     },
     "lce_forward": {
-        "source_sha": "bb8c98d7ddae9d41",
-        "bytes": 15153683711
+        "source_sha": "12d583695e732983",
+        "bytes": 15155788425
     },
     "kl_forward": {
-        "source_sha": "caaaf15903e43c73",
-        "bytes": 622516558
+        "source_sha": "48529b2dec4f5015",
+        "bytes": 622517077
     },
     "kl_vjp": {
-        "source_sha": "caaaf15903e43c73",
-        "bytes": 933640781
+        "source_sha": "48529b2dec4f5015",
+        "bytes": 933641173
+    },
+    "ce_forward_ex": {
+        "source_sha": "cc13f7f9d795ed5e",
+        "bytes": 622633460
+    },
+    "ce_vjp_ex": {
+        "source_sha": "cc13f7f9d795ed5e",
+        "bytes": 1244951377
+    },
+    "ce_forward_probs": {
+        "source_sha": "cc13f7f9d795ed5e",
+        "bytes": 622498070
+    },
+    "ce_vjp_probs": {
+        "source_sha": "cc13f7f9d795ed5e",
+        "bytes": 933606742
+    },
+    "js_forward": {
+        "source_sha": "636dff21e4e490f5",
+        "bytes": 1224835027
+    },
+    "js_vjp": {
+        "source_sha": "636dff21e4e490f5",
+        "bytes": 937528938
     },
 }
 
