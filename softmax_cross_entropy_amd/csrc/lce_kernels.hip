@@ -255,11 +255,15 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
         asm volatile("" ::: "memory");
     };
 
-    // Pipeline: the four K16 steps of a stage each run their 16 MFMAs while the
-    // fragments of the next step are read from LDS; the last step of a stage reads the
-    // first fragments of the next stage, after the stage's single barrier.
+    // Pipeline: the fragments of a K16 step are read from LDS two steps ahead, into four
+    // rotating sets, so each wave keeps twice as many reads in flight (one wave per SIMD
+    // is bound by LDS read latency).  A stage's single barrier sits between its steps 1
+    // and 2: by then every wave has read all four steps of the stage (steps 2 and 3 during
+    // steps 0 and 1), so the DMA of stage kt + 2 can go into its buffer, and stage kt + 1
+    // has landed, so steps 2 and 3 can read the next stage's first two steps.  The DMA
+    // still has four K16 steps to land.
     const int nk = (int)((a.D + BK - 1) / BK);
-    bf16x8 fa0[FB], fb0[FB], fa1[FB], fb1[FB];
+    bf16x8 fa0[FB], fb0[FB], fa1[FB], fb1[FB], fa2[FB], fb2[FB], fa3[FB], fb3[FB];
     // targets of this tile's rows, for the epilogue
     tile_targets[tid] = row0 + tid < a.N ? a.targets[row0 + tid] : -1;
     issue(0, 0);
@@ -270,34 +274,33 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
     asm volatile("" ::: "memory");
     if (nk > 1) issue(1, 1);
     read_frags(0, 0, fa0, fb0);
+    read_frags(0, 1, fa1, fb1);
     for (int kt = 0; kt + 1 < nk; ++kt) {
         const int cur = kt & 1;
-        read_frags(cur, 1, fa1, fb1);
+        read_frags(cur, 2, fa2, fb2);
         mfma_all(fa0, fb0);
         interleave();
-        read_frags(cur, 2, fa0, fb0);
+        read_frags(cur, 3, fa3, fb3);
         mfma_all(fa1, fb1);
-        interleave();
-        read_frags(cur, 3, fa1, fb1);
-        mfma_all(fa0, fb0);
         interleave();
         sync_stage(kt, cur, nk);
         // the last stage re-issues stage nk - 1 into the free buffer, which is never read:
         // no branch around the DMA, so it can interleave with the MFMAs
-        step_with_dma(kt + 2 < nk ? kt + 2 : nk - 1, cur, fa1, fb1, fa0, fb0);
+        step_with_dma(kt + 2 < nk ? kt + 2 : nk - 1, cur, fa2, fb2, fa0, fb0);
+        read_frags(cur ^ 1, 1, fa1, fb1);
+        mfma_all(fa3, fb3);
+        interleave();
     }
     {
         const int cur = (nk - 1) & 1;
-        read_frags(cur, 1, fa1, fb1);
+        read_frags(cur, 2, fa2, fb2);
         mfma_all(fa0, fb0);
         interleave();
-        read_frags(cur, 2, fa0, fb0);
+        read_frags(cur, 3, fa3, fb3);
         mfma_all(fa1, fb1);
         interleave();
-        read_frags(cur, 3, fa1, fb1);
-        mfma_all(fa0, fb0);
-        interleave();
-        mfma_all(fa1, fb1);
+        mfma_all(fa2, fb2);
+        mfma_all(fa3, fb3);
     }
     // the last loop iteration's (redundant) DMA must land before the workgroup can end
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
