@@ -50,47 +50,47 @@ CSRC = os.path.join(ROOT, "softmax_cross_entropy_amd", "csrc")
 TRAFFIC = {
     "ce_forward": {
         "source_sha": "5909a33a1b8df273",
-        "bytes": 622639540
+        "bytes": 622635972
     },
     "ce_vjp": {
         "source_sha": "5909a33a1b8df273",
-        "bytes": 1245005391
+        "bytes": 1245006495
     },
     "lce_forward": {
-        "source_sha": "12d583695e732983",
-        "bytes": 15155788425
+        "source_sha": "cd621515ebc402f8",
+        "bytes": 15154085086
     },
     "kl_forward": {
         "source_sha": "48529b2dec4f5015",
-        "bytes": 622517077
+        "bytes": 622516133
     },
     "kl_vjp": {
         "source_sha": "48529b2dec4f5015",
-        "bytes": 933641173
+        "bytes": 933640229
     },
     "ce_forward_ex": {
         "source_sha": "cc13f7f9d795ed5e",
-        "bytes": 622633460
+        "bytes": 622631908
     },
     "ce_vjp_ex": {
         "source_sha": "cc13f7f9d795ed5e",
-        "bytes": 1244951377
+        "bytes": 1244950304
     },
     "ce_forward_probs": {
         "source_sha": "cc13f7f9d795ed5e",
-        "bytes": 622498070
+        "bytes": 622496390
     },
     "ce_vjp_probs": {
         "source_sha": "cc13f7f9d795ed5e",
-        "bytes": 933606742
+        "bytes": 933605926
     },
     "js_forward": {
         "source_sha": "636dff21e4e490f5",
-        "bytes": 1224835027
+        "bytes": 1225023080
     },
     "js_vjp": {
         "source_sha": "636dff21e4e490f5",
-        "bytes": 937528938
+        "bytes": 937821357
     },
 }
 
