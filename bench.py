@@ -252,8 +252,9 @@ def main():
                          "profile holds a kernel of known traffic")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(rows shard across GPUs with no exchange; see the design notes)", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (rows are "
+              "independent, so each GPU would run the same kernels on its own share of the rows)",
+              file=sys.stderr)
         sys.exit(2)
     parts = set(args.parts.split(","))
 
