@@ -199,8 +199,9 @@ ce_status lce_forward(const void* H, const void* W, const int32_t* targets, int6
 
 /*
  * lce_backward_workspace_size: bytes of device workspace lce_backward needs for
- * (N, D, V): one 8192-column chunk of the logits gradient in bf16 (N * 16 KiB) plus
- * 64 MiB of GEMM scratch.  Returns 0 for arguments lce_backward would reject.
+ * (N, D, V): one 8192-column chunk of the logits gradient in bf16, row-major and
+ * transposed (2 * N * 16 KiB), plus 64 MiB of GEMM scratch.  Returns 0 for arguments
+ * lce_backward would reject.
  */
 size_t lce_backward_workspace_size(int64_t N, int64_t D, int64_t V);
 
@@ -214,8 +215,8 @@ size_t lce_backward_workspace_size(int64_t N, int64_t D, int64_t V);
  * chunk of 8192 vocabulary columns (the page's tile width), the forward's MFMA tile
  * kernel recomputes the chunk of Z and its epilogue writes
  * dZ = g_i (exp((z - m_i) - log s_i) - [col == y_i]) in bf16 (round to nearest even)
- * into the workspace; rocBLAS then adds dZ_c W_c into dH and writes dZ_c^T H into the
- * chunk's rows of dW, both with float32 accumulation.
+ * into the workspace, row-major and transposed; rocBLAS then adds dZ_c W_c into dH and
+ * writes dZ_c^T H into the chunk's rows of dW, both with float32 accumulation.
  *
  *   H, W, targets  as in lce_forward.
  *   lse      float32 [N][2], the (m, log s) pairs lce_forward wrote for the same H, W.

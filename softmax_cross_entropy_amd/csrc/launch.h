@@ -215,8 +215,10 @@ struct LceGradChunk {
     int64_t V;
     int64_t c0;
     int64_t width;
-    void* G;
+    void* G;      // dZ chunk, row-major [N][ldG]
     int64_t ldG;
+    void* GT;     // the same chunk transposed, [width][ldGT]
+    int64_t ldGT;
     hipStream_t stream;
 };
 

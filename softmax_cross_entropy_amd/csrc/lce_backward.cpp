@@ -5,12 +5,15 @@
 // training saves the forward's log-sum-exp and a chunked backward regenerates the
 // logits it needs tile by tile.  Here each chunk of 8192 vocabulary columns (the
 // page's dispatch tile) is one launch of the MFMA tile kernel whose epilogue turns the
-// regenerated logits straight into dZ (bf16, from the saved (m, log s) pair), followed
-// by two plain GEMMs on rocBLAS, accumulated in fp32:
+// regenerated logits straight into dZ (bf16, from the saved (m, log s) pair), written
+// both row-major and transposed, followed by two plain GEMMs on rocBLAS, accumulated
+// in fp32:
 //   dH        += dZ_c  W_c       (N x D, every chunk adds its share)
 //   dW[c0:c1]  = dZ_c^T H        (the chunk's own rows of dW)
-// Everything runs on the caller's stream; the dZ chunk and rocBLAS's scratch live in
-// the caller's workspace.
+// With both layouts neither GEMM reads a transposed operand (rocBLAS's kernel for
+// dZ_c^T H from the row-major chunk ran about 25% slower than the one without).
+// Everything runs on the caller's stream; the two dZ chunks and rocBLAS's scratch live
+// in the caller's workspace.
 #include <hip/hip_runtime.h>
 #include <rocblas/rocblas.h>
 
@@ -57,15 +60,17 @@ rocblas_status handle_for(int dev, void* ws, rocblas_handle* out) {
 size_t lce_backward_workspace_bytes(int64_t N, int64_t D, int64_t V) {
     (void)D;
     (void)V;
-    return align256((size_t)N * kChunk * 2) + kBlasBytes;
+    return 2 * align256((size_t)N * kChunk * 2) + kBlasBytes;
 }
 
 LceBackwardStatus run_lce_backward(const LceBackwardCall& c) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LceBackwardStatus::kHip;
     char* ws = static_cast<char*>(c.workspace);
+    const size_t chunk_bytes = align256((size_t)c.N * kChunk * 2);
     void* G = ws;
-    void* blas_ws = ws + align256((size_t)c.N * kChunk * 2);
+    void* GT = ws + chunk_bytes;
+    void* blas_ws = ws + 2 * chunk_bytes;
     rocblas_handle h = nullptr;
     if (handle_for(dev, blas_ws, &h) != rocblas_status_success) return LceBackwardStatus::kBlas;
     if (rocblas_set_stream(h, c.stream) != rocblas_status_success) return LceBackwardStatus::kBlas;
@@ -76,7 +81,7 @@ LceBackwardStatus run_lce_backward(const LceBackwardCall& c) {
     const rocblas_int n = (rocblas_int)c.N, d = (rocblas_int)c.D, ldg = (rocblas_int)kChunk;
     for (int64_t c0 = 0; c0 < c.V; c0 += kChunk) {
         const int64_t w = c.V - c0 < kChunk ? c.V - c0 : kChunk;
-        LceGradChunk gc{c.H, c.W, c.targets, c.lse, c.g, c.N, c.D, c.V, c0, w, G, kChunk, c.stream};
+        LceGradChunk gc{c.H, c.W, c.targets, c.lse, c.g, c.N, c.D, c.V, c0, w, G, kChunk, GT, c.N, c.stream};
         if (launch_lce_grad_chunk(gc) != hipSuccess) return LceBackwardStatus::kHip;
         // rocBLAS is column-major: a row-major [r][cols] array with leading dimension L
         // is a column-major cols x r matrix with the same L.
@@ -87,9 +92,10 @@ LceBackwardStatus run_lce_backward(const LceBackwardCall& c) {
                             rocblas_datatype_f32_r, d, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0,
                             0) != rocblas_status_success)
             return LceBackwardStatus::kBlas;
-        // dW_c^T (D x w) = H^T (D x N) * dZ_c (N x w), dZ_c stored as the w x N matrix dZ_c^T
-        if (rocblas_gemm_ex(h, rocblas_operation_none, rocblas_operation_transpose, d, (rocblas_int)w, n, &one,
-                            Hb, rocblas_datatype_bf16_r, d, G, rocblas_datatype_bf16_r, ldg, &zero,
+        // dW_c^T (D x w) = H^T (D x N) * dZ_c (N x w), dZ_c being the transposed chunk read
+        // as a column-major N x w matrix
+        if (rocblas_gemm_ex(h, rocblas_operation_none, rocblas_operation_none, d, (rocblas_int)w, n, &one,
+                            Hb, rocblas_datatype_bf16_r, d, GT, rocblas_datatype_bf16_r, n, &zero,
                             c.dW + c0 * c.D, rocblas_datatype_f32_r, d, c.dW + c0 * c.D, rocblas_datatype_f32_r,
                             d, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0) != rocblas_status_success)
             return LceBackwardStatus::kBlas;

@@ -65,6 +65,8 @@ struct TileArgs {
     const float* g;     // [N]
     __bf16* G;          // [N][ldG], column c at c - c0
     int64_t ldG;
+    __bf16* GT;         // the same chunk transposed: [width][ldGT], column c as row c - c0
+    int64_t ldGT;
 };
 
 // LDS layout of one operand stage: 256 rows x 8 chunks of 16 bytes (8 bf16 along K).
@@ -74,7 +76,10 @@ struct TileArgs {
 
 // kGrad = false: the forward epilogue ((m, s) per row per 128-column slab, target logit).
 // kGrad = true: the same tile of Z turned into dZ = g (exp((z - m) - log s) - [col = y])
-// with the saved (m, log s), stored in bf16 (the logits regenerated for the backward).
+// with the saved (m, log s), stored in bf16 (the logits regenerated for the backward),
+// both row-major and transposed: each of the two products of the backward then reads
+// its operand without a transpose.  The 32 lanes of a half-wave hold 32 consecutive
+// rows of each column, so the transposed stores are coalesced too.
 template <bool kGrad>
 __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
     // One LDS object (the compiler then sees the DMA writes and the fragment reads as
@@ -326,6 +331,7 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
             const float nlsl = -l.y * kLog2e;
             const float gr = a.g[row];
             __bf16* grow = a.G + row * a.ldG - a.c0;
+            uint16_t* gcol = reinterpret_cast<uint16_t*>(a.GT) + row;  // (c, row) at gcol[(c - c0) * ldGT]
             auto dz = [&](float z) { return gr * __builtin_amdgcn_exp2f(__builtin_fmaf(z - m, kLog2e, nlsl)); };
 #pragma unroll
             for (int j = 0; j < FB; ++j)
@@ -334,16 +340,25 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
                     const int64_t c = wcol0 + j * 32 + 8 * q + 4 * h2;  // 4 consecutive columns
                     const float v0 = dz(acc[i][j][4 * q]), v1 = dz(acc[i][j][4 * q + 1]);
                     const float v2 = dz(acc[i][j][4 * q + 2]), v3 = dz(acc[i][j][4 * q + 3]);
+                    const int64_t ct = (c - a.c0) * a.ldGT;
                     if (c + 3 < a.c_end) {
                         uint2 w;
                         w.x = Elem<__bf16>::bits2(v0, v1);
                         w.y = Elem<__bf16>::bits2(v2, v3);
                         *reinterpret_cast<uint2*>(grow + c) = w;
+                        gcol[ct] = (uint16_t)w.x;
+                        gcol[ct + a.ldGT] = (uint16_t)(w.x >> 16);
+                        gcol[ct + 2 * a.ldGT] = (uint16_t)w.y;
+                        gcol[ct + 3 * a.ldGT] = (uint16_t)(w.y >> 16);
                     } else {
                         const float v[4] = {v0, v1, v2, v3};
 #pragma unroll
                         for (int t = 0; t < 4; ++t)
-                            if (c + t < a.c_end) grow[c + t] = (__bf16)v[t];
+                            if (c + t < a.c_end) {
+                                const __bf16 b = (__bf16)v[t];
+                                grow[c + t] = b;
+                                gcol[ct + t * a.ldGT] = __builtin_bit_cast(uint16_t, b);
+                            }
                     }
                 }
             // the target column: stored again as g (p - 1) by the lane that stored it
@@ -359,7 +374,9 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
                     const float hi = (jj & 1) ? acc[i][3][e] : acc[i][2][e];
                     z = ee == e ? ((jj & 2) ? hi : lo) : z;
                 }
-                grow[y] = (__bf16)(dz(z) - gr);
+                const __bf16 b = (__bf16)(dz(z) - gr);
+                grow[y] = b;
+                gcol[((int64_t)y - a.c0) * a.ldGT] = __builtin_bit_cast(uint16_t, b);
             }
         }
     } else {
@@ -525,7 +542,8 @@ hipError_t launch_lce_grad_chunk(const LceGradChunk& c) {
     const Geometry g = geometry(c.N, c.width);
     TileArgs a{static_cast<const __bf16*>(c.H), static_cast<const __bf16*>(c.W), c.targets, c.N, c.D, c.V,
                c.c0, c.c0 + c.width, g.n_row_tiles, g.n_col_tiles, g.gr, g.gc, g.n_rg, g.n_sb, 0, nullptr,
-               nullptr, reinterpret_cast<const float2*>(c.lse), c.g, static_cast<__bf16*>(c.G), c.ldG};
+               nullptr, reinterpret_cast<const float2*>(c.lse), c.g, static_cast<__bf16*>(c.G), c.ldG,
+               static_cast<__bf16*>(c.GT), c.ldGT};
     hipLaunchKernelGGL(lce_tile<true>, dim3((unsigned)g.blocks), dim3(kThreads), 0, c.stream, a);
     return hipGetLastError();
 }
