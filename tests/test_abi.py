@@ -135,7 +135,7 @@ def test_lce_rejects_bad_arguments():
     assert lce(ws=ctypes.c_void_p(7 * A + 256)) == ALIAS  # workspace inside W
 
 
-P_DH, P_DW = ctypes.c_void_p(A * 200), ctypes.c_void_p(A * 210)  # clear of the 64.5 MiB workspace
+P_DH, P_DW = ctypes.c_void_p(A * 200), ctypes.c_void_p(A * 210)  # clear of the 65 MiB workspace
 
 
 def lbw(H=P_LOGITS, W=P_W, t=P_T, lse=P_LSE, g=P_G, N=32, D=64, V=1000, dH=P_DH, dW=P_DW, ws=P_WS, wsb=None):
@@ -146,7 +146,7 @@ def lbw(H=P_LOGITS, W=P_W, t=P_T, lse=P_LSE, g=P_G, N=32, D=64, V=1000, dH=P_DH,
 
 def test_lce_backward_rejects_bad_arguments():
     need = abi.lce_backward_workspace_size(32, 64, 1000)
-    assert need == 32 * 8192 * 2 + (64 << 20)
+    assert need == 2 * 32 * 8192 * 2 + (64 << 20)  # dZ chunk, row-major and transposed; GEMM scratch
     assert abi.lce_backward_workspace_size(32, 60, 1000) == 0
     assert abi.lce_backward_workspace_size(1 << 31, 64, 1000) == 0
     assert lbw(D=60) == SHAPE
