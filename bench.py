@@ -57,8 +57,8 @@ TRAFFIC = {
         "bytes": 1245006495
     },
     "lce_forward": {
-        "source_sha": "cd621515ebc402f8",
-        "bytes": 15154085086
+        "source_sha": "8cc9189b31607a6b",
+        "bytes": 15154570106
     },
     "kl_forward": {
         "source_sha": "48529b2dec4f5015",
