@@ -393,7 +393,7 @@ ce_status ce_forward_ex(const void* logits, ce_layout in, ce_dtype dt, const int
  *           gradient of the total, for a sum or mean.
  *   count   int64 [1] as ce_forward_ex wrote it; read for CE_REDUCE_MEAN (g / count per
  *           row), otherwise may be NULL.
- *   The rest as in ce_vjp.  Ignored rows get dlogits 0.
+ *   The rest as in ce_vjp.  Ignored rows get dlogits 0; their logits are not read.
  */
 ce_status ce_vjp_ex(const void* logits, ce_layout in, ce_dtype dt, const int32_t* targets, const float* lse,
                     const float* g, int64_t n_rows, int64_t V, ce_options opt, const int64_t* count, void* dlogits,

@@ -364,8 +364,10 @@ struct OVjpArgs {
 struct ORow {
     float m;    // row max, NaN for an invalid index target
     float lsl;  // log s * log2(e)
-    float g;    // upstream gradient of this row, 0 on an ignored row
-    float W;    // sum of the weights (probability targets)
+    float g;    // upstream gradient of this row
+    float gW;   // g W (probability targets)
+    float gk;   // g (1 - eps) (probability targets)
+    float ge;   // g eps / V, 0 when eps is 0
     float cy;   // target weight (1 - eps) + eps / V (index targets)
     int32_t y;
     int32_t zero;  // ignored row: the gradient is 0 whatever the logits hold
@@ -386,12 +388,15 @@ __device__ __forceinline__ ORow load_orow(const OVjpArgs& a, int64_t r, float gs
     o.lsl = l.y * kLog2e;
     o.g = a.reduction == 0 ? a.g[r] : gs;
     o.cy = a.keep + a.eps_v;
+    // eps = 0 leaves g p - 0 = g p, bit for bit, even for an infinite g
+    o.ge = a.eps_v == 0.f ? 0.f : o.g * a.eps_v;
+    o.gk = o.g * a.keep;
     o.zero = 0;
-    o.W = 0.f;
+    o.gW = 0.f;
     o.y = -1;
     if constexpr (kProbs) {
         o.m = l.x;
-        o.W = a.wsum[r];
+        o.gW = o.g * a.wsum[r];
     } else {
         o.y = a.y[r];
         o.zero = a.has_ignore && o.y == a.ignore_index;
@@ -404,17 +409,16 @@ __device__ __forceinline__ float oprob(float z, const ORow& o) {
     return __builtin_amdgcn_exp2f(__builtin_fmaf(z - o.m, kLog2e, -o.lsl));
 }
 
-// Gradient of one element: index targets g (p - eps / V) off the target; probability
-// targets g (W p - w).  An ignored row gives 0.
+// Gradient of one element, with g folded into the per-row constants: index targets
+// g p - g eps / V off the target; probability targets g W p - (g (1 - eps) t + g eps / V).
+// Ignored rows never come here: their work items store zeros without reading the logits.
 template <bool kProbs>
-__device__ __forceinline__ float ograd(float z, float t, const ORow& o, const OVjpArgs& a) {
+__device__ __forceinline__ float ograd(float z, float t, const ORow& o) {
     const float p = oprob(z, o);
-    float v;
     if constexpr (kProbs)
-        v = o.g * (o.W * p - __builtin_fmaf(a.keep, t, a.eps_v));
+        return __builtin_fmaf(o.gW, p, -__builtin_fmaf(o.gk, t, o.ge));
     else
-        v = o.g * (p - a.eps_v);
-    return o.zero ? 0.f : v;
+        return __builtin_fmaf(o.g, p, -o.ge);
 }
 
 // One 16-byte vector of gradients.  Index targets: the one lane whose vector holds the
@@ -423,14 +427,14 @@ __device__ __forceinline__ float ograd(float z, float t, const ORow& o, const OV
 // select chain: an indexed read of the vector would make the compiler stage every
 // vector through LDS.
 template <typename T, bool kProbs>
-__device__ __forceinline__ void ovec(const U4& bz, const U4& bt, const ORow& o, const OVjpArgs& a, int64_t first,
+__device__ __forceinline__ void ovec(const U4& bz, const U4& bt, const ORow& o, int64_t first,
                                      char* dst, T* drow) {
     constexpr int kVec = Elem<T>::kVec;
     float fz[kVec], ft[kVec], out[kVec];
     Elem<T>::unpack(bz, fz);
     if constexpr (kProbs) Elem<T>::unpack(bt, ft);
 #pragma unroll
-    for (int k = 0; k < kVec; ++k) out[k] = ograd<kProbs>(fz[k], kProbs ? ft[k] : 0.f, o, a);
+    for (int k = 0; k < kVec; ++k) out[k] = ograd<kProbs>(fz[k], kProbs ? ft[k] : 0.f, o);
     store_u4(dst, Elem<T>::pack(out));
     if constexpr (!kProbs) {
         const int64_t rel = (int64_t)o.y - first;
@@ -440,22 +444,35 @@ __device__ __forceinline__ void ovec(const U4& bz, const U4& bt, const ORow& o, 
 #pragma unroll
             for (int k = 0; k < kVec; ++k) bits |= (r == (uint32_t)k ? 0xffffffffu : 0u) & __float_as_uint(fz[k]);
             const float zy = __uint_as_float(bits);
-            Elem<T>::store1(drow + o.y, o.zero ? 0.f : o.g * (oprob(zy, o) - o.cy));
+            Elem<T>::store1(drow + o.y, o.g * (oprob(zy, o) - o.cy));
         }
     }
 }
 
 template <typename T, bool kProbs>
-__device__ __forceinline__ void oscalar(const T* z, const T* t, T* d, int64_t i, const ORow& o, const OVjpArgs& a) {
+__device__ __forceinline__ void oscalar(const T* z, const T* t, T* d, int64_t i, const ORow& o) {
     const float zi = Elem<T>::load1(z + i);
     float v;
     if constexpr (kProbs) {
-        v = ograd<true>(zi, Elem<T>::load1(t + i), o, a);
+        v = ograd<true>(zi, Elem<T>::load1(t + i), o);
     } else {
-        v = ograd<false>(zi, 0.f, o, a);
-        if (i == (int64_t)o.y && !o.zero) v = o.g * (oprob(zi, o) - o.cy);
+        v = ograd<false>(zi, 0.f, o);
+        if (i == (int64_t)o.y) v = o.g * (oprob(zi, o) - o.cy);
     }
     Elem<T>::store1(d + i, v);
+}
+
+// Zeros over elements [e0, e1) of an ignored row's gradient, in 16-byte stores where
+// the row allows, by threads tid, tid + nthr, ...
+template <typename T>
+__device__ __forceinline__ void ozero(T* d, int64_t e0, int64_t e1, int tid, int nthr) {
+    if (e0 >= e1) return;
+    RowSplit<T> sp(d + e0, e1 - e0);
+    char* vb = reinterpret_cast<char*>(d + e0 + sp.head);
+    const U4 zero{};
+    for (int64_t j = tid; j < sp.nvec; j += nthr) store_u4(vb + j * 16, zero);
+    const int64_t ns = sp.n_scalar(e1 - e0);
+    for (int64_t k = tid; k < ns; k += nthr) Elem<T>::store1(d + e0 + sp.scalar_index(k), 0.f);
 }
 
 template <typename T, bool kProbs>
@@ -479,7 +496,9 @@ __global__ __launch_bounds__(G > kBlock ? G : kBlock) void ceo_vjp_lanes(OVjpArg
         const T* t = kProbs ? static_cast<const T*>(a.t) + row_offset(r, a.tl) : nullptr;
         T* d = static_cast<T*>(a.d) + row_offset(r, a.dl);
         const ORow o = load_orow<kProbs>(a, r, gs);
-        if (ophases<T, kProbs>(z, t, d)) {
+        if (o.zero) {
+            ozero(d, 0, a.V, lane, G);
+        } else if (ophases<T, kProbs>(z, t, d)) {
             RowSplit<T> sp(z, a.V);
             const char* zb = reinterpret_cast<const char*>(z + sp.head);
             const char* tb = kProbs ? reinterpret_cast<const char*>(t + sp.head) : nullptr;
@@ -495,18 +514,18 @@ __global__ __launch_bounds__(G > kBlock ? G : kBlock) void ceo_vjp_lanes(OVjpArg
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int64_t v = j + (int64_t)u * G;
-                    ovec<T, kProbs>(bz[u], bt[u], o, a, sp.head + v * kVec, db + v * 16, d);
+                    ovec<T, kProbs>(bz[u], bt[u], o, sp.head + v * kVec, db + v * 16, d);
                 }
             }
             for (; j < sp.nvec; j += G) {
                 U4 bt{};
                 if constexpr (kProbs) bt = load_u4_stream(tb + j * 16);
-                ovec<T, kProbs>(load_u4_stream(zb + j * 16), bt, o, a, sp.head + j * kVec, db + j * 16, d);
+                ovec<T, kProbs>(load_u4_stream(zb + j * 16), bt, o, sp.head + j * kVec, db + j * 16, d);
             }
             const int64_t ns = sp.n_scalar(a.V);
-            for (int64_t k = lane; k < ns; k += G) oscalar<T, kProbs>(z, t, d, sp.scalar_index(k), o, a);
+            for (int64_t k = lane; k < ns; k += G) oscalar<T, kProbs>(z, t, d, sp.scalar_index(k), o);
         } else {
-            for (int64_t i = lane; i < a.V; i += G) oscalar<T, kProbs>(z, t, d, i, o, a);
+            for (int64_t i = lane; i < a.V; i += G) oscalar<T, kProbs>(z, t, d, i, o);
         }
     }
 }
@@ -525,7 +544,11 @@ __global__ __launch_bounds__(kBlock) void ceo_vjp_chunks(OVjpArgs a, int64_t chu
         const T* t = kProbs ? static_cast<const T*>(a.t) + row_offset(r, a.tl) : nullptr;
         T* d = static_cast<T*>(a.d) + row_offset(r, a.dl);
         const ORow o = load_orow<kProbs>(a, r, gs);
-        if (ophases<T, kProbs>(z, t, d)) {
+        if (o.zero) {
+            // the same element ranges as the path for rows in different 16-byte phases
+            const int64_t e0 = c * kChunkVec * kVec;
+            ozero(d, e0, e0 + kChunkVec * kVec < a.V ? e0 + kChunkVec * kVec : a.V, tid, kBlock);
+        } else if (ophases<T, kProbs>(z, t, d)) {
             RowSplit<T> sp(z, a.V);
             const char* zb = reinterpret_cast<const char*>(z + sp.head);
             const char* tb = kProbs ? reinterpret_cast<const char*>(t + sp.head) : nullptr;
@@ -541,23 +564,23 @@ __global__ __launch_bounds__(kBlock) void ceo_vjp_chunks(OVjpArgs a, int64_t chu
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int64_t v = v0 + (int64_t)u * kBlock;
-                    ovec<T, kProbs>(bz[u], bt[u], o, a, sp.head + v * kVec, db + v * 16, d);
+                    ovec<T, kProbs>(bz[u], bt[u], o, sp.head + v * kVec, db + v * 16, d);
                 }
             } else {
                 for (int64_t j = v0; j < sp.nvec; j += kBlock) {
                     U4 bt{};
                     if constexpr (kProbs) bt = load_u4_stream(tb + j * 16);
-                    ovec<T, kProbs>(load_u4_stream(zb + j * 16), bt, o, a, sp.head + j * kVec, db + j * 16, d);
+                    ovec<T, kProbs>(load_u4_stream(zb + j * 16), bt, o, sp.head + j * kVec, db + j * 16, d);
                 }
             }
             if (c == 0) {
                 const int64_t ns = sp.n_scalar(a.V);
-                for (int64_t k = tid; k < ns; k += kBlock) oscalar<T, kProbs>(z, t, d, sp.scalar_index(k), o, a);
+                for (int64_t k = tid; k < ns; k += kBlock) oscalar<T, kProbs>(z, t, d, sp.scalar_index(k), o);
             }
         } else {
             const int64_t e0 = c * kChunkVec * kVec;
             const int64_t e1 = e0 + kChunkVec * kVec < a.V ? e0 + kChunkVec * kVec : a.V;
-            for (int64_t i = e0 + tid; i < e1; i += kBlock) oscalar<T, kProbs>(z, t, d, i, o, a);
+            for (int64_t i = e0 + tid; i < e1; i += kBlock) oscalar<T, kProbs>(z, t, d, i, o);
         }
     }
 }
