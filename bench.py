@@ -141,12 +141,14 @@ def js_bytes(rows, V, e):
     return rows * (4 * V * e + 24), rows * (3 * V * e + 24)
 
 
-def opt_bytes(rows, V, e):
+def opt_bytes(rows, V, e, ignored=0):
     """Algorithmic HBM bytes per call of the index-target options (smoothing, ignore_index,
     mean): the forward reads the logits and the target and writes loss and lse (16 per
-    row); the VJP reads the logits, lse and target (12) and writes the gradient.  The
-    reduction's second read of loss and targets is not counted."""
-    return rows * (V * e + 16), rows * (2 * V * e + 12)
+    row; ignored rows too, whose lse is still written); the VJP reads lse and target (12)
+    and writes the gradient of every row, and reads the logits of the rows that are not
+    ignored (an ignored row's gradient is 0 whatever its logits).  The reduction's second
+    read of loss and targets is not counted."""
+    return rows * (V * e + 16), rows * (V * e + 12) + (rows - ignored) * V * e
 
 
 def probs_bytes(rows, V, e):
@@ -209,7 +211,7 @@ def cpu_baseline(ce_batch, lce_inputs, lce_rows=32):
     oco.forward_index(z, y_ign, 0.1, -100, "mean")
     oco.grad_index(z, y_ign, 1.0, 0.1, -100, "mean")
     opt_s = time.perf_counter() - t0
-    of_b, ov_b = opt_bytes(32, b.V, 2)
+    of_b, ov_b = opt_bytes(32, b.V, 2, ignored=len(range(0, 32, 16)))
     blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     return {
         "value": (fwd_b + vjp_b) / ce_s / 1e9,
@@ -330,6 +332,48 @@ def main():
     def ms(a, b):
         return [ev[i][a].elapsed_time(ev[i][b]) for i in range(K)]
 
+    # The MI355X's 256 MB Infinity Cache sits in front of HBM.  A VJP's gradient writes
+    # stay there as dirty lines after the kernel ends, so the next streaming kernel first
+    # writes them back.  In the step, lce_forward's reads (15 GB through the cache) do that
+    # between one step's VJP and the next step's forward.  Each pair below is timed in two
+    # states: 'clean', after a 512 MiB read (outside the timed region) leaves the cache
+    # holding clean lines, as in the step; and 'back to back', pairs with nothing between,
+    # where every call also writes back the previous call's lines: the steady rate HBM
+    # sustains for this kernel alone.
+    CLEAN = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    clean_out = torch.empty((), dtype=torch.float32, device=dev)
+
+    def clean_cache():
+        torch.sum(CLEAN, dim=0, out=clean_out)
+
+    def timed_pair(fwd, vjp, reps=K, pre=None):
+        for i in range(3):
+            if pre:
+                pre()
+            fwd(i)
+            vjp(i)
+        torch.cuda.synchronize()
+        pev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+        for i in range(reps):
+            if pre:
+                pre()
+            pev[i][0].record(stream)
+            fwd(i)
+            pev[i][1].record(stream)
+            vjp(i)
+            pev[i][2].record(stream)
+        torch.cuda.synchronize()
+        return (float(np.mean([e[0].elapsed_time(e[1]) for e in pev])),
+                float(np.mean([e[1].elapsed_time(e[2]) for e in pev])))
+
+    def both_states(fwd, vjp):
+        return {"clean": timed_pair(fwd, vjp, pre=clean_cache), "back_to_back": timed_pair(fwd, vjp)}
+
+    ce_b2b = None
+    if ce_batch is not None:
+        ce_b2b = timed_pair(lambda i: abi.ce_forward(X[i % 2], T, loss=loss, lse=lse),
+                            lambda i: abi.ce_vjp(X[i % 2], T, lse, G, dlogits=dX))
+
     kl_ms = None
     if "kl" in parts:
         kq, kp, kg = inputs.kl_pair(KL_ROWS, KL_V, "f32", scale=4.0)
@@ -341,37 +385,9 @@ def main():
         lq_o = torch.empty(KL_ROWS, 2, device=dev)
         lp_o = torch.empty(KL_ROWS, 2, device=dev)
         dq_o = torch.empty_like(KQ[0])
-        for i in range(3):
-            abi.kl_forward(KQ[i % 2], KP[i % 2], kl=kl_o, lse_q=lq_o, lse_p=lp_o)
-            abi.kl_vjp(KQ[i % 2], KP[i % 2], lq_o, lp_o, KG, dq=dq_o)
-        torch.cuda.synchronize()
-        kev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-        for i in range(K):
-            kev[i][0].record(stream)
-            abi.kl_forward(KQ[i % 2], KP[i % 2], kl=kl_o, lse_q=lq_o, lse_p=lp_o)
-            kev[i][1].record(stream)
-            abi.kl_vjp(KQ[i % 2], KP[i % 2], lq_o, lp_o, KG, dq=dq_o)
-            kev[i][2].record(stream)
-        torch.cuda.synchronize()
-        kl_ms = (float(np.mean([e[0].elapsed_time(e[1]) for e in kev])),
-                 float(np.mean([e[1].elapsed_time(e[2]) for e in kev])))
+        kl_ms = both_states(lambda i: abi.kl_forward(KQ[i % 2], KP[i % 2], kl=kl_o, lse_q=lq_o, lse_p=lp_o),
+                            lambda i: abi.kl_vjp(KQ[i % 2], KP[i % 2], lq_o, lp_o, KG, dq=dq_o))
         del KQ, KP, dq_o
-
-    def timed_pair(fwd, vjp, reps=K):
-        for i in range(3):
-            fwd(i)
-            vjp(i)
-        torch.cuda.synchronize()
-        pev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
-        for i in range(reps):
-            pev[i][0].record(stream)
-            fwd(i)
-            pev[i][1].record(stream)
-            vjp(i)
-            pev[i][2].record(stream)
-        torch.cuda.synchronize()
-        return (float(np.mean([e[0].elapsed_time(e[1]) for e in pev])),
-                float(np.mean([e[1].elapsed_time(e[2]) for e in pev])))
 
     js_ms = None
     if "js" in parts:
@@ -385,7 +401,7 @@ def main():
         jlp = torch.empty(KL_ROWS, 2, device=dev)
         jh = torch.empty(KL_ROWS, device=dev)
         jd = torch.empty_like(JQ[0])
-        js_ms = timed_pair(
+        js_ms = both_states(
             lambda i: abi.js_forward(JQ[i % 2], JP[i % 2], js=j_o, lse_q=jlq, lse_p=jlp, hq=jh),
             lambda i: abi.js_vjp(JQ[i % 2], JP[i % 2], jlq, jlp, jh, JG, dq=jd))
         del JQ, JP, jd
@@ -399,7 +415,7 @@ def main():
         o_cnt = torch.empty(1, dtype=torch.int64, device=dev)
         o_ws = torch.empty(abi.ce_reduce_workspace_size(), dtype=torch.uint8, device=dev)
         o_g = torch.ones(1, device=dev)
-        opt_ms = timed_pair(
+        opt_ms = both_states(
             lambda i: abi.ce_forward_ex(X[i % 2], TI, 0.1, -100, "mean", loss=loss, lse=lse, total=o_tot,
                                         count=o_cnt, workspace=o_ws),
             lambda i: abi.ce_vjp_ex(X[i % 2], TI, lse, o_g, 0.1, -100, "mean", count=o_cnt, dlogits=dX))
@@ -417,7 +433,7 @@ def main():
         p_ws = torch.empty(abi.ce_reduce_workspace_size(), dtype=torch.uint8, device=dev)
         p_g = torch.ones(1, device=dev)
         p_d = torch.empty_like(PZ)
-        probs_ms = timed_pair(
+        probs_ms = both_states(
             lambda i: abi.ce_forward_probs(PZ, PT, 0.1, "mean", loss=p_loss, lse=p_lse, wsum=p_w, total=p_tot,
                                            count=p_cnt, workspace=p_ws),
             lambda i: abi.ce_vjp_probs(PZ, PT, p_lse, p_w, p_g, 0.1, "mean", count=p_cnt, dlogits=p_d))
@@ -450,21 +466,33 @@ def main():
     cfg = {"workload": []}
     parts_out = {}
     rooflines = {}
+    def rate(byts, t):
+        return byts / (t * 1e-3) / 1e9
+
+    def b2b_out(fb, vb, f, v):
+        return {"fwd_ms": f, "vjp_ms": v, "ms": f + v, "GB_s": rate(fb + vb, f + v),
+                "frac_hbm_peak": rate(fb + vb, f + v) / HBM_PEAK_GBS}
+
+    def hbm_rooflines(names, byts, b2b, other, other_key):
+        # the back-to-back time: the rate HBM sustains, deferred cache write-backs included
+        for name, nb, t, t2 in zip(names, byts, b2b, other):
+            a = rate(nb, t)
+            rooflines[name] = {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": a / HBM_PEAK_GBS, "traffic": traffic_for(name), "ms": t,
+                               "timing": "back to back", other_key: t2, "algorithmic_bytes": nb}
+
     if ce_batch is not None:
         fwd_b, vjp_b = ce_bytes(CE_ROWS, CE_V, 2)
         f_ms = float(np.mean(ms(0, 1)))
         v_ms = float(np.mean(ms(1, 2)))
         fv_ms = float(np.mean(ms(0, 2)))
-        gbs = (fwd_b + vjp_b) / (fv_ms * 1e-3) / 1e9
+        gbs = rate(fwd_b + vjp_b, fv_ms)
         parts_out["ce_fwd_vjp"] = {"ms": fv_ms, "GB_s": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS,
                                    "algorithmic_bytes": fwd_b + vjp_b,
-                                   "fwd_ms": f_ms, "fwd_GB_s": fwd_b / (f_ms * 1e-3) / 1e9,
-                                   "vjp_ms": v_ms, "vjp_GB_s": vjp_b / (v_ms * 1e-3) / 1e9}
-        for name, byts, t in (("ce_forward", fwd_b, f_ms), ("ce_vjp", vjp_b, v_ms)):
-            a = byts / (t * 1e-3) / 1e9
-            rooflines[name] = {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                               "frac": a / HBM_PEAK_GBS, "traffic": traffic_for(name), "ms": t,
-                               "algorithmic_bytes": byts}
+                                   "fwd_ms": f_ms, "fwd_GB_s": rate(fwd_b, f_ms),
+                                   "vjp_ms": v_ms, "vjp_GB_s": rate(vjp_b, v_ms),
+                                   "back_to_back": b2b_out(fwd_b, vjp_b, *ce_b2b)}
+        hbm_rooflines(("ce_forward", "ce_vjp"), (fwd_b, vjp_b), ce_b2b, (f_ms, v_ms), "ms_in_step")
         cfg["workload"].append(f"ce_forward+ce_vjp bf16 [{CE_ROWS} x {CE_V}]")
         cfg["ce"] = {"rows": CE_ROWS, "V": CE_V, "dtype": "bf16"}
         out["value"] = gbs
@@ -497,22 +525,13 @@ def main():
                                      "kernels": "per 8192-column chunk: lce_tile (dZ epilogue) + two rocBLAS "
                                                 "GEMMs (one lce_backward call)"}
         cfg["lce_backward"] = {"N": LCE_N, "D": LCE_D, "V": LCE_V, "out": "fp32 dH, dW", "timed": "apart"}
-    if kl_ms is not None:
-        kf_b, kv_b = kl_bytes(KL_ROWS, KL_V, 4)
-        kf, kv = kl_ms
-        parts_out["kl_fwd_vjp"] = {"ms": kf + kv, "GB_s": (kf_b + kv_b) / ((kf + kv) * 1e-3) / 1e9,
-                                   "frac_hbm_peak": (kf_b + kv_b) / ((kf + kv) * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                   "algorithmic_bytes": kf_b + kv_b, "fwd_ms": kf, "vjp_ms": kv, "in_step": False}
-        for name, byts, t in (("kl_forward", kf_b, kf), ("kl_vjp", kv_b, kv)):
-            a = byts / (t * 1e-3) / 1e9
-            rooflines[name] = {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                               "frac": a / HBM_PEAK_GBS, "traffic": traffic_for(name), "ms": t,
-                               "algorithmic_bytes": byts}
-        cfg["kl"] = {"rows": KL_ROWS, "V": KL_V, "dtype": "f32", "scale": 4.0, "timed": "apart"}
     for key, tms, (fb, vb), names, cfgv in (
+            ("kl_fwd_vjp", kl_ms, kl_bytes(KL_ROWS, KL_V, 4), ("kl_forward", "kl_vjp"),
+             {"rows": KL_ROWS, "V": KL_V, "dtype": "f32", "scale": 4.0, "timed": "apart"}),
             ("js_fwd_vjp", js_ms, js_bytes(KL_ROWS, KL_V, 4), ("js_forward", "js_vjp"),
              {"rows": KL_ROWS, "V": KL_V, "dtype": "f32", "scale": 4.0, "timed": "apart"}),
-            ("ce_options", opt_ms, opt_bytes(CE_ROWS, CE_V, 2), ("ce_forward_ex", "ce_vjp_ex"),
+            ("ce_options", opt_ms, opt_bytes(CE_ROWS, CE_V, 2, ignored=len(range(0, CE_ROWS, 16))),
+             ("ce_forward_ex", "ce_vjp_ex"),
              {"rows": CE_ROWS, "V": CE_V, "dtype": "bf16", "label_smoothing": 0.1, "ignore_index": "every 16th row",
               "reduction": "mean", "timed": "apart"}),
             ("ce_probs", probs_ms, probs_bytes(KL_ROWS, KL_V, 4), ("ce_forward_probs", "ce_vjp_probs"),
@@ -520,17 +539,18 @@ def main():
               "label_smoothing": 0.1, "reduction": "mean", "timed": "apart"})):
         if tms is None:
             continue
-        f, v = tms
-        parts_out[key] = {"ms": f + v, "GB_s": (fb + vb) / ((f + v) * 1e-3) / 1e9,
-                          "frac_hbm_peak": (fb + vb) / ((f + v) * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                          "algorithmic_bytes": fb + vb, "fwd_ms": f, "vjp_ms": v, "in_step": False}
-        for name, byts, t in ((names[0], fb, f), (names[1], vb, v)):
-            a = byts / (t * 1e-3) / 1e9
-            rooflines[name] = {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                               "frac": a / HBM_PEAK_GBS, "traffic": traffic_for(name), "ms": t,
-                               "algorithmic_bytes": byts}
+        f, v = tms["clean"]
+        parts_out[key] = {"ms": f + v, "GB_s": rate(fb + vb, f + v),
+                          "frac_hbm_peak": rate(fb + vb, f + v) / HBM_PEAK_GBS,
+                          "algorithmic_bytes": fb + vb, "fwd_ms": f, "vjp_ms": v, "in_step": False,
+                          "cache": "clean", "back_to_back": b2b_out(fb, vb, *tms["back_to_back"])}
+        hbm_rooflines(names, (fb, vb), tms["back_to_back"], (f, v), "ms_clean_cache")
         cfg[key] = cfgv
     cfg["workload"] = " + ".join(cfg["workload"])
+    cfg["timing"] = ("CE parts: inside the step (after the previous step's lce_forward); parts timed apart: each "
+                     "fwd+VJP pair after a 512 MiB read that leaves the Infinity Cache clean, as in the step, "
+                     "and again back to back (each call also writes back the previous call's cached "
+                     "gradient lines); HBM rooflines: the back-to-back times")
     out["config"] = cfg
     out["parts"] = parts_out
     # the dominant kernel of the step by time (the parts timed apart count only without a step)
