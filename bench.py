@@ -245,9 +245,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--parts", default="ce,lce,lbw,kl,js,opt,probs",
+    ap.add_argument("--parts", default="ce,lce,lbw,kl,js,opt,probs,shapes",
                     help="comma list of ce, lce, lbw (lce_backward), kl (kl_forward + kl_vjp), js (js_forward + "
-                         "js_vjp), opt (ce_forward_ex + ce_vjp_ex), probs (ce_forward_probs + ce_vjp_probs)")
+                         "js_vjp), opt (ce_forward_ex + ce_vjp_ex), probs (ce_forward_probs + ce_vjp_probs), "
+                         "shapes (ce_forward + ce_vjp at the small-vocabulary, strided and huge-row shapes)")
     ap.add_argument("--bwd-steps", type=int, default=5, help="timed lce_backward calls")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run one elementwise copy (torch.neg) of MIB MiB fp32 first, so a counter "
@@ -259,6 +260,10 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     parts = set(args.parts.split(","))
+
+    def note(msg):
+        # progress on stderr; stdout carries the one JSON line
+        print(f"bench: {msg}", file=sys.stderr, flush=True)
 
     import torch
 
@@ -376,6 +381,7 @@ def main():
 
     kl_ms = None
     if "kl" in parts:
+        note("kl")
         kq, kp, kg = inputs.kl_pair(KL_ROWS, KL_V, "f32", scale=4.0)
         kq2, kp2, _ = inputs.kl_pair(KL_ROWS, KL_V, "f32", scale=4.0, stream=1)
         KQ = [torch.from_numpy(kq).to(dev), torch.from_numpy(kq2).to(dev)]
@@ -391,6 +397,7 @@ def main():
 
     js_ms = None
     if "js" in parts:
+        note("js")
         jq, jp, jg = inputs.kl_pair(KL_ROWS, KL_V, "f32", scale=4.0, stream=4)
         jq2, jp2, _ = inputs.kl_pair(KL_ROWS, KL_V, "f32", scale=4.0, stream=5)
         JQ = [torch.from_numpy(jq).to(dev), torch.from_numpy(jq2).to(dev)]
@@ -408,6 +415,7 @@ def main():
 
     opt_ms = None
     if "opt" in parts and ce_batch is not None:
+        note("opt")
         y_ign = ce_batch.targets.copy()
         y_ign[::16] = -100
         TI = up(y_ign)
@@ -422,6 +430,7 @@ def main():
 
     probs_ms = None
     if "probs" in parts:
+        note("probs")
         pz = inputs.kl_pair(KL_ROWS, KL_V, "f32", scale=4.0, stream=2)[0]
         PZ = torch.from_numpy(pz).to(dev)
         PT = torch.from_numpy(inputs.prob_targets(KL_ROWS, KL_V, "f32", workload=20, stream=3)).to(dev)
@@ -439,8 +448,56 @@ def main():
             lambda i: abi.ce_vjp_probs(PZ, PT, p_lse, p_w, p_g, 0.1, "mean", count=p_cnt, dlogits=p_d))
         del PZ, PT, p_d
 
+    # ce_forward + ce_vjp at the other workload shapes: the small-vocabulary layouts (one
+    # lane per row for 8 classes, lane groups for 1024), the strided batch view and the
+    # row count past 2**32 threads.  Each shape rotates copies of its input, at least
+    # 1 GiB in all, so no input is read again from the 256 MB Infinity Cache.
+    shape_ms = []
+    if "shapes" in parts:
+        def dev_copy(a, dt):
+            t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if dt == "bf16" else a)
+            return (t.view(torch.bfloat16) if dt == "bf16" else t).to(dev)
+
+        def strided():
+            x3, y3 = inputs.strided_view_source()
+            return x3, "f32", (lambda t: t[:, :-1]), inputs.shifted_targets(y3)
+
+        def plain(make):
+            def build():
+                b = make()
+                return b.logits, b.dtype, (lambda t: t), b.targets
+            return build
+
+        shape_list = (
+            ("f32 [1048576 x 8]", plain(inputs.small_v_rows)),
+            ("f32 [65536 x 1024] offsets and -inf rows", plain(lambda: inputs.numerics_stress("f32"))),
+            ("f16 [65536 x 1024] offsets and -inf rows", plain(lambda: inputs.numerics_stress("f16"))),
+            ("f32 view [10, 119, 32768][:, :-1] (1180 rows)", strided),
+            ("bf16 [8192 x 32000]", plain(lambda: inputs.large_vocab(8192, 32000))),
+            ("f32 [135266304 x 8]", plain(inputs.huge_rows)),
+        )
+        for label, build in shape_list:
+            note(f"shapes: {label}")
+            store, dt, view_of, tgt = build()
+            ncopy = max(1, -(-(1 << 30) // store.nbytes))
+            views = [view_of(dev_copy(store, dt)) for _ in range(ncopy)]
+            v0 = views[0]
+            n_rows, V = v0.numel() // v0.shape[-1], v0.shape[-1]
+            del store
+            ST = torch.from_numpy(tgt).to(dev)
+            SG = torch.ones(n_rows, device=dev)
+            s_loss = torch.empty(n_rows, device=dev)
+            s_lse = torch.empty(n_rows, 2, device=dev)
+            s_d = torch.empty(v0.shape, dtype=v0.dtype, device=dev)
+            tms = both_states(lambda i: abi.ce_forward(views[i % ncopy], ST, loss=s_loss, lse=s_lse),
+                              lambda i: abi.ce_vjp(views[i % ncopy], ST, s_lse, SG, dlogits=s_d))
+            shape_ms.append((label, n_rows, V, v0.element_size(), ncopy, tms))
+            del views, v0, ST, SG, s_loss, s_lse, s_d
+            torch.cuda.empty_cache()
+
     bwd_ms = None
     if "lbw" in parts and lce_in is not None:
+        note("lbw")
         G_up = torch.from_numpy(np.random.default_rng([5, 0]).uniform(0.25, 2.0, LCE_N).astype(np.float32)).to(dev)
         dH = torch.empty(LCE_N, LCE_D, dtype=torch.float32, device=dev)
         dW = torch.empty(LCE_V, LCE_D, dtype=torch.float32, device=dev)
@@ -546,6 +603,24 @@ def main():
                           "cache": "clean", "back_to_back": b2b_out(fb, vb, *tms["back_to_back"])}
         hbm_rooflines(names, (fb, vb), tms["back_to_back"], (f, v), "ms_clean_cache")
         cfg[key] = cfgv
+    if shape_ms:
+        shapes_out = {}
+        for label, n_rows, V, e, ncopy, tms in shape_ms:
+            fb, vb = ce_bytes(n_rows, V, e)
+            f, v = tms["clean"]
+            shapes_out[label] = {"rows": n_rows, "V": V, "ms": f + v, "GB_s": rate(fb + vb, f + v),
+                                 "frac_hbm_peak": rate(fb + vb, f + v) / HBM_PEAK_GBS,
+                                 "algorithmic_bytes": fb + vb, "fwd_ms": f, "vjp_ms": v, "input_copies": ncopy,
+                                 "cache": "clean", "back_to_back": b2b_out(fb, vb, *tms["back_to_back"])}
+            for name, nb, t, t2 in (("ce_forward", fb, tms["back_to_back"][0], f),
+                                    ("ce_vjp", vb, tms["back_to_back"][1], v)):
+                a = rate(nb, t)
+                rooflines[f"{name} {label}"] = {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS,
+                                                "unit": "GB/s", "frac": a / HBM_PEAK_GBS, "traffic": None,
+                                                "ms": t, "timing": "back to back", "ms_clean_cache": t2,
+                                                "algorithmic_bytes": nb}
+        parts_out["shapes"] = shapes_out
+        cfg["shapes"] = {"timed": "apart", "g": 1.0, "shapes": [x[0] for x in shape_ms]}
     cfg["workload"] = " + ".join(cfg["workload"])
     cfg["timing"] = ("CE parts: inside the step (after the previous step's lce_forward); parts timed apart: each "
                      "fwd+VJP pair after a 512 MiB read that leaves the Infinity Cache clean, as in the step, "

@@ -11,7 +11,9 @@
 //
 // Three row layouts, all HBM streaming with 16-byte loads coalesced across lanes:
 //   * narrow: rows of 1, 2, 4 or 8 aligned vectors; one lane per row and several
-//     rows per lane in flight (the 1,048,576 x 8 fp32 shape is 2 vectors per row);
+//     rows per lane in flight.  The default takes it for forward rows of up to 2
+//     vectors (the 1,048,576 x 8 fp32 shape has 2) and VJP rows of 1; for longer rows
+//     one lane's vectors are 32 B or more apart and the instructions touch part lines;
 //   * lanes:  G lanes per row (G <= 64), 64 / G rows per wavefront, online state
 //     per lane, then a butterfly merge of (m, s) pairs across the G lanes;
 //   * rowwg:  one workgroup of 64 * NW threads per row for long rows, per-wave
