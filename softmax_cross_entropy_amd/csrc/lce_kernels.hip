@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
     const int64_t col0 = a.c0 + (int64_t)col_tile * BN;
 
     // ---- global -> LDS loads: each wave fills 64 rows of A and of B per stage ----
-    // One global_load_lds_dwordx4 writes 64 lanes x 16 bytes = 8 LDS rows; lane i lands
+    // One buffer_load_dwordx4 ... lds writes 64 lanes x 16 bytes = 8 LDS rows; lane i lands
     // at (row = first + i / 8, physical chunk i % 8), so it fetches the logical chunk
     // that the swizzle maps there.  Rows past N (or V) re-read the last valid row; their
     // results are never stored (columns past V are masked in the epilogue).
@@ -125,21 +125,30 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
         const int r = par * 8 + (lane >> 3);  // (row >> 1) & 7 depends only on q's parity
         koff[par] = ((lane & 7) ^ ((r >> 1) & 7)) * 8;
     }
-    // Addresses: a wave-uniform base (the tile's first row at K offset k0) plus a 32-bit
-    // per-lane byte offset; rows past N (or V) are clamped to the last valid row.
+    // Addresses: a buffer descriptor per operand tile (its first row, its valid rows)
+    // plus a 32-bit per-lane byte offset; rows past N (or V) are clamped to the last
+    // valid row, so every load stays inside its descriptor's range.
     const int64_t a_rows = a.N - row0 < BM ? a.N - row0 : BM;  // valid rows in this tile
     const int64_t b_rows = a.c_end - col0 < BN ? a.c_end - col0 : BN;
     const uint32_t row_bytes = (uint32_t)(a.D * 2);
     const char* a_tile = reinterpret_cast<const char*>(a.H + row0 * a.D);
     const char* b_tile = reinterpret_cast<const char*>(a.W + col0 * a.D);
+    // The DMA goes through buffer_load_dwordx4 ... lds rather than global_load_lds: the
+    // compiler counts LDS reads precisely only while no FLAT-encoded instruction is in
+    // flight, and with the global form pending it waited for all LDS reads
+    // (s_waitcnt lgkmcnt(0)) before every group of MFMAs, including the reads issued
+    // for later K16 steps.  Word 3 of the descriptor: raw 32-bit data, no swizzle.
+    const __amdgpu_buffer_rsrc_t rsrc_a =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a_tile, (short)0, (int)((uint32_t)a_rows * row_bytes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsrc_b =
+        __builtin_amdgcn_make_buffer_rsrc((void*)b_tile, (short)0, (int)((uint32_t)b_rows * row_bytes), 0x00020000);
 
     // The LDS destination of group q is the group-0 slot plus q * 1 KiB; the instruction's
     // immediate offset moves the LDS and the global address together, so every group
     // shares one LDS base (M0) and the global address is pre-biased by -q KiB.
     // DMA of one stage, group by group: groups 0..7 load A rows, 8..15 load W rows.
-    // Group q fills LDS rows wave * 64 + (q % 8) * 8 .. + 7.  Global addresses are a
-    // wave-uniform tile base plus a non-negative 32-bit byte offset (row * 2D + K bytes,
-    // below 256 * 2D), which the hardware zero-extends.
+    // Group q fills LDS rows wave * 64 + (q % 8) * 8 .. + 7.  The byte offset into the
+    // tile is row * 2D + K bytes, below (valid rows) * 2D.
     auto dma_group = [&](auto qc, int kt, int buf) {
         constexpr int q = decltype(qc)::value % 8;
         constexpr bool is_b = decltype(qc)::value >= 8;
@@ -149,18 +158,34 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
         const int rr = r < nrows ? r : (int)nrows - 1;
         // K tail: past D, re-read this row's last chunk; zeroed in LDS once it lands
         const uint32_t kb = (uint32_t)(k0 + koff[q & 1] < a.D ? koff[q & 1] : a.D - 8 - k0) * 2;
-        const char* g = (is_b ? b_tile : a_tile) + k0 * 2 + ((uint32_t)rr * row_bytes + kb);
+        const uint32_t voff = (uint32_t)(k0 * 2) + ((uint32_t)rr * row_bytes + kb);
         char* dst = &lds[buf][is_b ? 1 : 0][(wave * 64 + q * 8) * 128];
-        __builtin_amdgcn_global_load_lds((const void*)g, (lds_void_t*)dst, 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_b ? rsrc_b : rsrc_a, (lds_void_t*)dst, 16, voff, 0, 0, 0);
     };
     auto issue = [&](int kt, int buf) {
         [&]<int... Q>(std::integer_sequence<int, Q...>) {
             (dma_group(std::integral_constant<int, Q>{}, kt, buf), ...);
         }(std::make_integer_sequence<int, 16>{});
     };
+    // Waits are written with the builtin, which the compiler's own wait insertion sees
+    // (an inline-asm wait is opaque to it, so it added lgkmcnt(0) waits of its own after
+    // the barrier); the empty asm statements keep LDS accesses from moving across them.
+    // s_waitcnt immediates on gfx9: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8.
+    constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0)
+    constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
     // Waits until the DMA of stage s has landed (loads retire in order; nothing else is
     // in flight by then).
-    auto wait_stage = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+    auto wait_stage = [&]() {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        asm volatile("" ::: "memory");
+    };
+    auto lds_barrier = [&]() {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
     // In a K-tail stage the chunks past D hold copies of a valid chunk: overwrite this
     // lane's slots with zeros after its loads have landed, before the barrier that
     // publishes the stage.
@@ -255,9 +280,7 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
         // wave has finished reading buffer `cur`, which then takes stage kt + 2
         wait_stage();
         if (kt + 1 < nk) zero_tail(kt + 1, cur ^ 1);
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
+        lds_barrier();
     };
 
     // Pipeline: the fragments of a K16 step are read from LDS two steps ahead, into four
@@ -274,9 +297,7 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
     issue(0, 0);
     wait_stage();
     zero_tail(0, 0);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+    lds_barrier();
     if (nk > 1) issue(1, 1);
     read_frags(0, 0, fa0, fb0);
     read_frags(0, 1, fa1, fb1);
@@ -308,7 +329,7 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
         mfma_all(fa3, fb3);
     }
     // the last loop iteration's (redundant) DMA must land before the workgroup can end
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_stage();
 
     // ---- epilogue: (m, s) per row over this wave's 128 columns ----------------
     // acc[i][j][e] holds Z[row = wrow0 + i*32 + l32][col = wcol0 + j*32 + 8*(e/4) + 4*h2 + e%4]:
