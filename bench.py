@@ -49,48 +49,48 @@ CSRC = os.path.join(ROOT, "softmax_cross_entropy_amd", "csrc")
 # and headers at measurement time: a changed kernel reports traffic null until it is measured again.
 TRAFFIC = {
     "ce_forward": {
-        "source_sha": "5909a33a1b8df273",
-        "bytes": 622635972
+        "source_sha": "a20accd9afb738a2",
+        "bytes": 622630402
     },
     "ce_vjp": {
-        "source_sha": "5909a33a1b8df273",
-        "bytes": 1245006495
+        "source_sha": "a20accd9afb738a2",
+        "bytes": 1245001212
     },
     "lce_forward": {
-        "source_sha": "8cc9189b31607a6b",
-        "bytes": 15154570106
+        "source_sha": "dc196b071464686b",
+        "bytes": 15154255746
     },
     "kl_forward": {
         "source_sha": "48529b2dec4f5015",
-        "bytes": 622516133
+        "bytes": 622508420
     },
     "kl_vjp": {
         "source_sha": "48529b2dec4f5015",
-        "bytes": 933640229
+        "bytes": 933661954
     },
     "ce_forward_ex": {
-        "source_sha": "cc13f7f9d795ed5e",
-        "bytes": 622631908
+        "source_sha": "4ee7710e8505ad5a",
+        "bytes": 622627394
     },
     "ce_vjp_ex": {
-        "source_sha": "cc13f7f9d795ed5e",
-        "bytes": 1244950304
+        "source_sha": "4ee7710e8505ad5a",
+        "bytes": 1206057485
     },
     "ce_forward_probs": {
-        "source_sha": "cc13f7f9d795ed5e",
-        "bytes": 622496390
+        "source_sha": "4ee7710e8505ad5a",
+        "bytes": 622489605
     },
     "ce_vjp_probs": {
-        "source_sha": "cc13f7f9d795ed5e",
-        "bytes": 933605926
+        "source_sha": "4ee7710e8505ad5a",
+        "bytes": 933601029
     },
     "js_forward": {
         "source_sha": "636dff21e4e490f5",
-        "bytes": 1225023080
+        "bytes": 1224893383
     },
     "js_vjp": {
         "source_sha": "636dff21e4e490f5",
-        "bytes": 937821357
+        "bytes": 936264483
     },
 }
 
