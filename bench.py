@@ -526,6 +526,11 @@ def main():
     def rate(byts, t):
         return byts / (t * 1e-3) / 1e9
 
+    def spread(ts):
+        # per-step times of the K timed steps (ms): the value above is their mean
+        ts = sorted(ts)
+        return {"median_ms": float(ts[len(ts) // 2]), "min_ms": float(ts[0]), "max_ms": float(ts[-1])}
+
     def b2b_out(fb, vb, f, v):
         return {"fwd_ms": f, "vjp_ms": v, "ms": f + v, "GB_s": rate(fb + vb, f + v),
                 "frac_hbm_peak": rate(fb + vb, f + v) / HBM_PEAK_GBS}
@@ -548,6 +553,7 @@ def main():
                                    "algorithmic_bytes": fwd_b + vjp_b,
                                    "fwd_ms": f_ms, "fwd_GB_s": rate(fwd_b, f_ms),
                                    "vjp_ms": v_ms, "vjp_GB_s": rate(vjp_b, v_ms),
+                                   "per_step": spread(ms(0, 2)),
                                    "back_to_back": b2b_out(fwd_b, vjp_b, *ce_b2b)}
         hbm_rooflines(("ce_forward", "ce_vjp"), (fwd_b, vjp_b), ce_b2b, (f_ms, v_ms), "ms_in_step")
         cfg["workload"].append(f"ce_forward+ce_vjp bf16 [{CE_ROWS} x {CE_V}]")
@@ -559,7 +565,7 @@ def main():
         fl = lce_flops(LCE_N, LCE_D, LCE_V)
         tf = fl / (l_ms * 1e-3) / 1e12
         parts_out["lce_forward"] = {"ms": l_ms, "TFLOP_s": tf, "frac_mfma_bf16_peak": tf / MFMA_BF16_PEAK_TFLOPS,
-                                    "flop": fl}
+                                    "flop": fl, "per_step": spread(ms(2, 3))}
         rooflines["lce_forward"] = {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS,
                                     "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS,
                                     "traffic": traffic_for("lce_forward"),
