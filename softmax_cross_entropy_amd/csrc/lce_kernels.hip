@@ -42,6 +42,13 @@ constexpr int kThreads = 256;        // 4 waves as 2 x 2, each owning 128 x 128 
 constexpr int WT = 128;              // wave tile edge
 constexpr int FB = WT / 32;          // 4 x 4 MFMA 32x32 blocks per wave
 constexpr int kStageBytes = BM * BK * 2;  // 32 KiB per operand per stage
+constexpr int kStageArea = 2 * 2 * kStageBytes;  // two stages of A and B
+// The gradient epilogue stages each wave's 128 x 128 bf16 block of dZ through LDS,
+// column-major with a column pitch of 136 elements (272 bytes: 16-byte aligned columns,
+// and the two half-waves' columns four apart land in different banks).
+constexpr int kTPitch = WT + 8;
+constexpr int kWaveStaging = WT * kTPitch * 2;
+constexpr int kStagingBytes = 4 * kWaveStaging;
 constexpr int kTilesPerGroup = 32;   // tiles per super-block (one per CU of an XCD)
 constexpr int kXcds = 8;
 
@@ -78,15 +85,17 @@ struct TileArgs {
 // kGrad = true: the same tile of Z turned into dZ = g (exp((z - m) - log s) - [col = y])
 // with the saved (m, log s), stored in bf16 (the logits regenerated for the backward),
 // both row-major and transposed: each of the two products of the backward then reads
-// its operand without a transpose.  The 32 lanes of a half-wave hold 32 consecutive
-// rows of each column, so the transposed stores are coalesced too.
+// its operand without a transpose.  The transposed copy is staged through LDS and
+// leaves in 16-byte stores of 8 rows of a column.
 template <bool kGrad>
 __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
     // One LDS object (the compiler then sees the DMA writes and the fragment reads as
-    // one array and inserts no waits of its own): two stages of A and B, then targets.
-    __shared__ __attribute__((aligned(16))) char smem[2 * 2 * kStageBytes + BM * 4];
+    // one array and inserts no waits of its own): two stages of A and B (or, in the
+    // gradient epilogue, the dZ staging blocks), then targets.
+    constexpr int kData = kGrad && kStagingBytes > kStageArea ? kStagingBytes : kStageArea;
+    __shared__ __attribute__((aligned(16))) char smem[kData + BM * 4];
     char (*lds)[2][kStageBytes] = reinterpret_cast<char (*)[2][kStageBytes]>(smem);
-    int32_t* tile_targets = reinterpret_cast<int32_t*>(smem + 2 * 2 * kStageBytes);
+    int32_t* tile_targets = reinterpret_cast<int32_t*>(smem + kData);
 
     // ---- which tile: XCD-aware super-blocks ----------------------------------
     // Consecutive workgroups go to the 8 XCDs in turn.  The k-th workgroup an XCD
@@ -340,7 +349,14 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
 
     if constexpr (kGrad) {
         // dZ for this lane's 4 rows x 64 columns.  A row with an out-of-range target
-        // gets m = NaN, so its whole row of dZ is NaN (its loss is NaN too).
+        // gets m = NaN, so its whole row of dZ is NaN (its loss is NaN too).  The
+        // row-major copy is stored directly, 4 columns per store; the transposed copy goes
+        // through this wave's LDS block first, so that it leaves in 16-byte stores of 8
+        // rows of a column.  After the barrier no wave reads the stage buffers any more
+        // (the last DMA has landed: wait_stage above).
+        lds_barrier();
+        char* const tblk = smem + wave * kWaveStaging;
+        auto tput = [&](int cl, int rl, uint16_t v) { *reinterpret_cast<uint16_t*>(tblk + (cl * kTPitch + rl) * 2) = v; };
 #pragma unroll
         for (int i = 0; i < FB; ++i) {
             const int lr = wm * WT + i * 32 + l32;
@@ -352,34 +368,31 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
             const float nlsl = -l.y * kLog2e;
             const float gr = a.g[row];
             __bf16* grow = a.G + row * a.ldG - a.c0;
-            uint16_t* gcol = reinterpret_cast<uint16_t*>(a.GT) + row;  // (c, row) at gcol[(c - c0) * ldGT]
+            const int rl = i * 32 + l32;  // row within the wave's block
             auto dz = [&](float z) { return gr * __builtin_amdgcn_exp2f(__builtin_fmaf(z - m, kLog2e, nlsl)); };
 #pragma unroll
             for (int j = 0; j < FB; ++j)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int64_t c = wcol0 + j * 32 + 8 * q + 4 * h2;  // 4 consecutive columns
+                    const int cl = j * 32 + 8 * q + 4 * h2;  // 4 consecutive columns of the block
+                    const int64_t c = wcol0 + cl;
                     const float v0 = dz(acc[i][j][4 * q]), v1 = dz(acc[i][j][4 * q + 1]);
                     const float v2 = dz(acc[i][j][4 * q + 2]), v3 = dz(acc[i][j][4 * q + 3]);
-                    const int64_t ct = (c - a.c0) * a.ldGT;
+                    uint2 w;
+                    w.x = Elem<__bf16>::bits2(v0, v1);
+                    w.y = Elem<__bf16>::bits2(v2, v3);
+                    // the block always takes all four; columns past the chunk are never read back
+                    tput(cl, rl, (uint16_t)w.x);
+                    tput(cl + 1, rl, (uint16_t)(w.x >> 16));
+                    tput(cl + 2, rl, (uint16_t)w.y);
+                    tput(cl + 3, rl, (uint16_t)(w.y >> 16));
                     if (c + 3 < a.c_end) {
-                        uint2 w;
-                        w.x = Elem<__bf16>::bits2(v0, v1);
-                        w.y = Elem<__bf16>::bits2(v2, v3);
                         *reinterpret_cast<uint2*>(grow + c) = w;
-                        gcol[ct] = (uint16_t)w.x;
-                        gcol[ct + a.ldGT] = (uint16_t)(w.x >> 16);
-                        gcol[ct + 2 * a.ldGT] = (uint16_t)w.y;
-                        gcol[ct + 3 * a.ldGT] = (uint16_t)(w.y >> 16);
                     } else {
                         const float v[4] = {v0, v1, v2, v3};
 #pragma unroll
                         for (int t = 0; t < 4; ++t)
-                            if (c + t < a.c_end) {
-                                const __bf16 b = (__bf16)v[t];
-                                grow[c + t] = b;
-                                gcol[ct + t * a.ldGT] = __builtin_bit_cast(uint16_t, b);
-                            }
+                            if (c + t < a.c_end) grow[c + t] = (__bf16)v[t];
                     }
                 }
             // the target column: stored again as g (p - 1) by the lane that stored it
@@ -397,7 +410,31 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
                 }
                 const __bf16 b = (__bf16)(dz(z) - gr);
                 grow[y] = b;
-                gcol[((int64_t)y - a.c0) * a.ldGT] = __builtin_bit_cast(uint16_t, b);
+                tput(cc, rl, __builtin_bit_cast(uint16_t, b));  // after this lane's first write of it
+            }
+        }
+        // The transposed copy: lane k of 2048 16-byte pieces takes column k / 16 of the
+        // block, rows 8 (k % 16) .. + 7; 16 lanes write one column's 256 bytes.  LDS
+        // accesses of one wave complete in order, so the reads see this wave's writes.
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __builtin_amdgcn_wave_barrier();
+        uint16_t* const gt = reinterpret_cast<uint16_t*>(a.GT);
+        const bool t16 = (a.ldGT % 8) == 0;  // columns of GT start on 16-byte boundaries
+#pragma unroll 4
+        for (int it = 0; it < WT * WT / 8 / 64; ++it) {
+            const int k = it * 64 + lane;
+            const int cl = k >> 4, rc = (k & 15) * 8;
+            const int64_t c = wcol0 + cl;
+            const int64_t r = wrow0 + rc;
+            if (c >= a.c_end || r >= a.N) continue;
+            const U4 v = *reinterpret_cast<const U4*>(tblk + (cl * kTPitch + rc) * 2);
+            uint16_t* dst = gt + (c - a.c0) * a.ldGT + r;
+            if (t16 && r + 8 <= a.N) {
+                store_u4(dst, v);
+            } else {
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+                    if (r + t < a.N) dst[t] = (uint16_t)(v.w[t >> 1] >> (16 * (t & 1)));
             }
         }
     } else {
