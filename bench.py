@@ -50,47 +50,47 @@ CSRC = os.path.join(ROOT, "softmax_cross_entropy_amd", "csrc")
 TRAFFIC = {
     "ce_forward": {
         "source_sha": "a20accd9afb738a2",
-        "bytes": 622630402
+        "bytes": 622632289
     },
     "ce_vjp": {
         "source_sha": "a20accd9afb738a2",
-        "bytes": 1245001212
+        "bytes": 1245000923
     },
     "lce_forward": {
-        "source_sha": "dc196b071464686b",
-        "bytes": 15154255746
+        "source_sha": "02a17b9b50c09617",
+        "bytes": 15159957315
     },
     "kl_forward": {
         "source_sha": "48529b2dec4f5015",
-        "bytes": 622508420
+        "bytes": 622509410
     },
     "kl_vjp": {
         "source_sha": "48529b2dec4f5015",
-        "bytes": 933661954
+        "bytes": 933662945
     },
     "ce_forward_ex": {
         "source_sha": "4ee7710e8505ad5a",
-        "bytes": 622627394
+        "bytes": 622627617
     },
     "ce_vjp_ex": {
         "source_sha": "4ee7710e8505ad5a",
-        "bytes": 1206057485
+        "bytes": 1206058590
     },
     "ce_forward_probs": {
         "source_sha": "4ee7710e8505ad5a",
-        "bytes": 622489605
+        "bytes": 622490019
     },
     "ce_vjp_probs": {
         "source_sha": "4ee7710e8505ad5a",
-        "bytes": 933601029
+        "bytes": 933601251
     },
     "js_forward": {
         "source_sha": "636dff21e4e490f5",
-        "bytes": 1224893383
+        "bytes": 1224875037
     },
     "js_vjp": {
         "source_sha": "636dff21e4e490f5",
-        "bytes": 936264483
+        "bytes": 936252931
     },
 }
 
