@@ -570,7 +570,11 @@ def main():
                                     "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS,
                                     "traffic": traffic_for("lce_forward"),
                                     "ms": l_ms, "algorithmic_flop": fl,
-                                    "kernels": "lce_tile_mfma + lce_merge (one lce_forward call)"}
+                                    "kernels": "lce_tile_mfma + lce_merge (one lce_forward call)",
+                                    "traffic_note": "FETCH_SIZE counts L2 fills from beyond each XCD's L2 (Infinity "
+                                                    "Cache or HBM): with 32 tiles of 256 x 256 in flight per XCD, each "
+                                                    "W tile is filled once per XCD and each H tile once per 4 x 8 "
+                                                    "super-block, 14.99 GB by the tile order; H and W are 1.31 GB"}
         cfg["workload"].append(f"lce_forward bf16 N={LCE_N} D={LCE_D} V={LCE_V}")
         cfg["lce"] = {"N": LCE_N, "D": LCE_D, "V": LCE_V, "dtype": "bf16 in, fp32 accumulate"}
         if "value" not in out:
