@@ -57,7 +57,7 @@ TRAFFIC = {
         "bytes": 1245000923
     },
     "lce_forward": {
-        "source_sha": "02a17b9b50c09617",
+        "source_sha": "784936aa4c391cbe",
         "bytes": 15159957315
     },
     "kl_forward": {

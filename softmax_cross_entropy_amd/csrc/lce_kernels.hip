@@ -356,7 +356,9 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
         // (the last DMA has landed: wait_stage above).
         lds_barrier();
         char* const tblk = smem + wave * kWaveStaging;
-        auto tput = [&](int cl, int rl, uint16_t v) { *reinterpret_cast<uint16_t*>(tblk + (cl * kTPitch + rl) * 2) = v; };
+        auto tput = [&](int cl, int rl, uint16_t v) {
+            *reinterpret_cast<uint16_t*>(tblk + (cl * kTPitch + rl) * 2) = v;
+        };
 #pragma unroll
         for (int i = 0; i < FB; ++i) {
             const int lr = wm * WT + i * 32 + l32;
