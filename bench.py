@@ -212,6 +212,29 @@ def cpu_baseline(ce_batch, lce_inputs, lce_rows=32):
     oco.grad_index(z, y_ign, 1.0, 0.1, -100, "mean")
     opt_s = time.perf_counter() - t0
     of_b, ov_b = opt_bytes(32, b.V, 2, ignored=len(range(0, 32, 16)))
+    pt = inputs.prob_targets(32, KL_V, "f32", workload=20, stream=3).astype(np.float64)
+    t0 = time.perf_counter()
+    oco.forward_probs(zq, pt, 0.1, "mean")
+    oco.grad_probs(zq, pt, 1.0, 0.1, "mean")
+    probs_s = time.perf_counter() - t0
+    pf_b, pv_b = probs_bytes(32, KL_V, 4)
+    # the CE oracle at the other workload shapes, on a bounded sample of rows of each
+    shapes = {}
+    x3, y3 = inputs.strided_view_source()
+    for label, (zs, ys) in (
+            ("f32 [1048576 x 8], 262,144 rows", (lambda c: (c.logits[: 1 << 18], c.targets[: 1 << 18]))(
+                inputs.small_v_rows())),
+            ("f32 [65536 x 1024], 8,192 rows", (lambda c: (c.logits[:8192], c.targets[:8192]))(
+                inputs.numerics_stress("f32"))),
+            ("f32 view [10, 119, 32768][:, :-1], 256 rows",
+             (np.ascontiguousarray(x3[:, :-1]).reshape(-1, x3.shape[-1])[:256], inputs.shifted_targets(y3)[:256]))):
+        z = oce.decode(zs, "f32")
+        t0 = time.perf_counter()
+        _, m, ls = oce.forward(z, ys)
+        oce.grad(z, ys, np.ones(len(ys)), m, ls)
+        sec = time.perf_counter() - t0
+        fb, vb = ce_bytes(len(ys), z.shape[1], 4)
+        shapes[label] = {"value": (fb + vb) / sec / 1e9, "unit": "GB/s", "cores": 1, "seconds": sec}
     blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     return {
         "value": (fwd_b + vjp_b) / ce_s / 1e9,
@@ -229,6 +252,10 @@ def cpu_baseline(ce_batch, lce_inputs, lce_rows=32):
                                  f"{b.rows} rows, all {b.V} columns"},
         "js": {"value": (jf_b + jv_b) / js_s / 1e9, "unit": "GB/s", "cores": 1, "seconds": js_s,
                "sample": f"JS fwd+grad oracle (float64 NumPy) on 32 of {KL_ROWS} rows, all {KL_V} columns"},
+        "ce_probs": {"value": (pf_b + pv_b) / probs_s / 1e9, "unit": "GB/s", "cores": 1, "seconds": probs_s,
+                     "sample": f"probability-target oracle (eps 0.1, mean; float64 NumPy) on 32 of {KL_ROWS} rows, "
+                               f"all {KL_V} columns"},
+        "shapes": shapes,
         "kl": {"value": (kf_b + kv_b) / kl_s / 1e9, "unit": "GB/s", "cores": 1, "seconds": kl_s,
                "sample": f"KL fwd+grad oracle (float64 NumPy) on 32 of {KL_ROWS} rows, all {KL_V} columns"},
         "lce_backward": {"value": 3 * lce_flops(lce_rows, LCE_D, LCE_V) / lbw_s / 1e12, "unit": "TFLOP/s",
