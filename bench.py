@@ -49,11 +49,11 @@ CSRC = os.path.join(ROOT, "softmax_cross_entropy_amd", "csrc")
 # and headers at measurement time: a changed kernel reports traffic null until it is measured again.
 TRAFFIC = {
     "ce_forward": {
-        "source_sha": "a20accd9afb738a2",
+        "source_sha": "8fff8ae9f765ddd5",
         "bytes": 622632289
     },
     "ce_vjp": {
-        "source_sha": "a20accd9afb738a2",
+        "source_sha": "8fff8ae9f765ddd5",
         "bytes": 1245000923
     },
     "lce_forward": {

@@ -392,7 +392,7 @@ template <typename T>
 hipError_t fwd_typed(const FwdCall& c) {
     FwdArgs a{c.logits, dev_layout(c.in), c.targets, c.n_rows, c.V, c.loss, reinterpret_cast<float2*>(c.lse)};
     const dim3 grid((unsigned)c.plan.blocks);
-    constexpr int kU = Elem<T>::kVec == 8 ? 4 : 8;  // 64 elements in flight per lane per step
+    constexpr int kU = Elem<T>::kVec == 8 ? 4 : 8;  // 32 elements in flight per lane per step
     if (c.plan.narrow_nv > 0) {
         switch (c.plan.narrow_nv) {
             case 1: hipLaunchKernelGGL((ce_fwd_narrow<T, 1, 4>), grid, dim3(kBlock), 0, c.stream, a); break;
