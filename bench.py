@@ -126,6 +126,13 @@ def ce_bytes(rows, V, e):
     return fwd, vjp
 
 
+def fused_bytes(rows, V, e):
+    """Algorithmic HBM bytes of one ce_forward_vjp call: each row is read once (V*e)
+    and its gradient written (V*e); per row the target and g are read (8) and the loss
+    and lse written (12)."""
+    return rows * (2 * V * e + 20)
+
+
 def kl_bytes(rows, V, e):
     """Algorithmic HBM bytes per call: the forward reads both rows and writes kl (4)
     and the two (m, log s) pairs (16); the VJP reads both rows, the pairs and g (20)
@@ -272,8 +279,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--parts", default="ce,lce,lbw,kl,js,opt,probs,shapes",
-                    help="comma list of ce, lce, lbw (lce_backward), kl (kl_forward + kl_vjp), js (js_forward + "
+    ap.add_argument("--parts", default="ce,fused,lce,lbw,kl,js,opt,probs,shapes",
+                    help="comma list of ce, fused (ce_forward_vjp on the ce workload; needs ce), lce, lbw "
+                         "(lce_backward), kl (kl_forward + kl_vjp), js (js_forward + "
                          "js_vjp), opt (ce_forward_ex + ce_vjp_ex), probs (ce_forward_probs + ce_vjp_probs), "
                          "shapes (ce_forward + ce_vjp at the small-vocabulary, strided and huge-row shapes)")
     ap.add_argument("--bwd-steps", type=int, default=5, help="timed lce_backward calls")
@@ -401,10 +409,35 @@ def main():
     def both_states(fwd, vjp):
         return {"clean": timed_pair(fwd, vjp, pre=clean_cache), "back_to_back": timed_pair(fwd, vjp)}
 
+    def timed_one(fn, reps=K, pre=None):
+        for i in range(3):
+            if pre:
+                pre()
+            fn(i)
+        torch.cuda.synchronize()
+        pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for i in range(reps):
+            if pre:
+                pre()
+            pev[i][0].record(stream)
+            fn(i)
+            pev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([e[0].elapsed_time(e[1]) for e in pev]))
+
     ce_b2b = None
     if ce_batch is not None:
         ce_b2b = timed_pair(lambda i: abi.ce_forward(X[i % 2], T, loss=loss, lse=lse),
                             lambda i: abi.ce_vjp(X[i % 2], T, lse, G, dlogits=dX))
+
+    fused_ms = None
+    if ce_batch is not None and "fused" in parts:
+        note("ce_forward_vjp")
+
+        def fused_call(i):
+            abi.ce_forward_vjp(X[i % 2], T, G, loss=loss, lse=lse, dlogits=dX)
+
+        fused_ms = {"clean": timed_one(fused_call, pre=clean_cache), "back_to_back": timed_one(fused_call)}
 
     kl_ms = None
     if "kl" in parts:
@@ -587,6 +620,21 @@ def main():
         cfg["ce"] = {"rows": CE_ROWS, "V": CE_V, "dtype": "bf16"}
         out["value"] = gbs
         out["unit"] = "GB/s"
+        if fused_ms is not None:
+            ub = fused_bytes(CE_ROWS, CE_V, 2)
+            tc, tb = fused_ms["clean"], fused_ms["back_to_back"]
+            parts_out["ce_forward_vjp"] = {
+                "ms": tc, "GB_s": rate(ub, tc), "frac_hbm_peak": rate(ub, tc) / HBM_PEAK_GBS,
+                "algorithmic_bytes": ub, "in_step": False, "cache": "clean",
+                "vs_two_calls_in_step": fv_ms / tc,
+                "back_to_back": {"ms": tb, "GB_s": rate(ub, tb), "frac_hbm_peak": rate(ub, tb) / HBM_PEAK_GBS,
+                                 "vs_two_calls": (ce_b2b[0] + ce_b2b[1]) / tb},
+                "note": "one kernel for a g known before the forward: each row read from HBM once"}
+            a = rate(ub, tb)
+            rooflines["ce_forward_vjp"] = {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                           "frac": a / HBM_PEAK_GBS, "traffic": traffic_for("ce_forward_vjp"),
+                                           "ms": tb, "timing": "back to back", "ms_clean_cache": tc,
+                                           "algorithmic_bytes": ub}
     if lce_in is not None:
         l_ms = float(np.mean(ms(2, 3)))
         fl = lce_flops(LCE_N, LCE_D, LCE_V)
@@ -607,7 +655,8 @@ def main():
         if "value" not in out:
             out["value"] = tf
             out["unit"] = "TFLOP/s"
-    step_kernels = list(rooflines)  # ce_forward, ce_vjp, lce_forward: the kernels of the timed step
+    # ce_forward, ce_vjp, lce_forward: the kernels of the timed step
+    step_kernels = [k for k in rooflines if k != "ce_forward_vjp"]
     if bwd_ms is not None:
         fl = 3 * lce_flops(LCE_N, LCE_D, LCE_V)
         tf = fl / (bwd_ms * 1e-3) / 1e12

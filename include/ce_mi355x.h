@@ -5,6 +5,7 @@
  *
  *   ce_forward    per-row loss and log-sum-exp of a [rows, V] logits view
  *   ce_vjp        dlogits = g_i * (softmax(z_i) - onehot(y_i)) from the saved log-sum-exp
+ *   ce_forward_vjp  ce_forward and ce_vjp in one kernel, for a g known before the forward
  *   lce_forward   per-row loss and log-sum-exp of H.W^T, streamed over vocabulary
  *                 tiles without materialising the N x V logits
  *   lce_backward  dH and dW of sum_i g_i loss_i for lce_forward's loss; the logits
@@ -167,6 +168,48 @@ ce_status ce_vjp(const void* logits, ce_layout in, ce_dtype dt, const int32_t* t
 ce_status ce_vjp_lanes(const void* logits, ce_layout in, ce_dtype dt, const int32_t* targets,
                        const float* lse, const float* g, int64_t n_rows, int64_t V, void* dlogits,
                        ce_layout out, int32_t lanes_per_row, hipStream_t stream);
+
+/*
+ * ce_forward_vjp: ce_forward and ce_vjp in one kernel, for a caller that knows the
+ * upstream gradient g before the forward runs (a loss summed or averaged over the
+ * rows, as the next-token loss ".sum()" of MLX issue #4686 (above), Describe the bug).
+ *
+ * Source: Ineshin (above), section 1: the loss needs only the row's log-sum-exp and
+ * target logit, and the backward only that log-sum-exp; "One barrier short", first
+ * section: mlx-lm computes its divergences and their gradients in one fused pass so
+ * that the log-softmax rows never exist in memory.  Each row's
+ * Rows of more than 4096 and at most 20480 16-byte vectors (16384 for fp32) whose
+ * input and output rows share their 16-byte phase are held in the registers of one
+ * 1024-thread workgroup: the row max and the sum of exponentials are two passes over
+ * those registers and the gradient a third, so HBM carries one read and one write of
+ * the logits instead of ce_forward's read plus ce_vjp's read and write.  Other rows
+ * are reduced as ce_forward reduces them and then swept a second time by the same
+ * lanes, mostly from the GPU's caches.
+ *
+ *   logits, targets  as in ce_forward.
+ *   g        float32 [n_rows], contiguous: the upstream gradient of each row's loss.
+ *   loss, lse        written as by ce_forward.
+ *   dlogits  written as by ce_vjp with that lse and g, through `out`.
+ * dlogits always equal ce_vjp's for the lse this call writes, bit for bit.  Loss and
+ * lse equal ce_forward's bit for bit except for rows held in registers (their two-pass
+ * sum rounds differently, within float32 accumulation error) and for rows of 1 or 2
+ * aligned 16-byte vectors whose dlogits rows are not 16-byte aligned (ce_forward then
+ * takes one lane per row, this call a lane group).  dlogits may be the logits themselves (in place) only with an
+ * identical layout; otherwise no output may overlap the logits, targets, g or another
+ * output (CE_ERR_ALIAS).  Errors as ce_forward and ce_vjp.
+ */
+ce_status ce_forward_vjp(const void* logits, ce_layout in, ce_dtype dt, const int32_t* targets, const float* g,
+                         int64_t n_rows, int64_t V, float* loss, float* lse, void* dlogits, ce_layout out,
+                         hipStream_t stream);
+
+/*
+ * ce_forward_vjp_lanes: ce_forward_vjp with lanes_per_row chosen as in ce_forward_lanes
+ * (0: as ce_forward_vjp; a power of two in [1, 1024]; -1: one lane per row, which needs
+ * rows of 1, 2, 4 or 8 aligned 16-byte vectors in both views).  For tests and tuning.
+ */
+ce_status ce_forward_vjp_lanes(const void* logits, ce_layout in, ce_dtype dt, const int32_t* targets,
+                               const float* g, int64_t n_rows, int64_t V, float* loss, float* lse, void* dlogits,
+                               ce_layout out, int32_t lanes_per_row, hipStream_t stream);
 
 /*
  * lce_workspace_size: bytes of device workspace lce_forward needs for (N, D, V).

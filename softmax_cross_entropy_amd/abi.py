@@ -29,7 +29,8 @@ CE_REDUCE = {"none": 0, "sum": 1, "mean": 2}
 CE_NO_IGNORE = -(2 ** 31)
 
 # every symbol include/ce_mi355x.h declares
-EXPORTS = ("ce_forward", "ce_forward_lanes", "ce_vjp", "ce_vjp_lanes", "lce_workspace_size",
+EXPORTS = ("ce_forward", "ce_forward_lanes", "ce_vjp", "ce_vjp_lanes", "ce_forward_vjp", "ce_forward_vjp_lanes",
+           "lce_workspace_size",
            "lce_forward", "lce_backward_workspace_size", "lce_backward", "kl_forward", "kl_forward_lanes",
            "kl_vjp", "kl_vjp_lanes", "js_forward", "js_forward_lanes", "js_vjp", "js_vjp_lanes",
            "ce_reduce_workspace_size", "ce_forward_ex", "ce_vjp_ex", "ce_forward_probs",
@@ -73,6 +74,10 @@ def lib() -> ctypes.CDLL:
         L.ce_vjp.argtypes = [_vp, CELayout, ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _vp, CELayout, _vp]
         L.ce_vjp_lanes.argtypes = [_vp, CELayout, ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _vp, CELayout,
                                    _i32, _vp]
+        L.ce_forward_vjp.argtypes = [_vp, CELayout, ctypes.c_int, _vp, _vp, _i64, _i64, _vp, _vp, _vp, CELayout,
+                                     _vp]
+        L.ce_forward_vjp_lanes.argtypes = [_vp, CELayout, ctypes.c_int, _vp, _vp, _i64, _i64, _vp, _vp, _vp,
+                                           CELayout, _i32, _vp]
         L.lce_workspace_size.argtypes = [_i64, _i64, _i64]
         L.lce_workspace_size.restype = _sz
         L.lce_forward.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _sz, _vp]
@@ -105,7 +110,8 @@ def lib() -> ctypes.CDLL:
                                    _vp, _vp, CELayout, _vp]
         L.ce_status_string.argtypes = [ctypes.c_int]
         L.ce_status_string.restype = ctypes.c_char_p
-        for name in ("ce_forward", "ce_forward_lanes", "ce_vjp", "ce_vjp_lanes", "lce_forward", "lce_backward",
+        for name in ("ce_forward", "ce_forward_lanes", "ce_vjp", "ce_vjp_lanes", "ce_forward_vjp",
+                     "ce_forward_vjp_lanes", "lce_forward", "lce_backward",
                      "kl_forward", "kl_forward_lanes", "kl_vjp", "kl_vjp_lanes", "js_forward", "js_forward_lanes",
                      "js_vjp", "js_vjp_lanes", "ce_forward_ex", "ce_vjp_ex",
                      "ce_forward_probs", "ce_vjp_probs"):
@@ -193,6 +199,37 @@ def ce_vjp(logits: torch.Tensor, targets: torch.Tensor, lse: torch.Tensor, g: to
         st = lib().ce_vjp_lanes(*args, int(lanes_per_row), _stream(logits))
     _check(st, "ce_vjp")
     return dlogits
+
+
+def ce_forward_vjp(logits: torch.Tensor, targets: torch.Tensor, g: torch.Tensor, loss=None, lse=None, dlogits=None,
+                   lanes_per_row: int = 0):
+    """(loss [n], lse [n, 2], dlogits) of ce_forward then ce_vjp with g, in one kernel."""
+    if logits.stride(-1) != 1 and logits.shape[-1] > 1:
+        raise ValueError("logits need unit column stride")
+    lay, n, V = rows_layout(logits)
+    _need(targets, torch.int32, n, "targets")
+    _need(g, torch.float32, n, "g")
+    if loss is None:
+        loss = torch.empty(n, dtype=torch.float32, device=logits.device)
+    if lse is None:
+        lse = torch.empty(n, 2, dtype=torch.float32, device=logits.device)
+    _need(loss, torch.float32, n, "loss")
+    _need(lse, torch.float32, 2 * n, "lse")
+    if dlogits is None:
+        dlogits = torch.empty(logits.shape, dtype=logits.dtype, device=logits.device)
+    if dlogits.dtype != logits.dtype or dlogits.shape != logits.shape:
+        raise ValueError("dlogits must match logits in dtype and shape")
+    if dlogits.stride(-1) != 1 and V > 1:
+        raise ValueError("dlogits need unit column stride")
+    olay, _, _ = rows_layout(dlogits)
+    args = (_ptr(logits), lay, DTYPE_CODE[logits.dtype], _ptr(targets), _ptr(g), n, V, _ptr(loss), _ptr(lse),
+            _ptr(dlogits), olay)
+    if lanes_per_row == 0:
+        st = lib().ce_forward_vjp(*args, _stream(logits))
+    else:
+        st = lib().ce_forward_vjp_lanes(*args, int(lanes_per_row), _stream(logits))
+    _check(st, "ce_forward_vjp")
+    return loss, lse, dlogits
 
 
 def js_forward(q: torch.Tensor, p: torch.Tensor, js=None, lse_q=None, lse_p=None, hq=None, lanes_per_row: int = 0):

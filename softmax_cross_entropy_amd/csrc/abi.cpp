@@ -116,7 +116,7 @@ ce_status make_plan(bool narrow_ok, int64_t V, int es, int64_t n_rows, int32_t l
                     int cus, Plan* plan) {
     const int vec = 16 / es;
     const int64_t nvec = (V + vec - 1) / vec;
-    Plan p{0, 0, 0, 0};
+    Plan p{0, 0, 0, 0, 0};
     if (lanes_req == -1) {
         if (!narrow_ok) return CE_ERR_LAYOUT;
         p.narrow_nv = (int)(V / vec);
@@ -171,7 +171,7 @@ bool chunk_plan(int64_t V, int es, int64_t n_rows, int cus, Plan* plan) {
     const int64_t chunks = (nvec + per_chunk - 1) / per_chunk;
     const int64_t items = n_rows * chunks;
     const int64_t cap = (int64_t)cus * 256;
-    *plan = Plan{0, 0, items < cap ? items : cap, chunks};
+    *plan = Plan{0, 0, items < cap ? items : cap, chunks, 0};
     return true;
 }
 
@@ -245,6 +245,72 @@ ce_status vjp_impl(const void* logits, ce_layout in, ce_dtype dt, const int32_t*
     ce::VjpCall c{logits, host_layout(in, n_rows), (Dt)dt, targets, lse, g, n_rows, V, dlogits,
                   host_layout(out, n_rows), plan, stream};
     return from_hip(ce::launch_ce_vjp(c));
+}
+
+// Every input row and its output row start at the same offset within 16 bytes.
+bool same_phase_rows(const void* x, const ce_layout& in, const void* d, const ce_layout& out, int64_t n_rows,
+                     int es) {
+    if ((((uintptr_t)x ^ (uintptr_t)d) & 15u) != 0) return false;
+    if ((in.row_stride * es) % 16 != 0 || (out.row_stride * es) % 16 != 0) return false;
+    if (n_rows > in.rows_per_batch && (in.batch_stride * es) % 16 != 0) return false;
+    if (n_rows > out.rows_per_batch && (out.batch_stride * es) % 16 != 0) return false;
+    return true;
+}
+
+ce_status fused_impl(const void* logits, ce_layout in, ce_dtype dt, const int32_t* targets, const float* g,
+                     int64_t n_rows, int64_t V, float* loss, float* lse, void* dlogits, ce_layout out,
+                     int32_t lanes, hipStream_t stream) {
+    if (!valid_dtype((int)dt)) return CE_ERR_DTYPE;
+    if (n_rows < 0 || V < 1 || V > kMaxV) return CE_ERR_SHAPE;
+    if (lanes != 0 && lanes != -1 && (lanes < 1 || lanes > 1024 || (lanes & (lanes - 1)) != 0))
+        return CE_ERR_SHAPE;
+    if (n_rows == 0) return CE_OK;
+    if (!logits || !targets || !g || !loss || !lse || !dlogits) return CE_ERR_NULL;
+    const int es = esize(dt);
+    if (!layout_ok(in, n_rows, V, false) || !layout_ok(out, n_rows, V, true) || !aligned(logits, es) ||
+        !aligned(dlogits, es) || !aligned(targets, 4) || !aligned(g, 4) || !aligned(loss, 4) || !aligned(lse, 8))
+        return CE_ERR_LAYOUT;
+    const Extent ex_in = view_extent(logits, in, n_rows, V, es);
+    const Extent ex_out = view_extent(dlogits, out, n_rows, V, es);
+    const Extent ex_t = flat_extent(targets, n_rows * 4);
+    const Extent ex_g = flat_extent(g, n_rows * 4);
+    const Extent ex_loss = flat_extent(loss, n_rows * 4);
+    const Extent ex_lse = flat_extent(lse, n_rows * 8);
+    const bool in_place = logits == dlogits && same_layout(in, out, n_rows);
+    if (!in_place && overlaps(ex_in, ex_out)) return CE_ERR_ALIAS;
+    const Extent outs[3] = {ex_out, ex_loss, ex_lse};
+    for (int i = 0; i < 3; ++i) {
+        if (overlaps(outs[i], ex_t) || overlaps(outs[i], ex_g)) return CE_ERR_ALIAS;
+        if (i > 0 && overlaps(outs[i], ex_in)) return CE_ERR_ALIAS;
+        for (int j = 0; j < i; ++j)
+            if (overlaps(outs[i], outs[j])) return CE_ERR_ALIAS;
+    }
+    int cus = 0;
+    if (ce_status s = device_cus(&cus)) return s;
+    const int vec = 16 / es;
+    const bool narrow_ok = rows_aligned16(logits, in, n_rows, es) && rows_aligned16(dlogits, out, n_rows, es) &&
+                           V % vec == 0 && (V / vec == 1 || V / vec == 2 || V / vec == 4 || V / vec == 8);
+    Plan plan;
+    if (ce_status s = make_plan(narrow_ok, V, es, n_rows, lanes, false, cus, &plan)) return s;
+    // Rows the forward gives a 1024-thread workgroup, whose input and output rows share
+    // their 16-byte phase, and that fit in 1024 threads' registers: the register-resident
+    // kernel, which folds in the same order.
+    if (lanes == 0 && plan.lanes == 1024 && same_phase_rows(logits, in, dlogits, out, n_rows, es)) {
+        const int64_t need = ((V + vec - 1) / vec + 1023) / 1024;
+        const int* nvs = es == 4 ? ce::kRegsNV32 : ce::kRegsNV16;
+        const int cnt = es == 4 ? (int)(sizeof(ce::kRegsNV32) / sizeof(int)) : (int)(sizeof(ce::kRegsNV16) / sizeof(int));
+        for (int i = 0; i < cnt; ++i) {
+            if (need <= nvs[i]) {
+                plan.regs_nv = nvs[i];
+                const int64_t cap = (int64_t)cus * 16;
+                plan.blocks = n_rows < cap ? n_rows : cap;
+                break;
+            }
+        }
+    }
+    ce::FusedCall c{logits, host_layout(in, n_rows), (Dt)dt, targets, g, n_rows, V, loss, lse, dlogits,
+                    host_layout(out, n_rows), plan, stream};
+    return from_hip(ce::launch_ce_fused(c));
 }
 
 // ---- cross-entropy options ------------------------------------------------------
@@ -468,6 +534,18 @@ ce_status ce_vjp_lanes(const void* logits, ce_layout in, ce_dtype dt, const int3
                        const float* g, int64_t n_rows, int64_t V, void* dlogits, ce_layout out,
                        int32_t lanes_per_row, hipStream_t stream) {
     return vjp_impl(logits, in, dt, targets, lse, g, n_rows, V, dlogits, out, lanes_per_row, stream);
+}
+
+ce_status ce_forward_vjp(const void* logits, ce_layout in, ce_dtype dt, const int32_t* targets, const float* g,
+                         int64_t n_rows, int64_t V, float* loss, float* lse, void* dlogits, ce_layout out,
+                         hipStream_t stream) {
+    return fused_impl(logits, in, dt, targets, g, n_rows, V, loss, lse, dlogits, out, 0, stream);
+}
+
+ce_status ce_forward_vjp_lanes(const void* logits, ce_layout in, ce_dtype dt, const int32_t* targets,
+                               const float* g, int64_t n_rows, int64_t V, float* loss, float* lse, void* dlogits,
+                               ce_layout out, int32_t lanes_per_row, hipStream_t stream) {
+    return fused_impl(logits, in, dt, targets, g, n_rows, V, loss, lse, dlogits, out, lanes_per_row, stream);
 }
 
 size_t lce_workspace_size(int64_t N, int64_t D, int64_t V) {

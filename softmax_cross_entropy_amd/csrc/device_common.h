@@ -219,6 +219,10 @@ __device__ __forceinline__ U4 load_u4_stream(const void* p) {
     return u;
 }
 
+// Plain 16-byte load, for a pass whose lines are read again soon after (the one-pass
+// forward and VJP reads each row twice).
+__device__ __forceinline__ U4 load_u4(const void* p) { return *reinterpret_cast<const U4*>(p); }
+
 __device__ __forceinline__ void store_u4(void* p, const U4& u) {
     *reinterpret_cast<U4*>(p) = u;
 }

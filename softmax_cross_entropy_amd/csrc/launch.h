@@ -47,8 +47,26 @@ struct VjpCall {
     hipStream_t stream;
 };
 
+// ce_forward and ce_vjp in one kernel, with g known up front.
+struct FusedCall {
+    const void* logits;
+    HostLayout in;
+    Dt dt;
+    const int32_t* targets;
+    const float* g;
+    int64_t n_rows;
+    int64_t V;
+    float* loss;
+    float* lse;
+    void* dlogits;
+    HostLayout out;
+    Plan plan;
+    hipStream_t stream;
+};
+
 hipError_t launch_ce_forward(const FwdCall& c);
 hipError_t launch_ce_vjp(const VjpCall& c);
+hipError_t launch_ce_fused(const FusedCall& c);
 
 // KL divergence of the teacher rows p from the student rows q (same dtype, own views).
 struct KLFwdCall {

@@ -36,6 +36,15 @@ def test_ce_bytes(rows, V, e, fwd, vjp):
     assert (mb(f), mb(v)) == (fwd, vjp)
 
 
+def test_one_kernel_bytes():
+    """ce_forward_vjp reads each row once: two thirds of the two calls' row bytes, plus
+    20 bytes per row (target, g read; loss, lse written)."""
+    assert bench.fused_bytes(2048, 151936, 2) == 2048 * (2 * 151936 * 2 + 20)
+    assert mb(bench.fused_bytes(2048, 151936, 2)) == 1244.7
+    f, v = bench.ce_bytes(2048, 151936, 2)
+    assert abs(bench.fused_bytes(2048, 151936, 2) / (f + v) - 2 / 3) < 1e-4
+
+
 def test_lce_flops():
     assert bench.lce_flops(8192, 4096, 151936) == 2 * 8192 * 4096 * 151936
     assert abs(bench.lce_flops(8192, 4096, 151936) - 1.0196e13) < 1e9

@@ -1,0 +1,302 @@
+"""GPU parity of ce_forward_vjp (forward and VJP in one kernel) against the float64 oracle.
+
+Every case is checked against oracle/ under the tolerance rules of tests/gpu_util.py,
+and against the library's two calls:
+* where ce_forward_vjp streams the row twice (rows the forward gives fewer than 1024
+  lanes, or whose output is in another 16-byte phase), it folds each row in the
+  forward's order, so loss, lse and dlogits equal ce_forward followed by ce_vjp bit for
+  bit;
+* where it holds the row in registers (rows of more than 4096 16-byte vectors, up to
+  20480 for 16-bit types and 16384 for fp32, input and output in one phase) it takes
+  the max and the sum in two passes, so its lse differs from ce_forward's by float32
+  rounding; its dlogits still equal ce_vjp's given that lse, bit for bit.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import ce as oce
+from softmax_cross_entropy_amd import abi, inputs
+from tests import golden_io
+from tests.gpu_util import TORCH_DT, check_grad, check_loss, check_lse, decode, from_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+LANES = [0, 1, 2, 8, 64, 128, 256, 1024]
+SIZES = [1, 2, 3, 7, 8, 9, 16, 17, 31, 33, 64, 65, 127, 129, 255, 257, 1000, 1023, 1025, 4097]
+
+
+def bits(a: np.ndarray) -> np.ndarray:
+    return a.view(np.uint32) if a.dtype.itemsize == 4 else a.view(np.uint16)
+
+
+def fused(x, t, g, lanes=0, dlogits=None):
+    loss, lse, d = abi.ce_forward_vjp(x, t, g, dlogits=dlogits, lanes_per_row=lanes)
+    torch.cuda.synchronize()
+    return from_dev(loss), from_dev(lse), from_dev(d)
+
+
+def two_calls(x, t, g, lanes=0):
+    loss, lse = abi.ce_forward(x, t, lanes_per_row=lanes)
+    d = abi.ce_vjp(x, t, lse, g)
+    torch.cuda.synchronize()
+    return from_dev(loss), from_dev(lse), from_dev(d)
+
+
+def same_bits(a, b):
+    for u, v in zip(a, b):
+        assert np.array_equal(bits(u), bits(v))
+
+
+def vjp_of_own_lse(got, x, t, g, dlogits=None):
+    """dlogits equal ce_vjp's from the fused call's own lse, bit for bit."""
+    lse = torch.from_numpy(got[1]).cuda()
+    d = abi.ce_vjp(x, t, lse, g, dlogits=dlogits)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(from_dev(d)), bits(got[2]))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_boundary_sizes_all_layouts(dtype):
+    for V in SIZES:
+        b = inputs.normal_rows(67, V, dtype, workload=110, stream=V)
+        z = decode(b.logits, dtype)
+        rl, rm, rls = oce.forward(z, b.targets)
+        rd = oce.grad(z, b.targets, b.g, rm, rls)
+        x = to_dev(b.logits, dtype)
+        t = torch.from_numpy(b.targets).cuda()
+        g = torch.from_numpy(b.g).cuda()
+        vec = 16 // np.dtype(np.float32 if dtype == "f32" else np.float16).itemsize
+        lanes_list = LANES + ([-1] if V % vec == 0 and V // vec in (1, 2, 4, 8) else [])
+        for lanes in lanes_list:
+            got = fused(x, t, g, lanes)
+            check_loss(got[0], rl, dtype, f"loss V={V} lanes={lanes}")
+            check_lse(got[1], rm, rls, dtype)
+            check_grad(got[2], rd, dtype, f"dlogits V={V} lanes={lanes}")
+            same_bits(got, two_calls(x, t, g, lanes))
+
+
+def test_small_vocab_rows():
+    """1,048,576 rows x 8 fp32 classes: one lane per row (the row stays in registers)."""
+    b = inputs.small_v_rows()
+    x = to_dev(b.logits, "f32")
+    t = torch.from_numpy(b.targets).cuda()
+    g = torch.from_numpy(b.g).cuda()
+    z = decode(b.logits, "f32")
+    rl, rm, rls = oce.forward(z, b.targets)
+    for lanes in (0, -1, 8):
+        got = fused(x, t, g, lanes)
+        check_loss(got[0], rl, "f32")
+        check_lse(got[1], rm, rls, "f32")
+        check_grad(got[2], oce.grad(z, b.targets, b.g, rm, rls), "f32")
+        same_bits(got, two_calls(x, t, g, lanes))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_numerics_stress(dtype):
+    """Offsets up to 1e8 (fp16: the type's range), -inf rows, equal-logit pairs."""
+    b = inputs.numerics_stress(dtype)
+    x = to_dev(b.logits, dtype)
+    t = torch.from_numpy(b.targets).cuda()
+    g = torch.from_numpy(b.g).cuda()
+    z = decode(b.logits, dtype)
+    rl, rm, rls = oce.forward(z, b.targets)
+    for lanes in (0, 64, 1024):
+        got = fused(x, t, g, lanes)
+        check_loss(got[0], rl, dtype)
+        check_lse(got[1], rm, rls, dtype)
+        check_grad(got[2], oce.grad(z, b.targets, b.g, rm, rls), dtype)
+        same_bits(got, two_calls(x, t, g, lanes))
+
+
+def test_large_vocab_bf16():
+    """2048 x 151,936 bf16: dlogits bit for bit against ce_vjp from the call's own lse
+    on every row, the oracle on every loss and on a sample of gradient rows, and
+    gradient rows summing to ~0."""
+    b = inputs.large_vocab(2048, 151936)
+    x = to_dev(b.logits, "bf16")
+    t = torch.from_numpy(b.targets).cuda()
+    g = torch.from_numpy(b.g).cuda()
+    got = fused(x, t, g)  # held in registers: 19 vectors of 16 bytes per thread
+    vjp_of_own_lse(got, x, t, g)
+    rl, rm, rls = oce.forward_stored(b.logits, "bf16", b.targets, chunk=256)
+    check_loss(got[0], rl, "bf16")
+    check_lse(got[1], rm, rls, "bf16")
+    sample = np.unique(np.concatenate([[0, 1, 2047], np.random.default_rng(1).choice(2048, 48, False)]))
+    z = decode(b.logits[sample], "bf16")
+    check_grad(got[2][sample], oce.grad(z, b.targets[sample], b.g[sample], rm[sample], rls[sample]), "bf16")
+    assert np.max(np.abs(decode(got[2], "bf16").sum(axis=1))) <= 2.0 ** -8 * 4
+
+
+def test_strided_view_and_in_place():
+    """The [B, L - 1, V] next-token view read in place, into a fresh output and over
+    the logits themselves; the excluded last positions stay untouched."""
+    gold = golden_io.read("strided_view_grad_norm.txt")
+    x, y = inputs.strided_view_source(gold["B"], gold["L"], gold["V"])
+    yv = inputs.shifted_targets(y)
+    X = torch.from_numpy(x).cuda()
+    view = X[:, :-1]
+    t = torch.from_numpy(yv).cuda()
+    g = torch.ones(len(yv), dtype=torch.float32, device="cuda")
+    got = fused(view, t, g)
+    z = decode(np.ascontiguousarray(x[:, :-1]).reshape(-1, gold["V"]), "f32")
+    rl, rm, rls = oce.forward(z, yv)
+    rd = oce.grad(z, yv, np.ones(len(yv)), rm, rls)
+    check_loss(got[0], rl, "f32")
+    check_grad(got[2].reshape(-1, gold["V"]), rd, "f32")
+    norm = float(np.sqrt(np.sum(got[2].astype(np.float64) ** 2)))
+    assert abs(round(norm, 3) - gold["grad_norm"]) <= 1e-3
+    vjp_of_own_lse(got, view, t, g)  # 8192 vectors a row: held in registers
+    assert np.array_equal(from_dev(X), x)
+    # in place
+    l2, s2, d2 = abi.ce_forward_vjp(view, t, g, dlogits=view)
+    torch.cuda.synchronize()
+    assert d2.data_ptr() == view.data_ptr()
+    assert np.array_equal(from_dev(view), got[2])
+    assert np.array_equal(bits(from_dev(l2)), bits(got[0]))
+    assert np.array_equal(from_dev(X[:, -1]), x[:, -1])
+
+
+# rows of nvec 16-byte vectors around each register count: need = ceil(nvec / 1024)
+# vectors per thread rounds up to 8, 12, 16, 20 (16-bit) or 8, 16 (fp32); past the
+# largest the row is streamed twice
+REGS_V = {"bf16": [32776, 65544, 98312, 151936, 163840, 163848],
+          "f16": [32776, 163840],
+          "f32": [16388, 32772, 65536, 65540]}
+
+
+def regs_targets(V, kvec):
+    """Both row ends, the elements around every 1024-vector boundary (where a thread's
+    next register begins) and a spread of others."""
+    step = 1024 * kvec
+    pos = [0, 1, 2, 5, 7, 8, 9, V - 1, V - 2, V - 7, V - 9]
+    pos += [q * step + d for q in range(1, V // step + 1) for d in (-1, 0, 1, 7, 8)]
+    pos += list(range(11, V, V // 7))
+    return np.array(sorted({p for p in pos if 0 <= p < V}), np.int32)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_register_rows(dtype):
+    """The register-resident layout at every register count, with rows starting on and
+    off a 16-byte boundary (the output view shares the input's phase), in place too."""
+    es = 4 if dtype == "f32" else 2
+    kvec = 16 // es
+    for V in REGS_V[dtype]:
+        y = regs_targets(V, kvec)
+        n = len(y)
+        for shift in (0, 3):
+            width = V + 16  # a row stride of a whole number of 16-byte vectors
+            b = inputs.normal_rows(n, width, dtype, workload=112, stream=V + shift)
+            full = to_dev(b.logits, dtype)
+            view = full[:, shift:shift + V]
+            z = decode(b.logits[:, shift:shift + V], dtype)
+            g = np.linspace(-1.5, 2.0, n).astype(np.float32)
+            rl, rm, rls = oce.forward(z, y)
+            rd = oce.grad(z, y, g, rm, rls)
+            t = torch.from_numpy(y).cuda()
+            gd = torch.from_numpy(g).cuda()
+            out = torch.empty(n, width, dtype=TORCH_DT[dtype], device="cuda")[:, shift:shift + V]
+            got = fused(view, t, gd, dlogits=out)
+            check_loss(got[0], rl, dtype, f"loss V={V} shift={shift}")
+            check_lse(got[1], rm, rls, dtype)
+            check_grad(got[2], rd, dtype, f"dlogits V={V} shift={shift}")
+            vjp_of_own_lse(got, view, t, gd)
+            # in place over the logits view gives the same bits
+            got2 = fused(view, t, gd, dlogits=view)
+            same_bits(got2, got)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_misaligned_rows(dtype):
+    """Views off a 16-byte boundary, and an output in another 16-byte phase."""
+    for shift in (1, 3):
+        for V in (5, 64, 1000, 4099, 20483):
+            b = inputs.normal_rows(33, V + shift + 2, dtype, workload=111, stream=V)
+            view = to_dev(b.logits, dtype)[:, shift:shift + V]
+            zs = decode(b.logits[:, shift:shift + V], dtype)
+            y = b.targets % V
+            t = torch.from_numpy(y).cuda()
+            g = torch.from_numpy(b.g).cuda()
+            rl, rm, rls = oce.forward(zs, y)
+            rd = oce.grad(zs, y, b.g, rm, rls)
+            for lanes in (0, 1, 16, 256):
+                out = torch.empty(33, V + 1, dtype=TORCH_DT[dtype], device="cuda")[:, 1:]
+                for dl in (None, out):
+                    got = fused(view, t, g, lanes, dlogits=dl)
+                    check_loss(got[0], rl, dtype)
+                    check_grad(got[2], rd, dtype, f"dlogits V={V} shift={shift} lanes={lanes}")
+                    same_bits(got, two_calls(view, t, g, lanes))
+
+
+def test_degenerate_rows():
+    """Out-of-range targets, all -inf, +inf and NaN entries: NaN loss and gradient rows;
+    a row with only its target finite: loss 0; a -inf target: loss +inf."""
+    V = 300
+    x = np.random.default_rng(5).standard_normal((8, V)).astype(np.float32)
+    y = np.array([0, -1, V, 7, 1, 2, 3, 4], np.int32)
+    x[3] = -np.inf
+    x[4, 10] = np.inf
+    x[5, 11] = np.nan
+    x[6, :] = -np.inf
+    x[6, 3] = 2.5
+    x[7, 4] = -np.inf
+    X = to_dev(x, "f32")
+    t = torch.from_numpy(y).cuda()
+    g = torch.full((8,), 1.5, device="cuda")
+    for lanes in (0, 1, 64, 256):
+        loss, lse, d = fused(X, t, g, lanes)
+        assert np.all(np.isnan(loss[1:6])) and np.all(np.isnan(d[1:6]))
+        assert loss[6] == 0.0 and np.all(d[6] == 0.0)
+        assert loss[7] == np.inf and d[7, 4] == -1.5 and np.all(np.isfinite(d[7]))
+        z = decode(x[[0, 7]], "f32")
+        check_grad(d[[0, 7]], oce.grad(z, y[[0, 7]], np.full(2, 1.5)), "f32")
+
+
+def test_huge_row_count():
+    """2^27 + 2^20 rows x 8 fp32 classes: past 2^32 threads at 32 threads per row."""
+    gold = golden_io.read("huge_rows.txt")
+    n = gold["rows_fail"]
+    b = inputs.huge_rows(n, gold["classes"])
+    x = to_dev(b.logits, "f32")
+    t = torch.from_numpy(b.targets).cuda()
+    g = torch.ones(n, dtype=torch.float32, device="cuda")
+    loss = torch.full((n,), float("nan"), device="cuda")
+    lse = torch.full((n, 2), float("nan"), device="cuda")
+    d = torch.full_like(x, float("nan"))
+    abi.ce_forward_vjp(x, t, g, loss=loss, lse=lse, dlogits=d)
+    torch.cuda.synchronize()
+    assert not torch.isnan(loss).any().item()
+    assert not torch.isnan(d).any().item()
+    first = gold["first_wrong_row_when_wrapped"]
+    rows = np.unique(np.concatenate([
+        np.arange(0, 64), np.arange(first - 64, first + 64), np.arange(n - 64, n), np.arange(0, n, 997)]))
+    z = decode(b.logits[rows], "f32")
+    rl, rm, rls = oce.forward(z, b.targets[rows])
+    idx = torch.from_numpy(rows).cuda()
+    check_loss(from_dev(loss[idx]), rl, "f32")
+    check_lse(from_dev(lse[idx]), rm, rls, "f32")
+    check_grad(from_dev(d[idx]), oce.grad(z, b.targets[rows], np.ones(len(rows)), rm, rls), "f32")
+
+
+def test_empty_batch_and_rejections():
+    x = torch.empty(0, 128, device="cuda")
+    t = torch.empty(0, dtype=torch.int32, device="cuda")
+    loss, lse, d = abi.ce_forward_vjp(x, t, torch.empty(0, device="cuda"))
+    assert loss.numel() == 0 and d.shape == (0, 128)
+    x = torch.randn(16, 64, device="cuda")
+    t = torch.zeros(16, dtype=torch.int32, device="cuda")
+    g = torch.ones(16, device="cuda")
+    buf = torch.empty(16 * 64 + 64, device="cuda")
+    cases = [
+        dict(x=x[:, :32], dlogits=x[:, 32:]),                 # output overlaps the logits
+        dict(x=x, loss=x.view(-1)[:16]),                        # loss inside the logits
+        dict(x=x, lse=buf[:32].view(16, 2), dlogits=buf[:1024].view(16, 64)),  # two outputs overlap
+    ]
+    for c in cases:
+        with pytest.raises(abi.CEError) as e:
+            abi.ce_forward_vjp(c["x"], t, g, loss=c.get("loss"), lse=c.get("lse"), dlogits=c.get("dlogits"))
+        assert e.value.status == -7
+    with pytest.raises(abi.CEError) as e:  # one lane per row needs short aligned rows
+        abi.ce_forward_vjp(torch.randn(4, 100, device="cuda"), t[:4], g[:4], lanes_per_row=-1)
+    assert e.value.status == -4
