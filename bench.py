@@ -48,50 +48,54 @@ CSRC = os.path.join(ROOT, "softmax_cross_entropy_amd", "csrc")
 # copy of known size; see profiles/.  Keyed by the sha256 of the kernel's source file
 # and headers at measurement time: a changed kernel reports traffic null until it is measured again.
 TRAFFIC = {
+    "ce_forward_vjp": {
+        "source_sha": "9dc3062d21cff818",
+        "bytes": 1278933873
+    },
     "ce_forward": {
-        "source_sha": "8fff8ae9f765ddd5",
-        "bytes": 622632289
+        "source_sha": "9dc3062d21cff818",
+        "bytes": 622629120
     },
     "ce_vjp": {
-        "source_sha": "8fff8ae9f765ddd5",
-        "bytes": 1245000923
+        "source_sha": "9dc3062d21cff818",
+        "bytes": 1245013817
     },
     "lce_forward": {
-        "source_sha": "784936aa4c391cbe",
-        "bytes": 15159957315
+        "source_sha": "e2287f29fdb0f37a",
+        "bytes": 15153861679
     },
     "kl_forward": {
-        "source_sha": "48529b2dec4f5015",
-        "bytes": 622509410
+        "source_sha": "e99c62d129ca65ee",
+        "bytes": 622509249
     },
     "kl_vjp": {
-        "source_sha": "48529b2dec4f5015",
-        "bytes": 933662945
+        "source_sha": "e99c62d129ca65ee",
+        "bytes": 933664575
     },
     "ce_forward_ex": {
-        "source_sha": "4ee7710e8505ad5a",
-        "bytes": 622627617
+        "source_sha": "fd46a070d3e3f5c8",
+        "bytes": 622627200
     },
     "ce_vjp_ex": {
-        "source_sha": "4ee7710e8505ad5a",
-        "bytes": 1206058590
+        "source_sha": "fd46a070d3e3f5c8",
+        "bytes": 1206061487
     },
     "ce_forward_probs": {
-        "source_sha": "4ee7710e8505ad5a",
-        "bytes": 622490019
+        "source_sha": "fd46a070d3e3f5c8",
+        "bytes": 622489922
     },
     "ce_vjp_probs": {
-        "source_sha": "4ee7710e8505ad5a",
-        "bytes": 933601251
+        "source_sha": "fd46a070d3e3f5c8",
+        "bytes": 933601474
     },
     "js_forward": {
-        "source_sha": "636dff21e4e490f5",
-        "bytes": 1224875037
+        "source_sha": "9141875e3f66e2e8",
+        "bytes": 1224756024
     },
     "js_vjp": {
-        "source_sha": "636dff21e4e490f5",
-        "bytes": 936252931
-    },
+        "source_sha": "9141875e3f66e2e8",
+        "bytes": 936542808
+    }
 }
 
 
