@@ -178,9 +178,9 @@ ce_status ce_vjp_lanes(const void* logits, ce_layout in, ce_dtype dt, const int3
  * target logit, and the backward only that log-sum-exp; "One barrier short", first
  * section: mlx-lm computes its divergences and their gradients in one fused pass so
  * that the log-softmax rows never exist in memory.  Each row's
- * Rows of more than 4096 and at most 20480 16-byte vectors (16384 for fp32) whose
+ * Rows of more than 2048 and at most 20480 16-byte vectors (16384 for fp32) whose
  * input and output rows share their 16-byte phase are held in the registers of one
- * 1024-thread workgroup: the row max and the sum of exponentials are two passes over
+ * workgroup of 512 or 1024 threads: the row max and the sum of exponentials are two passes over
  * those registers and the gradient a third, so HBM carries one read and one write of
  * the logits instead of ce_forward's read plus ce_vjp's read and write.  Other rows
  * are reduced as ce_forward reduces them and then swept a second time by the same

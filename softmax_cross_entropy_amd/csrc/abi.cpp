@@ -292,13 +292,16 @@ ce_status fused_impl(const void* logits, ce_layout in, ce_dtype dt, const int32_
                            V % vec == 0 && (V / vec == 1 || V / vec == 2 || V / vec == 4 || V / vec == 8);
     Plan plan;
     if (ce_status s = make_plan(narrow_ok, V, es, n_rows, lanes, false, cus, &plan)) return s;
-    // Rows the forward gives a 1024-thread workgroup, whose input and output rows share
-    // their 16-byte phase, and that fit in 1024 threads' registers: the register-resident
+    // Rows the forward gives a 512- or 1024-thread workgroup, whose input and output rows share
+    // their 16-byte phase, and that fit in those threads' registers: the register-resident
     // kernel, which folds in the same order.
-    if (lanes == 0 && plan.lanes == 1024 && same_phase_rows(logits, in, dlogits, out, n_rows, es)) {
-        const int64_t need = ((V + vec - 1) / vec + 1023) / 1024;
-        const int* nvs = es == 4 ? ce::kRegsNV32 : ce::kRegsNV16;
-        const int cnt = es == 4 ? (int)(sizeof(ce::kRegsNV32) / sizeof(int)) : (int)(sizeof(ce::kRegsNV16) / sizeof(int));
+    if (lanes == 0 && (plan.lanes == 512 || plan.lanes == 1024) && plan.narrow_nv == 0 &&
+        same_phase_rows(logits, in, dlogits, out, n_rows, es)) {
+        const int64_t need = ((V + vec - 1) / vec + plan.lanes - 1) / plan.lanes;
+        const int* nvs = plan.lanes == 512 ? ce::kRegsNV512 : es == 4 ? ce::kRegsNV32 : ce::kRegsNV16;
+        const int cnt = plan.lanes == 512 ? 1
+                        : es == 4 ? (int)(sizeof(ce::kRegsNV32) / sizeof(int))
+                                  : (int)(sizeof(ce::kRegsNV16) / sizeof(int));
         for (int i = 0; i < cnt; ++i) {
             if (need <= nvs[i]) {
                 plan.regs_nv = nvs[i];

@@ -526,9 +526,9 @@ __global__ __launch_bounds__(G > kBlock ? G : kBlock) void ce_fused_rows(FusedAr
     }
 }
 
-// Rows of up to 1024 * NV vectors whose input and output share a 16-byte phase: one
-// workgroup of 1024 threads per row, and the whole row is loaded into registers at
-// once: vector j = tid + k * 1024 sits in buf[k], the row's unaligned head and tail
+// Rows of up to G * NV vectors whose input and output share a 16-byte phase: one
+// workgroup of G threads (the forward's lanes for the row: 512 or 1024) per row, and the
+// whole row is loaded into registers at once: vector j = tid + k * G sits in buf[k], the row's unaligned head and tail
 // elements in one register each of threads 0 .. ns - 1.  With the row in registers
 // the max and the sum are two passes over them (m = max z, then s = sum exp(z - m)),
 // each with its own exchange through LDS, rather than the online fold: the fold's
@@ -563,10 +563,9 @@ __device__ __forceinline__ void opaque(U4 (&buf)[NV]) {
         for (int e = 0; e < 4; ++e) __asm__ volatile("" : "+v"(buf[k].w[e]));
 }
 
-template <typename T, int NV>
-__global__ __launch_bounds__(1024) void ce_fused_regs(FusedArgs a) {
+template <typename T, int G, int NV>
+__global__ __launch_bounds__(G) void ce_fused_regs(FusedArgs a) {
     constexpr int kVec = Elem<T>::kVec;
-    constexpr int G = 1024;
     constexpr int NW = G / 64;
     // Two exchanges per row, each with its own slots.  A wave writes the max slots of the
     // next row only after the sum barrier of this row, which every wave reaches after
@@ -588,7 +587,7 @@ __global__ __launch_bounds__(1024) void ce_fused_regs(FusedArgs a) {
     // checks the strides), so every row has the same head and vector count.
     const T* row = static_cast<const T*>(a.logits) + row_offset(r, a.in);
     const RowSplit<T> sp(row, a.V);
-    const int nvec = (int)sp.nvec;  // at most 1024 * NV
+    const int nvec = (int)sp.nvec;  // at most G * NV
     const int64_t ns = sp.n_scalar(a.V);
     const int64_t sidx = tid < ns ? sp.scalar_index(tid) : 0;
     U4 buf[NV];
@@ -664,7 +663,7 @@ __global__ __launch_bounds__(1024) void ce_fused_regs(FusedArgs a) {
             __builtin_amdgcn_make_buffer_rsrc((void*)(nrow + sp.head), (short)0, nvec * 16, 0x00020000);
         const __amdgpu_buffer_rsrc_t dst =
             __builtin_amdgcn_make_buffer_rsrc((void*)(orow + sp.head), (short)0, nvec * 16, 0x00020000);
-        // in 32 bits: the row holds at most 1024 * NV * kVec elements
+        // in 32 bits: the row holds at most G * NV * kVec elements
         const int rel0 = rg.y - (int)sp.head - tid * kVec;
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
@@ -795,19 +794,24 @@ hipError_t fused_typed(const FusedCall& c) {
         }
         return hipGetLastError();
     }
+    if (c.plan.regs_nv > 0 && c.plan.lanes == 512) {
+        if (c.plan.regs_nv != 8) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((ce_fused_regs<T, 512, 8>), grid, dim3(512), 0, c.stream, a);
+        return hipGetLastError();
+    }
     if (c.plan.regs_nv > 0) {
         if constexpr (Elem<T>::kVec == 8) {
             switch (c.plan.regs_nv) {
-                case 8: hipLaunchKernelGGL((ce_fused_regs<T, 8>), grid, dim3(1024), 0, c.stream, a); break;
-                case 12: hipLaunchKernelGGL((ce_fused_regs<T, 12>), grid, dim3(1024), 0, c.stream, a); break;
-                case 16: hipLaunchKernelGGL((ce_fused_regs<T, 16>), grid, dim3(1024), 0, c.stream, a); break;
-                case 20: hipLaunchKernelGGL((ce_fused_regs<T, 20>), grid, dim3(1024), 0, c.stream, a); break;
+                case 8: hipLaunchKernelGGL((ce_fused_regs<T, 1024, 8>), grid, dim3(1024), 0, c.stream, a); break;
+                case 12: hipLaunchKernelGGL((ce_fused_regs<T, 1024, 12>), grid, dim3(1024), 0, c.stream, a); break;
+                case 16: hipLaunchKernelGGL((ce_fused_regs<T, 1024, 16>), grid, dim3(1024), 0, c.stream, a); break;
+                case 20: hipLaunchKernelGGL((ce_fused_regs<T, 1024, 20>), grid, dim3(1024), 0, c.stream, a); break;
                 default: return hipErrorInvalidValue;
             }
         } else {
             switch (c.plan.regs_nv) {
-                case 8: hipLaunchKernelGGL((ce_fused_regs<T, 8>), grid, dim3(1024), 0, c.stream, a); break;
-                case 16: hipLaunchKernelGGL((ce_fused_regs<T, 16>), grid, dim3(1024), 0, c.stream, a); break;
+                case 8: hipLaunchKernelGGL((ce_fused_regs<T, 1024, 8>), grid, dim3(1024), 0, c.stream, a); break;
+                case 16: hipLaunchKernelGGL((ce_fused_regs<T, 1024, 16>), grid, dim3(1024), 0, c.stream, a); break;
                 default: return hipErrorInvalidValue;
             }
         }

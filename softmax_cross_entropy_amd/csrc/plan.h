@@ -15,8 +15,8 @@ struct Plan {
     int lanes;
     int64_t blocks;
     int64_t chunks;  // VJP only: > 0 cuts each row into this many chunks of kChunkU * 256 vectors
-    int regs_nv;     // ce_forward_vjp only: > 0 holds each row in the registers of 1024 threads,
-                     // regs_nv 16-byte vectors per thread (see kRegsNV)
+    int regs_nv;     // ce_forward_vjp only: > 0 holds each row in the registers of `lanes`
+                     // threads, regs_nv 16-byte vectors per thread (see kRegsNV16)
 };
 
 // Vectors per thread the register-resident one-pass kernel is built for: 16-bit types
@@ -24,6 +24,8 @@ struct Plan {
 // smallest that holds it, ceil(nvec / 1024) <= regs_nv.
 constexpr int kRegsNV16[] = {8, 12, 16, 20};
 constexpr int kRegsNV32[] = {8, 16};
+// Rows the forward gives 512 lanes (2049 to 4096 vectors) take 512 threads of 8 vectors.
+constexpr int kRegsNV512[] = {8};
 
 // Vectors per thread in one chunk of the chunked VJP layout.
 constexpr int kChunkU = 2;

@@ -6,7 +6,7 @@ and against the library's two calls:
   lanes, or whose output is in another 16-byte phase), it folds each row in the
   forward's order, so loss, lse and dlogits equal ce_forward followed by ce_vjp bit for
   bit;
-* where it holds the row in registers (rows of more than 4096 16-byte vectors, up to
+* where it holds the row in registers (rows of more than 2048 16-byte vectors, up to
   20480 for 16-bit types and 16384 for fp32, input and output in one phase) it takes
   the max and the sum in two passes, so its lse differs from ce_forward's by float32
   rounding; its dlogits still equal ce_vjp's given that lse, bit for bit.
@@ -158,12 +158,13 @@ def test_strided_view_and_in_place():
     assert np.array_equal(from_dev(X[:, -1]), x[:, -1])
 
 
-# rows of nvec 16-byte vectors around each register count: need = ceil(nvec / 1024)
-# vectors per thread rounds up to 8, 12, 16, 20 (16-bit) or 8, 16 (fp32); past the
-# largest the row is streamed twice
-REGS_V = {"bf16": [32776, 65544, 98312, 151936, 163840, 163848],
-          "f16": [32776, 163840],
-          "f32": [16388, 32772, 65536, 65540]}
+# rows of nvec 16-byte vectors around each register count: rows of 2049 to 4096 vectors
+# take 512 threads of 8 vectors; longer rows 1024 threads of need = ceil(nvec / 1024)
+# vectors rounded up to 8, 12, 16, 20 (16-bit) or 8, 16 (fp32); past the largest the row
+# is streamed twice
+REGS_V = {"bf16": [16392, 32000, 32768, 32776, 65544, 98312, 151936, 163840, 163848],
+          "f16": [20000, 32776, 163840],
+          "f32": [8196, 16384, 16388, 32772, 65536, 65540]}
 
 
 def regs_targets(V, kvec):
