@@ -112,6 +112,37 @@ def test_vjp_aliasing():
     assert vjp(out=ctypes.c_void_p(4 * A - 16)) == ALIAS  # output runs into lse
 
 
+def fvj(logits=P_LOGITS, layout=None, dt=0, t=P_T, g=P_G, n=16, V=8, loss=P_LOSS, lse=P_LSE, out=P_OUT,
+        olayout=None, lanes=0):
+    layout = layout or lay(n, V)
+    olayout = olayout or lay(n, V)
+    return abi.lib().ce_forward_vjp_lanes(logits, layout, dt, t, g, n, V, loss, lse, out, olayout, lanes, None)
+
+
+def test_forward_vjp_rejects_bad_arguments():
+    for k in ("logits", "t", "g", "loss", "lse", "out"):
+        assert fvj(**{k: None}) == NULL, k
+    assert fvj(V=0) == SHAPE
+    assert fvj(V=1 << 31) == SHAPE
+    assert fvj(n=-1) == SHAPE
+    assert fvj(lanes=3) == SHAPE
+    assert fvj(dt=3) == DTYPE
+    assert fvj(olayout=abi.CELayout(16, 4, 64)) == LAYOUT  # output rows overlap
+    assert fvj(g=ctypes.c_void_p(5 * A + 2)) == LAYOUT
+    assert fvj(lse=ctypes.c_void_p(4 * A + 4)) == LAYOUT
+    assert fvj(n=0, logits=None, t=None, g=None, loss=None, lse=None, out=None) == OK
+
+
+def test_forward_vjp_aliasing():
+    assert fvj(out=ctypes.c_void_p(A + 64)) == ALIAS  # dlogits overlap the logits
+    assert fvj(out=P_LOGITS, olayout=lay(16, 16, 256), layout=lay(16, 8, 128)) == ALIAS
+    assert fvj(loss=ctypes.c_void_p(A + 64)) == ALIAS  # loss inside the logits
+    assert fvj(lse=ctypes.c_void_p(5 * A)) == ALIAS  # lse over g
+    assert fvj(out=ctypes.c_void_p(2 * A - 16)) == ALIAS  # dlogits run into the targets
+    assert fvj(loss=ctypes.c_void_p(6 * A + 64)) == ALIAS  # loss inside dlogits
+    assert fvj(lse=ctypes.c_void_p(3 * A + 32)) == ALIAS  # lse over loss
+
+
 def lce(H=P_LOGITS, W=P_W, t=P_T, N=32, D=64, V=1000, loss=P_LOSS, lse=P_LSE, ws=P_WS, wsb=None):
     if wsb is None:
         wsb = abi.lce_workspace_size(N, D, V)
@@ -298,6 +329,8 @@ def test_options_reject_bad_arguments():
 def test_valid_call_without_device_reports_device_error():
     assert fwd() == DEVICE
     assert vjp() == DEVICE
+    assert fvj() == DEVICE
+    assert fvj(out=P_LOGITS) == DEVICE  # in place with the same layout is allowed
     assert lce() == DEVICE
     assert lbw() == DEVICE
     assert lbw(H=None, t=None, lse=None, g=None, dH=None, ws=None, N=0, wsb=0) == DEVICE
