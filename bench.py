@@ -50,51 +50,51 @@ CSRC = os.path.join(ROOT, "softmax_cross_entropy_amd", "csrc")
 TRAFFIC = {
     "ce_forward_vjp": {
         "source_sha": "99c755947d60a7be",
-        "bytes": 1278931721
+        "bytes": 1278932614
     },
     "ce_forward": {
         "source_sha": "99c755947d60a7be",
-        "bytes": 622628376
+        "bytes": 622630005
     },
     "ce_vjp": {
         "source_sha": "99c755947d60a7be",
-        "bytes": 1245012273
+        "bytes": 1245011439
     },
     "lce_forward": {
         "source_sha": "60bb36e2a858e5cf",
-        "bytes": 15153447962
+        "bytes": 15154422166
     },
     "kl_forward": {
         "source_sha": "7d0597161c5dd882",
-        "bytes": 622501434
+        "bytes": 622488055
     },
     "kl_vjp": {
         "source_sha": "7d0597161c5dd882",
-        "bytes": 933633721
+        "bytes": 933634166
     },
     "ce_forward_ex": {
         "source_sha": "1ae1bc11d9d59da5",
-        "bytes": 622627064
+        "bytes": 622627126
     },
     "ce_vjp_ex": {
         "source_sha": "1ae1bc11d9d59da5",
-        "bytes": 1206059336
+        "bytes": 1206061289
     },
     "ce_forward_probs": {
         "source_sha": "1ae1bc11d9d59da5",
-        "bytes": 622490394
+        "bytes": 622503735
     },
     "ce_vjp_probs": {
         "source_sha": "1ae1bc11d9d59da5",
-        "bytes": 933600954
+        "bytes": 933601400
     },
     "js_forward": {
         "source_sha": "f1f68c852e71124b",
-        "bytes": 1224897876
+        "bytes": 1224732231
     },
     "js_vjp": {
         "source_sha": "f1f68c852e71124b",
-        "bytes": 936309079
+        "bytes": 936533902
     }
 }
 
@@ -130,8 +130,9 @@ def ce_bytes(rows, V, e):
     return fwd, vjp
 
 
-# the second one-kernel workload: rows the forward gives 512 lanes
-F2_ROWS, F2_V = 8192, 32000
+# the other one-kernel workloads: rows the forward gives 512 lanes (held in registers), and
+# short rows on 32 lanes (swept twice)
+F_SHAPES = (("bf16 [8192 x 32000]", 8192, 32000, "bf16"), ("f32 [65536 x 1024]", 65536, 1024, "f32"))
 
 
 def fused_bytes(rows, V, e):
@@ -446,26 +447,31 @@ def main():
             abi.ce_forward_vjp(X[i % 2], T, G, loss=loss, lse=lse, dlogits=dX)
 
         fused_ms = {"clean": timed_one(fused_call, pre=clean_cache), "back_to_back": timed_one(fused_call)}
-        # bf16 [8192 x 32,000]: rows of 4000 vectors, held by 512-thread workgroups; three
-        # input copies rotate so no call finds its logits in the Infinity Cache
-        sb = inputs.normal_rows(F2_ROWS, F2_V, "bf16", workload=90)
-        SX = [up(sb.logits, True) for _ in range(3)]
-        ST2, SG2 = up(sb.targets), up(sb.g)
-        s_l, s_s, s_d = torch.empty(F2_ROWS, device=dev), torch.empty(F2_ROWS, 2, device=dev), torch.empty_like(SX[0])
-        del sb
+        # more shapes: bf16 [8192 x 32,000] (rows of 4000 vectors, held by 512-thread
+        # workgroups) and fp32 [65,536 x 1024] (rows of 256 vectors on 32 lanes, swept
+        # twice); three input copies rotate so no call finds its logits in the Infinity Cache
+        fused_ms["shapes"] = []
+        for label, f_rows, f_v, f_dt in F_SHAPES:
+            sb = inputs.normal_rows(f_rows, f_v, f_dt, workload=90)
+            SX = [up(sb.logits, f_dt == "bf16") for _ in range(3)]
+            ST2, SG2 = up(sb.targets), up(sb.g)
+            s_l, s_s, s_d = torch.empty(f_rows, device=dev), torch.empty(f_rows, 2, device=dev), torch.empty_like(SX[0])
+            del sb
 
-        def f2_fused(i):
-            abi.ce_forward_vjp(SX[i % 3], ST2, SG2, loss=s_l, lse=s_s, dlogits=s_d)
+            def f2_fused(i):
+                abi.ce_forward_vjp(SX[i % 3], ST2, SG2, loss=s_l, lse=s_s, dlogits=s_d)
 
-        def f2_fwd(i):
-            abi.ce_forward(SX[i % 3], ST2, loss=s_l, lse=s_s)
+            def f2_fwd(i):
+                abi.ce_forward(SX[i % 3], ST2, loss=s_l, lse=s_s)
 
-        def f2_vjp(i):
-            abi.ce_vjp(SX[i % 3], ST2, s_s, SG2, dlogits=s_d)
+            def f2_vjp(i):
+                abi.ce_vjp(SX[i % 3], ST2, s_s, SG2, dlogits=s_d)
 
-        fused_ms["f2"] = {"clean": timed_one(f2_fused, pre=clean_cache), "back_to_back": timed_one(f2_fused),
-                          "two_calls": both_states(f2_fwd, f2_vjp)}
-        del SX, s_d
+            fused_ms["shapes"].append((label, f_rows, f_v, 4 if f_dt == "f32" else 2,
+                                       {"clean": timed_one(f2_fused, pre=clean_cache),
+                                        "back_to_back": timed_one(f2_fused),
+                                        "two_calls": both_states(f2_fwd, f2_vjp)}))
+            del SX, s_d
 
     kl_ms = None
     if "kl" in parts:
@@ -658,14 +664,14 @@ def main():
                 "back_to_back": {"ms": tb, "GB_s": rate(ub, tb), "frac_hbm_peak": rate(ub, tb) / HBM_PEAK_GBS,
                                  "vs_two_calls": (ce_b2b[0] + ce_b2b[1]) / tb},
                 "note": "one kernel for a g known before the forward: each row read from HBM once"}
-            f2 = fused_ms["f2"]
-            ub2 = fused_bytes(F2_ROWS, F2_V, 2)
-            two_c, two_b = sum(f2["two_calls"]["clean"]), sum(f2["two_calls"]["back_to_back"])
-            parts_out["ce_forward_vjp"]["bf16 [8192 x 32000]"] = {
-                "ms": f2["clean"], "GB_s": rate(ub2, f2["clean"]), "algorithmic_bytes": ub2,
-                "two_calls_ms": two_c, "vs_two_calls": two_c / f2["clean"],
-                "back_to_back": {"ms": f2["back_to_back"], "GB_s": rate(ub2, f2["back_to_back"]),
-                                 "two_calls_ms": two_b, "vs_two_calls": two_b / f2["back_to_back"]}}
+            for label, f_rows, f_v, f_e, f2 in fused_ms["shapes"]:
+                ub2 = fused_bytes(f_rows, f_v, f_e)
+                two_c, two_b = sum(f2["two_calls"]["clean"]), sum(f2["two_calls"]["back_to_back"])
+                parts_out["ce_forward_vjp"][label] = {
+                    "ms": f2["clean"], "GB_s": rate(ub2, f2["clean"]), "algorithmic_bytes": ub2,
+                    "two_calls_ms": two_c, "vs_two_calls": two_c / f2["clean"],
+                    "back_to_back": {"ms": f2["back_to_back"], "GB_s": rate(ub2, f2["back_to_back"]),
+                                     "two_calls_ms": two_b, "vs_two_calls": two_b / f2["back_to_back"]}}
             a = rate(ub, tb)
             rooflines["ce_forward_vjp"] = {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                            "frac": a / HBM_PEAK_GBS, "traffic": traffic_for("ce_forward_vjp"),
