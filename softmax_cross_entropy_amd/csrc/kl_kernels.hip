@@ -10,11 +10,19 @@
 // array for two exchanges without a barrier between them).
 //
 // One pass per row keeps, per lane, the online pair (m_q, s_q) of the student, the
-// pair (m_p, s_p) of the teacher and t = sum_j exp(p_j - m_p) (p_j - q_j), rescaled
-// with s_p.  Since sum_j softmax(p)_j = 1,
-//   kl = t / s_p - (m_p + log s_p) + (m_q + log s_q),
-// so neither log-softmax is ever materialised.  A teacher entry whose weight
-// exp(p_j - m_p) is 0 (p_j = -inf) contributes nothing to t (0 log 0 = 0).
+// pair (m_p, s_p) of the teacher and
+//   t = sum_j exp(p_j - m_p) ((p_j - m_p) - (q_j - m_q)),
+// each logit taken against its own row's running maximum and t rescaled with s_p.
+// Since sum_j softmax(p)_j = 1,
+//   kl = t / s_p - log s_p + log s_q,
+// so neither log-softmax is ever materialised.  Every term of t is a difference of
+// logits of one row, so t / s_p stays of the size of the rows' spread whatever offset
+// either row carries: a sum over the raw differences p_j - q_j would carry the offset
+// gap m_p - m_q and cancel it against the maxima at the end, losing the result in
+// float32 once that gap reaches 1e4.  When a maximum moves, the terms already in t
+// shift by the move: t' = c (t + s_p ((m_p - m_p') - (m_q - m_q'))), c = exp(m_p - m_p').
+// A teacher entry whose weight exp(p_j - m_p) is 0 (p_j = -inf) contributes nothing
+// to t (0 log 0 = 0).
 //
 // Row layouts as in the cross-entropy kernels: G lanes per row (G <= 64, 64 / G rows
 // per wavefront) or one workgroup of 64 * NW threads per row, whose waves exchange
@@ -33,10 +41,20 @@ constexpr int kBlock = 256;
 struct KLState {
     float mq, sq;  // student: running max and sum exp(q - mq)
     float mp, sp;  // teacher: running max and sum exp(p - mp)
-    float t;       // sum exp(p - mp) (p - q), rescaled with sp
+    float t;       // sum exp(p - mp) ((p - mp) - (q - mq)), rescaled with sp
 };
 
 __device__ __forceinline__ KLState kl_empty() { return KLState{kNegInf, 0.f, kNegInf, 0.f, 0.f}; }
+
+// The terms already in t, taken against the reference points (rq, rp), moved to the
+// reference points (nq, np): each term gains (rp - np) - (rq - nq), and the teacher
+// weights scale by c = exp(rp - np).  Reference points are ref_point of the maxima, so
+// an empty state (s_p = 0, t = 0) moves to any point without forming -inf - -inf.
+__device__ __forceinline__ float kl_shift_t(float t, float sp, float rq, float rp, float nq, float np_,
+                                            float c) {
+#pragma clang fp contract(off)
+    return __fmul_rn(t + __fmul_rn(sp, (rp - np_) - (rq - nq)), c);
+}
 
 // Folds N pairs (q_k, p_k) into the state with one rescale per distribution.
 template <int N>
@@ -52,15 +70,17 @@ __device__ __forceinline__ void kl_add(KLState& st, const float (&q)[N], const f
     float sq = 0.f, sp = 0.f, t = 0.f;
 #pragma unroll
     for (int k = 0; k < N; ++k) {
-        sq += exp_e(q[k] - rq);
-        const float w = exp_e(p[k] - rp);
+        const float dq = q[k] - rq;
+        sq += exp_e(dq);
+        const float dp = p[k] - rp;
+        const float w = exp_e(dp);
         sp += w;
-        t += w > 0.f ? w * (p[k] - q[k]) : 0.f;
+        t += w > 0.f ? w * (dp - dq) : 0.f;
     }
     const float cp = exp_e(st.mp - rp);
+    st.t = kl_shift_t(st.t, st.sp, ref_point(st.mq), ref_point(st.mp), rq, rp, cp) + t;
     st.sq = __fmul_rn(st.sq, exp_e(st.mq - rq)) + sq;
     st.sp = __fmul_rn(st.sp, cp) + sp;
-    st.t = __fmul_rn(st.t, cp) + t;
     st.mq = mq;
     st.mp = mp;
 }
@@ -74,10 +94,11 @@ __device__ __forceinline__ KLState kl_merge(const KLState& a, const KLState& b) 
     o.mq = q.m;
     o.sq = q.s;
     o.mp = fmaxf(a.mp, b.mp);
-    const float r = ref_point(o.mp);
-    const float ca = exp_e(a.mp - r), cb = exp_e(b.mp - r);
+    const float rq = ref_point(o.mq), rp = ref_point(o.mp);
+    const float ca = exp_e(a.mp - rp), cb = exp_e(b.mp - rp);
     o.sp = __fmul_rn(a.sp, ca) + __fmul_rn(b.sp, cb);
-    o.t = __fmul_rn(a.t, ca) + __fmul_rn(b.t, cb);
+    o.t = kl_shift_t(a.t, a.sp, ref_point(a.mq), ref_point(a.mp), rq, rp, ca) +
+          kl_shift_t(b.t, b.sp, ref_point(b.mq), ref_point(b.mp), rq, rp, cb);
     return o;
 }
 
@@ -106,7 +127,7 @@ struct KLFwdArgs {
 
 __device__ __forceinline__ void kl_store(const KLFwdArgs& a, int64_t r, const KLState& st) {
     const float lsq = log_e(st.sq), lsp = log_e(st.sp);
-    a.kl[r] = st.t / st.sp + ((st.mq - st.mp) + (lsq - lsp));
+    a.kl[r] = st.t / st.sp + (lsq - lsp);
     a.lse_q[r] = make_float2(st.mq, lsq);
     a.lse_p[r] = make_float2(st.mp, lsp);
 }

@@ -291,3 +291,17 @@ def kl_pair(rows: int, V: int, dtype: str, scale: float = 4.0, workload: int = 2
     q = encode(normal_f32(gen, (rows, V), scale), dtype)
     p = encode(normal_f32(gen, (rows, V), scale), dtype)
     return q, p, np.ones(rows, np.float32)
+
+
+def with_row_offsets(x: np.ndarray, dtype: str, offsets, workload: int, stream: int = 0):
+    """Stored logits ``x`` [rows, V] plus one offset per row drawn uniformly from
+    ``offsets``, added in float64 to the stored values and stored again in ``dtype``.
+    Returns (stored rows, the offset of each row).  "Shift by the max in cross_entropy",
+    Proposed changes: results must not depend on a shared offset of a row's logits."""
+    gen = rng(workload, stream)
+    off = np.asarray(offsets, np.float64)[gen.integers(0, len(offsets), size=x.shape[0])]
+    if dtype == BF16:
+        base = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    else:
+        base = x.astype(np.float64)
+    return encode((base + off[:, None]).astype(np.float32), dtype), off
