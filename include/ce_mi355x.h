@@ -124,20 +124,6 @@ ce_status ce_forward(const void* logits, ce_layout in, ce_dtype dt, const int32_
                      int64_t n_rows, int64_t V, float* loss, float* lse, hipStream_t stream);
 
 /*
- * ce_forward_lanes: ce_forward with the row-to-lane mapping chosen by the caller.
- * lanes_per_row = 0 picks the mapping from V and dt exactly as ce_forward does.
- * A power of two in [1, 1024] assigns that many lanes to each row (up to 64 lanes:
- * 64 / lanes rows per wavefront; above 64: one row per workgroup of that many
- * threads, combined through LDS).  -1 asks for the one-lane-per-row path for
- * short aligned rows and fails with CE_ERR_LAYOUT where that path does not apply.
- * Results agree with ce_forward up to float32 summation order.  Intended for tests
- * and tuning; any other value returns CE_ERR_SHAPE.
- */
-ce_status ce_forward_lanes(const void* logits, ce_layout in, ce_dtype dt, const int32_t* targets,
-                           int64_t n_rows, int64_t V, float* loss, float* lse,
-                           int32_t lanes_per_row, hipStream_t stream);
-
-/*
  * ce_vjp: dlogits_ij = g_i * (exp((z_ij - m_i) - log s_i) - [j == y_i]).
  *
  * The vector-Jacobian product of ce_forward's per-row loss with upstream gradient g.
@@ -159,17 +145,6 @@ ce_status ce_vjp(const void* logits, ce_layout in, ce_dtype dt, const int32_t* t
                  ce_layout out, hipStream_t stream);
 
 /*
- * ce_vjp_lanes: ce_vjp with lanes_per_row chosen as in ce_forward_lanes.  With
- * lanes_per_row = 0 a row spanning at least 2048 16-byte vectors is cut into chunks
- * of 512 vectors, each handled by its own 256-thread workgroup (ce_vjp does the
- * same); a power of two keeps whole rows on that many lanes.  Every layout computes
- * each element with the same float32 operations, so all give identical bits.
- */
-ce_status ce_vjp_lanes(const void* logits, ce_layout in, ce_dtype dt, const int32_t* targets,
-                       const float* lse, const float* g, int64_t n_rows, int64_t V, void* dlogits,
-                       ce_layout out, int32_t lanes_per_row, hipStream_t stream);
-
-/*
  * ce_forward_vjp: ce_forward and ce_vjp in one kernel, for a caller that knows the
  * upstream gradient g before the forward runs (a loss summed or averaged over the
  * rows, as the next-token loss ".sum()" of MLX issue #4686 (above), Describe the bug).
@@ -177,7 +152,7 @@ ce_status ce_vjp_lanes(const void* logits, ce_layout in, ce_dtype dt, const int3
  * Source: Ineshin (above), section 1: the loss needs only the row's log-sum-exp and
  * target logit, and the backward only that log-sum-exp; "One barrier short", first
  * section: mlx-lm computes its divergences and their gradients in one fused pass so
- * that the log-softmax rows never exist in memory.  Each row's
+ * that the log-softmax rows never exist in memory.
  * Rows of more than 2048 and at most 20480 16-byte vectors (16384 for fp32) whose
  * input and output rows share their 16-byte phase are held in the registers of one
  * workgroup of 512 or 1024 threads: the row max and the sum of exponentials are two passes over
@@ -201,15 +176,6 @@ ce_status ce_vjp_lanes(const void* logits, ce_layout in, ce_dtype dt, const int3
 ce_status ce_forward_vjp(const void* logits, ce_layout in, ce_dtype dt, const int32_t* targets, const float* g,
                          int64_t n_rows, int64_t V, float* loss, float* lse, void* dlogits, ce_layout out,
                          hipStream_t stream);
-
-/*
- * ce_forward_vjp_lanes: ce_forward_vjp with lanes_per_row chosen as in ce_forward_lanes
- * (0: as ce_forward_vjp; a power of two in [1, 1024]; -1: one lane per row, which needs
- * rows of 1, 2, 4 or 8 aligned 16-byte vectors in both views).  For tests and tuning.
- */
-ce_status ce_forward_vjp_lanes(const void* logits, ce_layout in, ce_dtype dt, const int32_t* targets,
-                               const float* g, int64_t n_rows, int64_t V, float* loss, float* lse, void* dlogits,
-                               ce_layout out, int32_t lanes_per_row, hipStream_t stream);
 
 /*
  * lce_workspace_size: bytes of device workspace lce_forward needs for (N, D, V).
@@ -300,11 +266,6 @@ ce_status lce_backward(const void* H, const void* W, const int32_t* targets, con
 ce_status kl_forward(const void* q, ce_layout q_layout, const void* p, ce_layout p_layout, ce_dtype dt,
                      int64_t n_rows, int64_t V, float* kl, float* lse_q, float* lse_p, hipStream_t stream);
 
-/* kl_forward with lanes_per_row as in ce_forward_lanes (-1 is not accepted here). */
-ce_status kl_forward_lanes(const void* q, ce_layout q_layout, const void* p, ce_layout p_layout, ce_dtype dt,
-                           int64_t n_rows, int64_t V, float* kl, float* lse_q, float* lse_p,
-                           int32_t lanes_per_row, hipStream_t stream);
-
 /*
  * kl_vjp: dq_ij = g_i * (exp((q_ij - m_q,i) - log s_q,i) - exp((p_ij - m_p,i) - log s_p,i)),
  * the gradient of sum_i g_i kl_i with respect to the student logits (the page's
@@ -320,11 +281,6 @@ ce_status kl_forward_lanes(const void* q, ce_layout q_layout, const void* p, ce_
 ce_status kl_vjp(const void* q, ce_layout q_layout, const void* p, ce_layout p_layout, ce_dtype dt,
                  const float* lse_q, const float* lse_p, const float* g, int64_t n_rows, int64_t V, void* dq,
                  ce_layout dq_layout, hipStream_t stream);
-
-/* kl_vjp with lanes_per_row as in ce_vjp_lanes (-1 is not accepted here). */
-ce_status kl_vjp_lanes(const void* q, ce_layout q_layout, const void* p, ce_layout p_layout, ce_dtype dt,
-                       const float* lse_q, const float* lse_p, const float* g, int64_t n_rows, int64_t V,
-                       void* dq, ce_layout dq_layout, int32_t lanes_per_row, hipStream_t stream);
 
 /*
  * js_forward: js_i = 1/2 KL(P_i || M_i) + 1/2 KL(Q_i || M_i), M = (P + Q) / 2, with
@@ -350,11 +306,6 @@ ce_status js_forward(const void* q, ce_layout q_layout, const void* p, ce_layout
                      int64_t n_rows, int64_t V, float* js, float* lse_q, float* lse_p, float* hq,
                      hipStream_t stream);
 
-/* js_forward with lanes_per_row as in kl_forward_lanes. */
-ce_status js_forward_lanes(const void* q, ce_layout q_layout, const void* p, ce_layout p_layout, ce_dtype dt,
-                           int64_t n_rows, int64_t V, float* js, float* lse_q, float* lse_p, float* hq,
-                           int32_t lanes_per_row, hipStream_t stream);
-
 /*
  * js_vjp: dq_ik = g_i Q_ik (h_ik - H_i), h_ik = (log Q_ik - log M_ik) / 2, the gradient of
  * sum_i g_i js_i with respect to the student logits, from js_forward's lse_q, lse_p, hq.
@@ -365,11 +316,6 @@ ce_status js_forward_lanes(const void* q, ce_layout q_layout, const void* p, ce_
 ce_status js_vjp(const void* q, ce_layout q_layout, const void* p, ce_layout p_layout, ce_dtype dt,
                  const float* lse_q, const float* lse_p, const float* hq, const float* g, int64_t n_rows, int64_t V,
                  void* dq, ce_layout dq_layout, hipStream_t stream);
-
-/* js_vjp with lanes_per_row as in kl_vjp_lanes. */
-ce_status js_vjp_lanes(const void* q, ce_layout q_layout, const void* p, ce_layout p_layout, ce_dtype dt,
-                       const float* lse_q, const float* lse_p, const float* hq, const float* g, int64_t n_rows,
-                       int64_t V, void* dq, ce_layout dq_layout, int32_t lanes_per_row, hipStream_t stream);
 
 /*
  * ---- Cross-entropy options --------------------------------------------------------

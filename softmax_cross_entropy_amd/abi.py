@@ -29,12 +29,14 @@ CE_REDUCE = {"none": 0, "sum": 1, "mean": 2}
 CE_NO_IGNORE = -(2 ** 31)
 
 # every symbol include/ce_mi355x.h declares
-EXPORTS = ("ce_forward", "ce_forward_lanes", "ce_vjp", "ce_vjp_lanes", "ce_forward_vjp", "ce_forward_vjp_lanes",
-           "lce_workspace_size",
-           "lce_forward", "lce_backward_workspace_size", "lce_backward", "kl_forward", "kl_forward_lanes",
-           "kl_vjp", "kl_vjp_lanes", "js_forward", "js_forward_lanes", "js_vjp", "js_vjp_lanes",
+EXPORTS = ("ce_forward", "ce_vjp", "ce_forward_vjp", "lce_workspace_size",
+           "lce_forward", "lce_backward_workspace_size", "lce_backward", "kl_forward",
+           "kl_vjp", "js_forward", "js_vjp",
            "ce_reduce_workspace_size", "ce_forward_ex", "ce_vjp_ex", "ce_forward_probs",
            "ce_vjp_probs", "ce_status_string")
+# the forced row-to-lane variants include/ce_mi355x_testing.h declares (tests and tuning)
+TESTING_EXPORTS = ("ce_forward_lanes", "ce_vjp_lanes", "ce_forward_vjp_lanes", "kl_forward_lanes", "kl_vjp_lanes",
+                   "js_forward_lanes", "js_vjp_lanes")
 
 
 class CELayout(ctypes.Structure):

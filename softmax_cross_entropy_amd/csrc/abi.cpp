@@ -7,6 +7,7 @@
 #include <cstring>
 
 #include "ce_mi355x.h"
+#include "ce_mi355x_testing.h"
 #include "launch.h"
 
 namespace {
@@ -294,7 +295,9 @@ ce_status fused_impl(const void* logits, ce_layout in, ce_dtype dt, const int32_
     if (ce_status s = make_plan(narrow_ok, V, es, n_rows, lanes, false, cus, &plan)) return s;
     // Rows the forward gives a 512- or 1024-thread workgroup, whose input and output rows share
     // their 16-byte phase, and that fit in those threads' registers: the register-resident
-    // kernel, which folds in the same order.
+    // kernel.  It takes the max and the sum in two passes, so its loss and lse round
+    // differently from ce_forward's online fold; its dlogits match ce_vjp's bit for bit
+    // for the lse it writes.
     if (lanes == 0 && (plan.lanes == 512 || plan.lanes == 1024) && plan.narrow_nv == 0 &&
         same_phase_rows(logits, in, dlogits, out, n_rows, es)) {
         const int64_t need = ((V + vec - 1) / vec + plan.lanes - 1) / plan.lanes;

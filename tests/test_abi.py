@@ -15,24 +15,36 @@ from softmax_cross_entropy_amd import abi
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ce_mi355x.h")
+TESTING_HEADER = os.path.join(ROOT, "include", "ce_mi355x_testing.h")
 
 OK, NULL, SHAPE, DTYPE, LAYOUT, WORKSPACE, LAUNCH, ALIAS, DEVICE, OPTION = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 
 pytestmark = pytest.mark.skipif(not os.path.exists(abi.LIB_PATH), reason="library not built")
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(path=HEADER):
+    text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(\w+)\s*\([^;{]*\)\s*;", text)))
 
 
 def test_exports_every_declared_symbol():
-    names = declared_functions()
+    names = declared_functions(HEADER)
+    testing = declared_functions(TESTING_HEADER)
     assert set(names) == set(abi.EXPORTS)
+    assert set(testing) == set(abi.TESTING_EXPORTS)
+    assert not set(names) & set(testing)
     L = ctypes.CDLL(abi.LIB_PATH)
-    for n in names:
+    for n in names + testing:
         assert hasattr(L, n), n
+
+
+def test_product_header_declares_no_tuning_knob():
+    """The product header's calls pick their own row-to-lane mapping; the calls that take
+    one from the caller live in the testing header only."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    assert "lanes_per_row" not in text
+    assert all(n.endswith("_lanes") for n in declared_functions(TESTING_HEADER))
 
 
 def test_status_strings():
