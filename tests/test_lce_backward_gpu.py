@@ -15,6 +15,7 @@ import torch
 
 from oracle import lce as olce
 from softmax_cross_entropy_amd import abi, inputs
+from tests.conftest import full_lce_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -134,20 +135,40 @@ def test_full_vocab_and_width_one_row_tile():
     within(dW[cols], rW, np.abs(dZc).T @ np.abs(H64), "dW columns")
 
 
-def test_bench_size_sampled_rows_and_column_sum():
-    """N = 8192, D = 4096, V = 151,936 as bench.py runs it: exact dH on sampled rows, and
-    the rows of dW summing to zero (every row of dZ sums to zero; the bf16 rounding
-    of dZ leaves at most 2^-8 sum_v |dZ_iv| <= 2^-7 g_i per row; twice that allowed)."""
-    N, D, V = 8192, 4096, 151936
-    H, W, y = inputs.linear_ce(N, D, V)
+def test_bench_size_sampled_rows_columns_and_column_sum(full_lce):
+    """N = 8192, D = 4096, V = 151,936 as bench.py runs it:
+    * dH on 64 sampled rows against the oracle, entry by entry;
+    * dW on 72 sampled vocabulary rows against the oracle, entry by entry: the first and
+      last columns of every 8192-column chunk boundary they touch, targets, and 24
+      columns of the 4480-column tail chunk;
+    * every row of dW summing to zero (every row of dZ sums to zero; the bf16 rounding
+      of dZ leaves at most 2^-8 sum_v |dZ_iv| <= 2^-7 g_i per row; twice that allowed)."""
+    H, W, y, W64 = full_lce["H"], full_lce["W"], full_lce["y"], full_lce["W64"]
+    N, D = H.shape
+    V = W.shape[0]
     g = upstream(N, 8192)
-    dH, dW = gpu_backward(H, W, y, g)
-    assert np.isfinite(dH).all() and np.isfinite(dW).all()
+    Hd, Wd = dev_bf16(H), dev_bf16(W)
+    yd = torch.from_numpy(np.ascontiguousarray(y, np.int32)).cuda()
+    _, lse = abi.lce_forward(Hd, Wd, yd)
+    dHd, dWd = abi.lce_backward(Hd, Wd, yd, lse, torch.from_numpy(g.astype(np.float32)).cuda())
+    torch.cuda.synchronize()
+    dH = dHd.cpu().numpy().astype(np.float64)
+    assert np.isfinite(dH).all() and torch.isfinite(dWd).all().item()
     rng = np.random.default_rng(1)
-    rows = np.unique(np.concatenate([rng.integers(0, N, 8), [0, N - 1]]))
+    rows = np.unique(np.concatenate([rng.choice(N, 62, replace=False), [0, N - 1]]))
     H64 = olce.decode_bf16(H)
-    rH, _, bH, _ = olce.grad64(H64[rows], olce.decode_bf16(W), y[rows], g[rows], bounds=True)
+    rH, _, bH, _ = olce.grad64(H64[rows], W64, y[rows], g[rows], bounds=True)
     within(dH[rows], rH, bH, "dH rows")
-    colsum = dW.sum(axis=0)
+    tail0 = V - V % 8192
+    cols = np.unique(np.concatenate([[0, 8191, 8192, 16383, 16384, tail0 - 1, tail0, V - 1], y[:16],
+                                     rng.integers(0, tail0, 24), rng.integers(tail0, V, 24)]))
+    assert len(cols) >= 64 and np.sum(cols >= tail0) >= 24
+    _, m, ls = full_lce_oracle(full_lce)
+    rW = olce.grad_columns(H, W, y, g, m, ls, cols)
+    dWc = dWd[torch.from_numpy(cols).cuda()].cpu().numpy().astype(np.float64)
+    Z = H64 @ W64[cols].T
+    dZc = g[:, None] * (np.exp((Z - m[:, None]) - ls[:, None]) - (y[:, None] == cols[None, :]))
+    within(dWc, rW, np.abs(dZc).T @ np.abs(H64), "dW columns")
+    colsum = dWd.sum(dim=0, dtype=torch.float64).cpu().numpy()
     lim = 2.0 ** -6 * (np.abs(g)[:, None] * np.abs(H64)).sum(axis=0) + 1e-3
     assert np.all(np.abs(colsum) <= lim), float((np.abs(colsum) / lim).max())

@@ -13,6 +13,7 @@ import torch
 
 from oracle import lce as olce
 from softmax_cross_entropy_amd import abi, inputs
+from tests.conftest import full_lce_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -29,9 +30,9 @@ def run(H, W, y):
     return loss.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
-def check(H, W, y, rows=None, W64=None):
+def check(H, W, y, rows=None, W64=None, ref=None):
     loss, lse = run(H, W, y)
-    rl, rm, rls = olce.forward(H, W, y, rows=rows, W64=W64)
+    rl, rm, rls = olce.forward(H, W, y, rows=rows, W64=W64) if ref is None else ref
     sel = slice(None) if rows is None else rows
     err = np.abs(loss[sel] - rl)
     assert np.all(err <= TOL), f"max loss error {err.max()} at row {np.argmax(err)}"
@@ -89,16 +90,11 @@ def test_target_is_row_argmax():
     assert np.mean(loss == lse[:, 1]) > 0.9
 
 
-def test_full_vocab_and_width_sampled_rows():
-    """N = 8192, D = 4096, V = 151,936 on the GPU; the oracle on 512 sampled rows,
-    including rows whose target falls in the last 4480 columns (the tail of the
-    8192-column tiling) and rows of the last row tile."""
-    N, D, V = 8192, 4096, 151936
-    H, W, y = inputs.linear_ce(N, D, V)
-    g = np.random.default_rng(0)
-    tail = np.flatnonzero(y >= V - 4480)
-    rows = np.unique(np.concatenate([
-        g.choice(N, 448, replace=False), tail[:32], np.arange(N - 16, N), np.arange(0, 16)]))
-    W64 = olce.decode_bf16(W)
-    _, _, err = check(H, W, y, rows=rows, W64=W64)
-    print(f"full size: {len(rows)} rows checked, max |dloss| = {err:.2e}")
+def test_full_vocab_and_width_every_row(full_lce):
+    """N = 8192, D = 4096, V = 151,936 on the GPU, every row against the oracle (about
+    1e13 float64 multiply-adds on the host), the tail of the 8192-column tiling and the
+    last row tile included."""
+    H, W, y = full_lce["H"], full_lce["W"], full_lce["y"]
+    assert np.any(y >= 151936 - 4480)
+    _, _, err = check(H, W, y, ref=full_lce_oracle(full_lce))
+    print(f"full size: all {len(y)} rows checked, max |dloss| = {err:.2e}")
