@@ -375,6 +375,27 @@ ce_status ce_forward_ex(const void* logits, ce_layout in, ce_dtype dt, const int
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * ce_forward_ex_noalloc: ce_forward_ex for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * The same call as ce_forward_ex without the workspace arguments: a sum or mean keeps
+ * its partials in a fixed array of ce_reduce_workspace_size() = 16 KiB that the library
+ * holds on each GPU it runs on, from its first such call on that GPU until the process
+ * ends.  That size covers the reduction at every n_rows and V (the rows are split into
+ * at most 1024 parts), so no input is too large for it.  The call allocates nothing and
+ * issues no memset; nothing in the array needs to start at zero (every partial is
+ * written before it is read).  Results are those of ce_forward_ex bit for bit.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's partials:
+ * calls that overlap in time on one GPU (on different streams, or from different host
+ * threads without ordering) race on it and must not be made.  With CE_REDUCE_NONE the
+ * array is not used.  Errors as ce_forward_ex; CE_ERR_DEVICE also if the array's
+ * address cannot be had on the current device.
+ */
+ce_status ce_forward_ex_noalloc(const void* logits, ce_layout in, ce_dtype dt, const int32_t* targets,
+                                int64_t n_rows, int64_t V, ce_options opt, float* loss, float* lse, float* total,
+                                int64_t* count, hipStream_t stream);
+
+/*
  * ce_vjp_ex: dlogits_ij = g_i ((1 - eps) (p_ij - [j == y_i]) + eps (p_ij - 1 / V)), the
  * gradient of ce_forward_ex's loss, from the saved lse.
  *

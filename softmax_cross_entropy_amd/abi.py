@@ -32,7 +32,7 @@ CE_NO_IGNORE = -(2 ** 31)
 EXPORTS = ("ce_forward", "ce_vjp", "ce_forward_vjp", "lce_workspace_size",
            "lce_forward", "lce_backward_workspace_size", "lce_backward", "kl_forward",
            "kl_vjp", "js_forward", "js_vjp",
-           "ce_reduce_workspace_size", "ce_forward_ex", "ce_vjp_ex", "ce_forward_probs",
+           "ce_reduce_workspace_size", "ce_forward_ex", "ce_forward_ex_noalloc", "ce_vjp_ex", "ce_forward_probs",
            "ce_vjp_probs", "ce_status_string")
 # the forced row-to-lane variants include/ce_mi355x_testing.h declares (tests and tuning)
 TESTING_EXPORTS = ("ce_forward_lanes", "ce_vjp_lanes", "ce_forward_vjp_lanes", "kl_forward_lanes", "kl_vjp_lanes",
@@ -104,6 +104,8 @@ def lib() -> ctypes.CDLL:
         L.ce_reduce_workspace_size.restype = _sz
         L.ce_forward_ex.argtypes = [_vp, CELayout, ctypes.c_int, _vp, _i64, _i64, CEOptions, _vp, _vp, _vp, _vp, _vp,
                                     _sz, _vp]
+        L.ce_forward_ex_noalloc.argtypes = [_vp, CELayout, ctypes.c_int, _vp, _i64, _i64, CEOptions, _vp, _vp,
+                                            _vp, _vp, _vp]
         L.ce_vjp_ex.argtypes = [_vp, CELayout, ctypes.c_int, _vp, _vp, _vp, _i64, _i64, CEOptions, _vp, _vp, CELayout,
                                 _vp]
         L.ce_forward_probs.argtypes = [_vp, CELayout, ctypes.c_int, _vp, CELayout, _i64, _i64, CEOptions, _vp, _vp,
@@ -115,7 +117,7 @@ def lib() -> ctypes.CDLL:
         for name in ("ce_forward", "ce_forward_lanes", "ce_vjp", "ce_vjp_lanes", "ce_forward_vjp",
                      "ce_forward_vjp_lanes", "lce_forward", "lce_backward",
                      "kl_forward", "kl_forward_lanes", "kl_vjp", "kl_vjp_lanes", "js_forward", "js_forward_lanes",
-                     "js_vjp", "js_vjp_lanes", "ce_forward_ex", "ce_vjp_ex",
+                     "js_vjp", "js_vjp_lanes", "ce_forward_ex", "ce_forward_ex_noalloc", "ce_vjp_ex",
                      "ce_forward_probs", "ce_vjp_probs"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -328,6 +330,24 @@ def ce_forward_ex(logits: torch.Tensor, targets: torch.Tensor, label_smoothing: 
                              options(label_smoothing, ignore_index, reduction), _ptr(loss), _ptr(lse), _ptr(total),
                              _ptr(count), _ptr(workspace), ws_bytes, _stream(logits))
     _check(st, "ce_forward_ex")
+    return loss, lse, total, count
+
+
+def ce_forward_ex_noalloc(logits: torch.Tensor, targets: torch.Tensor, label_smoothing: float, ignore_index,
+                          reduction: str, loss: torch.Tensor, lse: torch.Tensor, total=None, count=None):
+    """ce_forward_ex with the library's fixed per-GPU reduction scratch: the caller passes
+    every output (total and count for a sum or mean) and nothing is allocated."""
+    lay, n, V = _rows_view(logits, "logits")
+    _need(targets, torch.int32, n, "targets")
+    _need(loss, torch.float32, n, "loss")
+    _need(lse, torch.float32, 2 * n, "lse")
+    if reduction != "none":
+        _need(total, torch.float32, 1, "total")
+        _need(count, torch.int64, 1, "count")
+    st = lib().ce_forward_ex_noalloc(_ptr(logits), lay, DTYPE_CODE[logits.dtype], _ptr(targets), n, V,
+                                     options(label_smoothing, ignore_index, reduction), _ptr(loss), _ptr(lse),
+                                     _ptr(total), _ptr(count), _stream(logits))
+    _check(st, "ce_forward_ex_noalloc")
     return loss, lse, total, count
 
 

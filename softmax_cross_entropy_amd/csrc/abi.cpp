@@ -681,6 +681,23 @@ ce_status ce_forward_ex(const void* logits, ce_layout in, ce_dtype dt, const int
                            count, workspace, workspace_bytes, stream);
 }
 
+ce_status ce_forward_ex_noalloc(const void* logits, ce_layout in, ce_dtype dt, const int32_t* targets,
+                                int64_t n_rows, int64_t V, ce_options opt, float* loss, float* lse, float* total,
+                                int64_t* count, hipStream_t stream) {
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    if (opt.reduction != CE_REDUCE_NONE) {
+        if (hipError_t e = ce::reduce_scratch(&ws, &ws_bytes)) {
+            (void)e;
+            return CE_ERR_DEVICE;
+        }
+        // the scratch holds the reduction's need at every size; this cannot fail
+        if (ws_bytes < ce::kReduceWorkspaceBytes) return CE_ERR_WORKSPACE;
+    }
+    return options_forward(logits, in, dt, targets, false, nullptr, in, n_rows, V, opt, loss, lse, nullptr, total,
+                           count, ws, ws_bytes, stream);
+}
+
 ce_status ce_vjp_ex(const void* logits, ce_layout in, ce_dtype dt, const int32_t* targets, const float* lse,
                     const float* g, int64_t n_rows, int64_t V, ce_options opt, const int64_t* count, void* dlogits,
                     ce_layout out, hipStream_t stream) {

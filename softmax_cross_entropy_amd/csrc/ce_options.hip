@@ -24,6 +24,8 @@
 // The VJP is elementwise and cuts long rows into chunks of 256 * kChunkU vectors.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -669,6 +671,36 @@ hipError_t ovjp_dt(const OptVjpCall& c) {
 hipError_t launch_opt_forward(const OptFwdCall& c) { return c.t ? ofwd_dt<true>(c) : ofwd_dt<false>(c); }
 
 hipError_t launch_opt_vjp(const OptVjpCall& c) { return c.t ? ovjp_dt<true>(c) : ovjp_dt<false>(c); }
+
+// Reduction partials of ce_forward_ex_noalloc, for callers that cannot allocate device
+// memory: one fixed array per GPU, held for the life of the process.  Its size is the
+// reduction's whole need at any n_rows (at most kReduceMaxParts partial sums and
+// counts).  In host code `scratch` names a host-side stand-in, not device memory: host
+// code uses only the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[kReduceWorkspaceBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+hipError_t reduce_scratch(void** ptr, size_t* bytes) {
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev)) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        // the device is current: this is its own copy of the array
+        void* p = nullptr;
+        if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    *bytes = sizeof(scratch);
+    return hipSuccess;
+}
 
 int64_t reduce_parts(int64_t n_rows) {
     if (n_rows <= 0) return 0;

@@ -199,6 +199,9 @@ int64_t reduce_parts(int64_t n_rows);
 hipError_t launch_opt_forward(const OptFwdCall& c);
 hipError_t launch_opt_vjp(const OptVjpCall& c);
 hipError_t launch_loss_reduce(const ReduceCall& c);
+// This device's fixed reduction scratch (kReduceWorkspaceBytes, 256-byte aligned): its
+// device address, taken once per device with that device current.
+hipError_t reduce_scratch(void** ptr, size_t* bytes);
 
 hipError_t launch_kl_forward(const KLFwdCall& c);
 hipError_t launch_kl_vjp(const KLVjpCall& c);
