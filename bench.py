@@ -707,8 +707,8 @@ def main():
         rooflines["lce_backward"] = {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS,
                                      "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
                                      "ms": bwd_ms, "algorithmic_flop": fl,
-                                     "kernels": "per 8192-column chunk: lce_tile (dZ epilogue) + two rocBLAS "
-                                                "GEMMs (one lce_backward call)"}
+                                     "kernels": "per 8192-column chunk: lce_tile (dZ epilogue), the W chunk "
+                                                "transposed, two lce_tile products (one lce_backward call)"}
         cfg["lce_backward"] = {"N": LCE_N, "D": LCE_D, "V": LCE_V, "out": "fp32 dH, dW", "timed": "apart"}
     for key, tms, (fb, vb), names, cfgv in (
             ("kl_fwd_vjp", kl_ms, kl_bytes(KL_ROWS, KL_V, 4), ("kl_forward", "kl_vjp"),

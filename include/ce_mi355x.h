@@ -10,7 +10,7 @@
  *                 tiles without materialising the N x V logits
  *   lce_backward  dH and dW of sum_i g_i loss_i for lce_forward's loss; the logits
  *                 are regenerated chunk by chunk, and the two products with the
- *                 regenerated gradient chunk run on rocBLAS
+ *                 regenerated gradient chunk run on the same MFMA tile kernel
  *   kl_forward    per-row KL divergence of a teacher logits row from a student row
  *   kl_vjp        dq = g_i * (softmax(q_i) - softmax(p_i)) from the saved pairs
  *   js_forward    per-row Jensen-Shannon divergence of a student row and a teacher row
@@ -22,10 +22,10 @@
  * Conventions shared by every call
  * --------------------------------
  * - Pointers to tensors are DEVICE pointers owned by the caller.  The library keeps
- *   no pointer after a call returns and allocates no device memory: the lce calls'
- *   only scratch is the caller's workspace.  (lce_backward's first call on a host
- *   thread creates a rocBLAS handle for the current device and keeps it for the life
- *   of that thread; rocBLAS works in the caller's workspace.)
+ *   no pointer after a call returns and allocates no device memory: the only scratch
+ *   is the caller's workspace (lce_forward, lce_backward, and a sum or mean of the
+ *   _ex and _probs forwards), or, for ce_forward_ex_noalloc, a fixed 16 KiB array the
+ *   library holds on each GPU.
  * - Work is enqueued on `stream` (NULL = the default stream) and the call returns
  *   without synchronising.  Outputs are valid once the stream has been synchronised.
  * - Every argument is checked on the host before any launch.  A failed check returns
@@ -224,20 +224,24 @@ size_t lce_backward_workspace_size(int64_t N, int64_t D, int64_t V);
  * chunk of 8192 vocabulary columns (the page's tile width), the forward's MFMA tile
  * kernel recomputes the chunk of Z and its epilogue writes
  * dZ = g_i (exp((z - m_i) - log s_i) - [col == y_i]) in bf16 (round to nearest even)
- * into the workspace, row-major and transposed; rocBLAS then adds dZ_c W_c into dH and
- * writes dZ_c^T H into the chunk's rows of dW, both with float32 accumulation.
+ * into the workspace, row-major and transposed.  The same MFMA K loop then adds
+ * dZ_c W_c into dH and writes dZ_c^T H into the chunk's rows of dW, both with float32
+ * accumulation; it reads W_c and H through transposed bf16 copies in the workspace (H
+ * once per call, W_c once per chunk).  The call is made of kernels only (no library
+ * calls, no memsets), so it can be captured in a HIP graph.
  *
  *   H, W, targets  as in lce_forward.
  *   lse      float32 [N][2], the (m, log s) pairs lce_forward wrote for the same H, W.
  *   g        float32 [N], the upstream gradient of each row's loss.
- *   dH       float32 [N][D], row-major (written).
- *   dW       float32 [V][D], row-major (written).
+ *   dH       float32 [N][D], row-major, 16-byte aligned (written).
+ *   dW       float32 [V][D], row-major, 16-byte aligned (written).
  *   workspace, workspace_bytes: device scratch of at least
  *            lce_backward_workspace_size(N, D, V) bytes, 256-byte aligned.
  * A row whose target lies outside [0, V) has a NaN loss, so its dZ row is NaN: its
  * dH row and every entry of dW come out NaN.  dH and dW must not overlap the inputs,
  * the workspace or each other (CE_ERR_ALIAS).  Requirements on N, D, V as in
- * lce_forward, and N < 2^31.  A rocBLAS failure returns CE_ERR_LAUNCH.
+ * lce_forward, and N <= 2^22 (the product over the tokens addresses rows of 2 N bytes
+ * with 32-bit offsets).
  */
 ce_status lce_backward(const void* H, const void* W, const int32_t* targets, const float* lse,
                        const float* g, int64_t N, int64_t D, int64_t V, float* dH, float* dW,

@@ -16,8 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libce_mi355x.so")
 SOURCES = ["abi.cpp", "ce_kernels.hip", "ce_options.hip", "lce_kernels.hip", "lce_backward.cpp", "kl_kernels.hip", "js_kernels.hip"]
-# lce_backward runs its two plain GEMMs per vocabulary chunk on rocBLAS.
-LIBS = ["-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
+LIBS = []
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

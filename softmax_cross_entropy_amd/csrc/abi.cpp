@@ -18,6 +18,8 @@ using ce::Plan;
 
 constexpr int kMaxDevices = 64;
 constexpr int64_t kMaxV = 0x7fffffff;  // targets are int32
+// lce_backward's product over the tokens reads rows of 2 N bytes through 32-bit offsets
+constexpr int64_t kMaxBackwardN = (int64_t)1 << 22;
 
 // Per-device CU count, 0 = not looked up yet, -1 = not a gfx950 device.  Racing
 // first calls store the same value, so plain relaxed atomics suffice.
@@ -582,22 +584,22 @@ ce_status lce_forward(const void* H, const void* W, const int32_t* targets, int6
 }
 
 size_t lce_backward_workspace_size(int64_t N, int64_t D, int64_t V) {
-    if (N < 0 || N > 0x7fffffff || D < 1 || D % 8 != 0 || V < 1 || V > kMaxV || D > (int64_t)1 << 22) return 0;
+    if (N < 0 || N > kMaxBackwardN || D < 1 || D % 8 != 0 || V < 1 || V > kMaxV || D > (int64_t)1 << 22) return 0;
     return ce::lce_backward_workspace_bytes(N, D, V);
 }
 
 ce_status lce_backward(const void* H, const void* W, const int32_t* targets, const float* lse, const float* g,
                        int64_t N, int64_t D, int64_t V, float* dH, float* dW, void* workspace,
                        size_t workspace_bytes, hipStream_t stream) {
-    if (N < 0 || N > 0x7fffffff || D < 1 || D % 8 != 0 || V < 1 || V > kMaxV || D > (int64_t)1 << 22)
+    if (N < 0 || N > kMaxBackwardN || D < 1 || D % 8 != 0 || V < 1 || V > kMaxV || D > (int64_t)1 << 22)
         return CE_ERR_SHAPE;
     if (!W || !dW) return CE_ERR_NULL;
     if (N > 0 && (!H || !targets || !lse || !g || !dH)) return CE_ERR_NULL;
     const size_t need = ce::lce_backward_workspace_bytes(N, D, V);
     if (N > 0 && (!workspace || workspace_bytes < need)) return CE_ERR_WORKSPACE;
-    if (!aligned(W, 16) || !aligned(dW, 4)) return CE_ERR_LAYOUT;
+    if (!aligned(W, 16) || !aligned(dW, 16)) return CE_ERR_LAYOUT;
     if (N > 0 && (!aligned(H, 16) || !aligned(targets, 4) || !aligned(lse, 8) || !aligned(g, 4) ||
-                  !aligned(dH, 4) || !aligned(workspace, 256)))
+                  !aligned(dH, 16) || !aligned(workspace, 256)))
         return CE_ERR_LAYOUT;
     const Extent ex_dW = flat_extent(dW, V * D * 4);
     const Extent ex_W = flat_extent(W, V * D * 2);

@@ -245,6 +245,33 @@ struct LceGradChunk {
 
 hipError_t launch_lce_grad_chunk(const LceGradChunk& c);
 
+// C[r][c] (+)= sum_k A[r][k] B[c][k] for r < M, c < Ncols: bf16 A [M][lda] and B [Ncols][ldb],
+// both K-contiguous, K a multiple of 8 (lda, ldb too), fp32 C [M][ldc] with ldc a
+// multiple of 4 and C 16-byte aligned.
+struct LceGemm {
+    const void* A;
+    int64_t lda;
+    const void* B;
+    int64_t ldb;
+    int64_t M;
+    int64_t Ncols;
+    int64_t K;
+    float* C;
+    int64_t ldc;
+    bool accumulate;
+    hipStream_t stream;
+};
+
+hipError_t launch_lce_gemm(const LceGemm& c);
+
+// bf16 dst[c][r] = src[r][c] for r < R, c < C, and 0 for R <= r < Rpad; C, lds, ldd and
+// Rpad are multiples of 8, both pointers 16-byte aligned.
+hipError_t launch_transpose_bf16(const void* src, int64_t R, int64_t C, int64_t lds, void* dst, int64_t ldd,
+                                 int64_t Rpad, hipStream_t stream);
+// bf16 p[r][c] = 0 for r < rows, c_from <= c < c_to.
+hipError_t launch_zero_cols_bf16(void* p, int64_t rows, int64_t ld, int64_t c_from, int64_t c_to,
+                                 hipStream_t stream);
+
 // Writes n zeros (a kernel, not a memset, so a captured graph replays it safely).
 hipError_t launch_fill_zero_f32(float* p, int64_t n, hipStream_t stream);
 
@@ -263,7 +290,7 @@ struct LceBackwardCall {
     hipStream_t stream;
 };
 
-enum class LceBackwardStatus { kOk, kHip, kBlas };
+enum class LceBackwardStatus { kOk, kHip };
 
 size_t lce_backward_workspace_bytes(int64_t N, int64_t D, int64_t V);
 LceBackwardStatus run_lce_backward(const LceBackwardCall& c);

@@ -6,99 +6,79 @@
 // logits it needs tile by tile.  Here each chunk of 8192 vocabulary columns (the
 // page's dispatch tile) is one launch of the MFMA tile kernel whose epilogue turns the
 // regenerated logits straight into dZ (bf16, from the saved (m, log s) pair), written
-// both row-major and transposed, followed by two plain GEMMs on rocBLAS, accumulated
-// in fp32:
+// both row-major and transposed, followed by two products on the same MFMA K loop,
+// accumulated in fp32:
 //   dH        += dZ_c  W_c       (N x D, every chunk adds its share)
 //   dW[c0:c1]  = dZ_c^T H        (the chunk's own rows of dW)
-// With both layouts neither GEMM reads a transposed operand (rocBLAS's kernel for
-// dZ_c^T H from the row-major chunk ran about 25% slower than the one without).
-// Everything runs on the caller's stream; the two dZ chunks and rocBLAS's scratch live
-// in the caller's workspace.
+// The K loop reads both operands K-contiguous, so W_c and H enter these products
+// transposed: H^T once per call, W_c^T once per chunk (lce_transpose).  K is padded to
+// a multiple of 8 with zeros in both operands.  Everything runs on the caller's stream
+// in the caller's workspace; nothing is allocated and no state is kept between calls.
 #include <hip/hip_runtime.h>
-#include <rocblas/rocblas.h>
 
 #include "launch.h"
 
 namespace ce {
 namespace {
 
-constexpr int64_t kChunk = 8192;            // vocabulary columns per chunk
-constexpr size_t kBlasBytes = 64ull << 20;  // rocBLAS scratch inside the workspace
-constexpr int kMaxDevices = 64;
+constexpr int64_t kChunk = 8192;  // vocabulary columns per chunk
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+int64_t round8(int64_t x) { return (x + 7) & ~(int64_t)7; }
 
-// One rocBLAS handle per thread and device, created on first use and kept for the life
-// of the thread (rocBLAS handles must not be used by two threads at once).  The handle
-// is told to use the caller's workspace, so rocBLAS allocates no scratch of its own.
-struct Handles {
-    rocblas_handle h[kMaxDevices] = {};
-    void* ws[kMaxDevices] = {};
+struct Layout {
+    size_t g, gt, ht, wt, total;  // byte offsets of the four bf16 buffers
 };
 
-rocblas_status handle_for(int dev, void* ws, rocblas_handle* out) {
-    thread_local Handles hs;
-    if (!hs.h[dev]) {
-        rocblas_status s = rocblas_create_handle(&hs.h[dev]);
-        if (s != rocblas_status_success) {
-            hs.h[dev] = nullptr;
-            return s;
-        }
-        hs.ws[dev] = nullptr;
-    }
-    if (hs.ws[dev] != ws) {
-        rocblas_status s = rocblas_set_workspace(hs.h[dev], ws, kBlasBytes);
-        if (s != rocblas_status_success) return s;
-        hs.ws[dev] = ws;
-    }
-    *out = hs.h[dev];
-    return rocblas_status_success;
+// dZ chunk [N][kChunk]; its transpose [kChunk][N8]; H^T [D][N8]; W_c^T [D][kChunk].
+Layout layout(int64_t N, int64_t D) {
+    const int64_t n8 = round8(N);
+    Layout l;
+    l.g = 0;
+    l.gt = l.g + align256((size_t)N * kChunk * 2);
+    l.ht = l.gt + align256((size_t)kChunk * n8 * 2);
+    l.wt = l.ht + align256((size_t)D * n8 * 2);
+    l.total = l.wt + align256((size_t)D * kChunk * 2);
+    return l;
 }
 
 }  // namespace
 
 size_t lce_backward_workspace_bytes(int64_t N, int64_t D, int64_t V) {
-    (void)D;
     (void)V;
-    return 2 * align256((size_t)N * kChunk * 2) + kBlasBytes;
+    return layout(N, D).total;
 }
 
 LceBackwardStatus run_lce_backward(const LceBackwardCall& c) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LceBackwardStatus::kHip;
+    const Layout l = layout(c.N, c.D);
     char* ws = static_cast<char*>(c.workspace);
-    const size_t chunk_bytes = align256((size_t)c.N * kChunk * 2);
-    void* G = ws;
-    void* GT = ws + chunk_bytes;
-    void* blas_ws = ws + 2 * chunk_bytes;
-    rocblas_handle h = nullptr;
-    if (handle_for(dev, blas_ws, &h) != rocblas_status_success) return LceBackwardStatus::kBlas;
-    if (rocblas_set_stream(h, c.stream) != rocblas_status_success) return LceBackwardStatus::kBlas;
-
-    const char* Hb = static_cast<const char*>(c.H);
+    void* G = ws + l.g;
+    void* GT = ws + l.gt;
+    void* HT = ws + l.ht;
+    void* WT = ws + l.wt;
+    const int64_t n8 = round8(c.N);
+    auto ok = [](hipError_t e) { return e == hipSuccess; };
+    // H^T with zero columns N .. N8 - 1, and the same zero columns in the transposed dZ
+    // chunk (the tile kernel writes only columns below N): the K padding of dW's product
+    if (!ok(launch_transpose_bf16(c.H, c.N, c.D, c.D, HT, n8, n8, c.stream))) return LceBackwardStatus::kHip;
+    if (!ok(launch_zero_cols_bf16(GT, kChunk, n8, c.N, n8, c.stream))) return LceBackwardStatus::kHip;
     const char* Wb = static_cast<const char*>(c.W);
-    const float one = 1.0f, zero = 0.0f;
-    const rocblas_int n = (rocblas_int)c.N, d = (rocblas_int)c.D, ldg = (rocblas_int)kChunk;
     for (int64_t c0 = 0; c0 < c.V; c0 += kChunk) {
         const int64_t w = c.V - c0 < kChunk ? c.V - c0 : kChunk;
-        LceGradChunk gc{c.H, c.W, c.targets, c.lse, c.g, c.N, c.D, c.V, c0, w, G, kChunk, GT, c.N, c.stream};
-        if (launch_lce_grad_chunk(gc) != hipSuccess) return LceBackwardStatus::kHip;
-        // rocBLAS is column-major: a row-major [r][cols] array with leading dimension L
-        // is a column-major cols x r matrix with the same L.
-        // dH^T (D x N) += W_c^T (D x w) * dZ_c^T (w x N)
-        if (rocblas_gemm_ex(h, rocblas_operation_none, rocblas_operation_none, d, n, (rocblas_int)w, &one,
-                            Wb + c0 * c.D * 2, rocblas_datatype_bf16_r, d, G, rocblas_datatype_bf16_r, ldg,
-                            c0 == 0 ? &zero : &one, c.dH, rocblas_datatype_f32_r, d, c.dH,
-                            rocblas_datatype_f32_r, d, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0,
-                            0) != rocblas_status_success)
-            return LceBackwardStatus::kBlas;
-        // dW_c^T (D x w) = H^T (D x N) * dZ_c (N x w), dZ_c being the transposed chunk read
-        // as a column-major N x w matrix
-        if (rocblas_gemm_ex(h, rocblas_operation_none, rocblas_operation_none, d, (rocblas_int)w, n, &one,
-                            Hb, rocblas_datatype_bf16_r, d, GT, rocblas_datatype_bf16_r, n, &zero,
-                            c.dW + c0 * c.D, rocblas_datatype_f32_r, d, c.dW + c0 * c.D, rocblas_datatype_f32_r,
-                            d, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0) != rocblas_status_success)
-            return LceBackwardStatus::kBlas;
+        const int64_t w8 = round8(w);
+        LceGradChunk gc{c.H, c.W, c.targets, c.lse, c.g, c.N, c.D, c.V, c0, w, G, kChunk, GT, n8, c.stream};
+        if (!ok(launch_lce_grad_chunk(gc))) return LceBackwardStatus::kHip;
+        // W_c^T [D][w8], zero past w; and dZ_c's columns w .. w8 - 1 (stale from an earlier
+        // chunk) zeroed, so the padded K adds nothing
+        if (!ok(launch_transpose_bf16(Wb + c0 * c.D * 2, w, c.D, c.D, WT, kChunk, w8, c.stream)))
+            return LceBackwardStatus::kHip;
+        if (w8 > w && !ok(launch_zero_cols_bf16(G, c.N, kChunk, w, w8, c.stream))) return LceBackwardStatus::kHip;
+        // dH [N][D] (+)= dZ_c [N][w8] . (W_c^T [D][w8])^T
+        LceGemm p1{G, kChunk, WT, kChunk, c.N, c.D, w8, c.dH, c.D, c0 > 0, c.stream};
+        if (!ok(launch_lce_gemm(p1))) return LceBackwardStatus::kHip;
+        // dW[c0 : c0 + w] [w][D] = dZ_c^T [w][N8] . (H^T [D][N8])^T
+        LceGemm p2{GT, n8, HT, n8, w, c.D, n8, c.dW + c0 * c.D, c.D, false, c.stream};
+        if (!ok(launch_lce_gemm(p2))) return LceBackwardStatus::kHip;
     }
     return LceBackwardStatus::kOk;
 }

@@ -1,21 +1,26 @@
 // Fused linear cross-entropy forward for gfx950: loss and log-sum-exp of Z = H W^T
-// without materialising Z.
+// without materialising Z, and the kernels of its backward.
 //
 // Ineshin, "A fused linear cross-entropy forward kernel for Apple GPUs", section 1:
 // each vocabulary tile of Z is folded into a running per-row state (m, s),
 // m' = max(m, m_t), s' = s exp(m - m') + sum_j exp(z_j - m'), and the target logit
 // is captured by the tile that holds the target column.
 //
-// Two kernels:
-//   lce_tile   one 256 x 256 tile of Z per workgroup (bf16 MFMA 32x32x16, fp32 accumulate,
-//              K = D streamed through LDS in 64-wide double-buffered stages).  Its
-//              epilogue turns the fp32 accumulators straight into one (m, s) pair per
-//              row for each 128-column slab (exact slab maximum, then one exponential
-//              per logit), and stores the target logit from the same accumulator when
-//              the target column is in the slab.
-//   lce_merge  folds the slabs of each row in slab order into (m, s), then
-//              loss = (m - z_y) + log s and lse = (m, log s).
-// Workspace: partial (m, s) float2 [N][n_slabs], then z_y float [N].
+// Kernels:
+//   lce_tile<kTileFwd>   one 256 x 256 tile of Z per workgroup (bf16 MFMA 32x32x16, fp32
+//                    accumulate, K streamed through LDS in 64-wide double-buffered
+//                    stages).  Its epilogue turns the fp32 accumulators straight into one
+//                    (m, s) pair per row for each 128-column slab (exact slab maximum,
+//                    then one exponential per logit), and stores the target logit from
+//                    the same accumulator when the target column is in the slab.
+//   lce_merge        folds the slabs of each row in slab order into (m, s), then
+//                    loss = (m - z_y) + log s and lse = (m, log s).
+//   lce_tile<kTileGrad>  the same tile of Z turned into the bf16 gradient of the logits (the
+//                    backward's regenerated logits), row-major and transposed.
+//   lce_tile<kTileGemm>  the same K loop as a plain product C (+)= A B^T of two K-contiguous
+//                    bf16 operands into fp32: the backward's dH = dZ W and dW = dZ^T H,
+//                    with W and H transposed beforehand by lce_transpose.
+// Forward workspace: partial (m, s) float2 [N][n_slabs], then z_y float [N].
 //
 // The page's kernel merges fixed 8192-column tiles in a chain of dependent
 // dispatches.  Here every tile of the grid is independent (the merge is associative,
@@ -52,14 +57,20 @@ constexpr int kStagingBytes = 4 * kWaveStaging;
 constexpr int kTilesPerGroup = 32;   // tiles per super-block (one per CU of an XCD)
 constexpr int kXcds = 8;
 
+enum TileMode { kTileFwd = 0, kTileGrad = 1, kTileGemm = 2 };
+
+// The tile computes Z[r][c] = sum_k A[r][k] B[c][k] over K for A rows r < N and B rows
+// c in [c0, c_end), both operands bf16 and K-contiguous (an NT product).  In the lce
+// calls A = H and B = W (K = D); a plain product passes its own operands.
 struct TileArgs {
-    const __bf16* H;
-    const __bf16* W;
+    const __bf16* H;    // A: row r at H + r * lda
+    const __bf16* W;    // B: row c at W + c * ldb
     const int32_t* targets;
-    int64_t N;
-    int64_t D;
+    int64_t N;          // rows of A
+    int64_t K;          // reduction length (a multiple of 8)
+    int64_t lda, ldb;   // row strides of A and B, elements (multiples of 8)
     int64_t V;
-    int64_t c0, c_end;  // vocabulary columns [c0, c_end) this launch covers
+    int64_t c0, c_end;  // B rows (vocabulary columns) [c0, c_end) this launch covers
     int n_row_tiles, n_col_tiles;
     int gr, gc;      // super-block shape in tiles (gr * gc == 32)
     int n_rg, n_sb;  // row groups, super-blocks
@@ -74,6 +85,10 @@ struct TileArgs {
     int64_t ldG;
     __bf16* GT;         // the same chunk transposed: [width][ldGT], column c as row c - c0
     int64_t ldGT;
+    // plain product: C[r][c - c0] (+)= Z[r][c], fp32, row r at C + r * ldc
+    float* C;
+    int64_t ldc;
+    int32_t accumulate;
 };
 
 // LDS layout of one operand stage: 256 rows x 8 chunks of 16 bytes (8 bf16 along K).
@@ -81,14 +96,17 @@ struct TileArgs {
 // read touches at one K chunk land in 16 different 16-byte bank groups:
 //   byte offset of (row, chunk) = row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4).
 
-// kGrad = false: the forward epilogue ((m, s) per row per 128-column slab, target logit).
-// kGrad = true: the same tile of Z turned into dZ = g (exp((z - m) - log s) - [col = y])
+// kTileFwd: the forward epilogue ((m, s) per row per 128-column slab, target logit).
+// kTileGrad: the same tile of Z turned into dZ = g (exp((z - m) - log s) - [col = y])
 // with the saved (m, log s), stored in bf16 (the logits regenerated for the backward),
 // both row-major and transposed: each of the two products of the backward then reads
-// its operand without a transpose.  The transposed copy is staged through LDS and
-// leaves in 16-byte stores of 8 rows of a column.
-template <bool kGrad>
+// it K-contiguous.  The transposed copy is staged through LDS and leaves in 16-byte
+// stores of 8 rows of a column.
+// kTileGemm: the tile stored (or added) into an fp32 matrix.
+template <int kMode>
 __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
+    constexpr bool kGrad = kMode == kTileGrad;
+    constexpr bool kGemm = kMode == kTileGemm;
     // One LDS object (the compiler then sees the DMA writes and the fragment reads as
     // one array and inserts no waits of its own): two stages of A and B (or, in the
     // gradient epilogue, the dZ staging blocks), then targets.
@@ -139,18 +157,19 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
     // valid row, so every load stays inside its descriptor's range.
     const int64_t a_rows = a.N - row0 < BM ? a.N - row0 : BM;  // valid rows in this tile
     const int64_t b_rows = a.c_end - col0 < BN ? a.c_end - col0 : BN;
-    const uint32_t row_bytes = (uint32_t)(a.D * 2);
-    const char* a_tile = reinterpret_cast<const char*>(a.H + row0 * a.D);
-    const char* b_tile = reinterpret_cast<const char*>(a.W + col0 * a.D);
+    const uint32_t a_row_bytes = (uint32_t)(a.lda * 2);
+    const uint32_t b_row_bytes = (uint32_t)(a.ldb * 2);
+    const char* a_tile = reinterpret_cast<const char*>(a.H + row0 * a.lda);
+    const char* b_tile = reinterpret_cast<const char*>(a.W + col0 * a.ldb);
     // The DMA goes through buffer_load_dwordx4 ... lds rather than global_load_lds: the
     // compiler counts LDS reads precisely only while no FLAT-encoded instruction is in
     // flight, and with the global form pending it waited for all LDS reads
     // (s_waitcnt lgkmcnt(0)) before every group of MFMAs, including the reads issued
     // for later K16 steps.  Word 3 of the descriptor: raw 32-bit data, no swizzle.
     const __amdgpu_buffer_rsrc_t rsrc_a =
-        __builtin_amdgcn_make_buffer_rsrc((void*)a_tile, (short)0, (int)((uint32_t)a_rows * row_bytes), 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)a_tile, (short)0, (int)((uint32_t)a_rows * a_row_bytes), 0x00020000);
     const __amdgpu_buffer_rsrc_t rsrc_b =
-        __builtin_amdgcn_make_buffer_rsrc((void*)b_tile, (short)0, (int)((uint32_t)b_rows * row_bytes), 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)b_tile, (short)0, (int)((uint32_t)b_rows * b_row_bytes), 0x00020000);
 
     // The LDS destination of group q is the group-0 slot plus q * 1 KiB; the instruction's
     // immediate offset moves the LDS and the global address together, so every group
@@ -165,9 +184,9 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
         const int r = lrow + q * 8;
         const int64_t nrows = is_b ? b_rows : a_rows;
         const int rr = r < nrows ? r : (int)nrows - 1;
-        // K tail: past D, re-read this row's last chunk; zeroed in LDS once it lands
-        const uint32_t kb = (uint32_t)(k0 + koff[q & 1] < a.D ? koff[q & 1] : a.D - 8 - k0) * 2;
-        const uint32_t voff = (uint32_t)(k0 * 2) + ((uint32_t)rr * row_bytes + kb);
+        // K tail: past K, re-read this row's last chunk; zeroed in LDS once it lands
+        const uint32_t kb = (uint32_t)(k0 + koff[q & 1] < a.K ? koff[q & 1] : a.K - 8 - k0) * 2;
+        const uint32_t voff = (uint32_t)(k0 * 2) + ((uint32_t)rr * (is_b ? b_row_bytes : a_row_bytes) + kb);
         char* dst = &lds[buf][is_b ? 1 : 0][(wave * 64 + q * 8) * 128];
         __builtin_amdgcn_raw_ptr_buffer_load_lds(is_b ? rsrc_b : rsrc_a, (lds_void_t*)dst, 16, voff, 0, 0, 0);
     };
@@ -200,10 +219,10 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
     // publishes the stage.
     auto zero_tail = [&](int kt, int buf) {
         const int64_t k0 = (int64_t)kt * BK;
-        if (k0 + BK <= a.D) return;
+        if (k0 + BK <= a.K) return;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            if (k0 + koff[q & 1] >= a.D) {
+            if (k0 + koff[q & 1] >= a.K) {
                 const int o = (wave * 64 + q * 8) * 128 + lane * 16;
                 *reinterpret_cast<U4*>(&lds[buf][0][o]) = U4{{0u, 0u, 0u, 0u}};
                 *reinterpret_cast<U4*>(&lds[buf][1][o]) = U4{{0u, 0u, 0u, 0u}};
@@ -249,9 +268,7 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
             for (int j = 0; j < FB; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
     };
-    // One K16 step is 16 MFMAs and 8 LDS reads: one read after every 2 MFMAs.  The step
-    // that also issues the next stage's 16 DMA loads spreads them the same way, so the
-    // matrix pipe is never left idle while they are issued.
+    // One K16 step is 16 MFMAs and 8 LDS reads: one read after every 2 MFMAs.
     auto interleave = [&]() {
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
@@ -259,25 +276,29 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
         }
     };
-    // The K16 step after a stage's barrier: its 16 MFMAs (on fa, fb), the 8 LDS reads of
-    // the next stage's first fragments (into na, nb from buffer cur ^ 1) and the 16 DMA
-    // loads of stage kt_load (into buffer cur), in 8 chunks of 2 MFMAs + 1 read + 2 loads.
-    // The scheduler keeps the chunk order, so the DMA issue never idles the matrix pipe.
-    auto step_with_dma = [&](int kt_load, int cur, const bf16x8 (&fa)[FB], const bf16x8 (&fb)[FB],
-                             bf16x8 (&na)[FB], bf16x8 (&nb)[FB]) {
-        const char* As = &lds[cur ^ 1][0][wm * WT * 128];
-        const char* Bs = &lds[cur ^ 1][1][wn * WT * 128];
+    // A K16 step after a stage's barrier: its 16 MFMAs (on fa, fb) in 8 chunks of 2, each
+    // chunk followed by one LDS read of a later step's fragments (into na, nb from buffer
+    // rbuf, K16 step rkk) and one DMA load, group q0 + chunk, of stage kt_load into buffer
+    // lbuf.  The scheduler keeps the chunk order, so the DMA issue never idles the
+    // matrix pipe.  The stage's 16 DMA loads are split over the two steps after the
+    // barrier: issued in one step, they filled the vector-memory address queues (the
+    // counters showed them full a tenth of the kernel's time) and stalled the MFMAs
+    // queued behind them.
+    auto step_dma = [&](auto q0c, const bf16x8 (&fa)[FB], const bf16x8 (&fb)[FB], int rbuf, int rkk,
+                        bf16x8 (&na)[FB], bf16x8 (&nb)[FB], int kt_load, int lbuf) {
+        constexpr int q0 = decltype(q0c)::value;
+        const char* As = &lds[rbuf][0][wm * WT * 128];
+        const char* Bs = &lds[rbuf][1][wn * WT * 128];
         auto chunk = [&](auto cc) {
             constexpr int c = decltype(cc)::value;
             constexpr int i = c / 2, j0 = 2 * (c % 2);
             acc[i][j0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j0], fa[i], acc[i][j0], 0, 0, 0);
             acc[i][j0 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j0 + 1], fa[i], acc[i][j0 + 1], 0, 0, 0);
             if constexpr (c < 4)
-                na[c] = *reinterpret_cast<const bf16x8*>(As + c * 32 * 128 + off[0]);
+                na[c] = *reinterpret_cast<const bf16x8*>(As + c * 32 * 128 + off[rkk]);
             else
-                nb[c - 4] = *reinterpret_cast<const bf16x8*>(Bs + (c - 4) * 32 * 128 + off[0]);
-            dma_group(std::integral_constant<int, 2 * c>{}, kt_load, cur);
-            dma_group(std::integral_constant<int, 2 * c + 1>{}, kt_load, cur);
+                nb[c - 4] = *reinterpret_cast<const bf16x8*>(Bs + (c - 4) * 32 * 128 + off[rkk]);
+            dma_group(std::integral_constant<int, q0 + c>{}, kt_load, lbuf);
             __builtin_amdgcn_sched_barrier(0);
         };
         [&]<int... C>(std::integer_sequence<int, C...>) {
@@ -297,12 +318,12 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
     // is bound by LDS read latency).  A stage's single barrier sits between its steps 1
     // and 2: by then every wave has read all four steps of the stage (steps 2 and 3 during
     // steps 0 and 1), so the DMA of stage kt + 2 can go into its buffer, and stage kt + 1
-    // has landed, so steps 2 and 3 can read the next stage's first two steps.  The DMA
-    // still has four K16 steps to land.
-    const int nk = (int)((a.D + BK - 1) / BK);
+    // has landed, so steps 2 and 3 can read the next stage's first two steps.  The DMA,
+    // issued during steps 2 and 3, has two to three K16 steps to land.
+    const int nk = (int)((a.K + BK - 1) / BK);
     bf16x8 fa0[FB], fb0[FB], fa1[FB], fb1[FB], fa2[FB], fb2[FB], fa3[FB], fb3[FB];
     // targets of this tile's rows, for the epilogue
-    tile_targets[tid] = row0 + tid < a.N ? a.targets[row0 + tid] : -1;
+    if constexpr (!kGemm) tile_targets[tid] = row0 + tid < a.N ? a.targets[row0 + tid] : -1;
     issue(0, 0);
     wait_stage();
     zero_tail(0, 0);
@@ -321,10 +342,9 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
         sync_stage(kt, cur, nk);
         // the last stage re-issues stage nk - 1 into the free buffer, which is never read:
         // no branch around the DMA, so it can interleave with the MFMAs
-        step_with_dma(kt + 2 < nk ? kt + 2 : nk - 1, cur, fa2, fb2, fa0, fb0);
-        read_frags(cur ^ 1, 1, fa1, fb1);
-        mfma_all(fa3, fb3);
-        interleave();
+        const int kt_load = kt + 2 < nk ? kt + 2 : nk - 1;
+        step_dma(std::integral_constant<int, 0>{}, fa2, fb2, cur ^ 1, 0, fa0, fb0, kt_load, cur);
+        step_dma(std::integral_constant<int, 8>{}, fa3, fb3, cur ^ 1, 1, fa1, fb1, kt_load, cur);
     }
     {
         const int cur = (nk - 1) & 1;
@@ -347,7 +367,38 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
     const int64_t wrow0 = row0 + wm * WT;
     auto col_of = [&](int j, int e) { return j * 32 + 8 * (e / 4) + 4 * h2 + (e % 4); };
 
-    if constexpr (kGrad) {
+    if constexpr (kGemm) {
+        // acc[i][j][4q .. 4q + 3] are 4 consecutive columns of one row: 16-byte stores
+        // (or load, add, store), one row per lane, in a fixed order.
+#pragma unroll
+        for (int i = 0; i < FB; ++i) {
+            const int64_t row = wrow0 + i * 32 + l32;
+            if (row >= a.N) continue;
+            float* crow = a.C + row * a.ldc - a.c0;
+#pragma unroll
+            for (int j = 0; j < FB; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t c = wcol0 + j * 32 + 8 * q + 4 * h2;
+                    float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                    if (c + 3 < a.c_end) {
+                        float4* p = reinterpret_cast<float4*>(crow + c);
+                        if (a.accumulate) {
+                            const float4 o = *p;
+                            v[0] += o.x;
+                            v[1] += o.y;
+                            v[2] += o.z;
+                            v[3] += o.w;
+                        }
+                        *p = make_float4(v[0], v[1], v[2], v[3]);
+                    } else {
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            if (c + t < a.c_end) crow[c + t] = a.accumulate ? crow[c + t] + v[t] : v[t];
+                    }
+                }
+        }
+    } else if constexpr (kGrad) {
         // dZ for this lane's 4 rows x 64 columns.  A row with an out-of-range target
         // gets m = NaN, so its whole row of dZ is NaN (its loss is NaN too).  The
         // row-major copy is stored directly, 4 columns per store; the transposed copy goes
@@ -585,10 +636,25 @@ hipError_t launch_lce_forward(const LceCall& c) {
     char* ws = static_cast<char*>(c.workspace);
     float2* partial = reinterpret_cast<float2*>(ws);
     float* zy = reinterpret_cast<float*>(ws + align256((size_t)g.n_slabs * (size_t)c.N * sizeof(float2)));
-    TileArgs a{static_cast<const __bf16*>(c.H), static_cast<const __bf16*>(c.W), c.targets, c.N, c.D, c.V,
-               0, c.V, g.n_row_tiles, g.n_col_tiles, g.gr, g.gc, g.n_rg, g.n_sb, g.n_slabs, partial, zy,
-               nullptr, nullptr, nullptr, 0};
-    hipLaunchKernelGGL(lce_tile<false>, dim3((unsigned)g.blocks), dim3(kThreads), 0, c.stream, a);
+    TileArgs a{};
+    a.H = static_cast<const __bf16*>(c.H);
+    a.W = static_cast<const __bf16*>(c.W);
+    a.targets = c.targets;
+    a.N = c.N;
+    a.K = a.lda = a.ldb = c.D;
+    a.V = c.V;
+    a.c0 = 0;
+    a.c_end = c.V;
+    a.n_row_tiles = g.n_row_tiles;
+    a.n_col_tiles = g.n_col_tiles;
+    a.gr = g.gr;
+    a.gc = g.gc;
+    a.n_rg = g.n_rg;
+    a.n_sb = g.n_sb;
+    a.n_slabs = g.n_slabs;
+    a.partial = partial;
+    a.zy = zy;
+    hipLaunchKernelGGL(lce_tile<kTileFwd>, dim3((unsigned)g.blocks), dim3(kThreads), 0, c.stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     constexpr int kRowsPerBlock = kMergeThreads / kMergeLanes;
@@ -600,11 +666,52 @@ hipError_t launch_lce_forward(const LceCall& c) {
 
 hipError_t launch_lce_grad_chunk(const LceGradChunk& c) {
     const Geometry g = geometry(c.N, c.width);
-    TileArgs a{static_cast<const __bf16*>(c.H), static_cast<const __bf16*>(c.W), c.targets, c.N, c.D, c.V,
-               c.c0, c.c0 + c.width, g.n_row_tiles, g.n_col_tiles, g.gr, g.gc, g.n_rg, g.n_sb, 0, nullptr,
-               nullptr, reinterpret_cast<const float2*>(c.lse), c.g, static_cast<__bf16*>(c.G), c.ldG,
-               static_cast<__bf16*>(c.GT), c.ldGT};
-    hipLaunchKernelGGL(lce_tile<true>, dim3((unsigned)g.blocks), dim3(kThreads), 0, c.stream, a);
+    TileArgs a{};
+    a.H = static_cast<const __bf16*>(c.H);
+    a.W = static_cast<const __bf16*>(c.W);
+    a.targets = c.targets;
+    a.N = c.N;
+    a.K = a.lda = a.ldb = c.D;
+    a.V = c.V;
+    a.c0 = c.c0;
+    a.c_end = c.c0 + c.width;
+    a.n_row_tiles = g.n_row_tiles;
+    a.n_col_tiles = g.n_col_tiles;
+    a.gr = g.gr;
+    a.gc = g.gc;
+    a.n_rg = g.n_rg;
+    a.n_sb = g.n_sb;
+    a.lse = reinterpret_cast<const float2*>(c.lse);
+    a.g = c.g;
+    a.G = static_cast<__bf16*>(c.G);
+    a.ldG = c.ldG;
+    a.GT = static_cast<__bf16*>(c.GT);
+    a.ldGT = c.ldGT;
+    hipLaunchKernelGGL(lce_tile<kTileGrad>, dim3((unsigned)g.blocks), dim3(kThreads), 0, c.stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_lce_gemm(const LceGemm& c) {
+    const Geometry g = geometry(c.M, c.Ncols);
+    TileArgs a{};
+    a.H = static_cast<const __bf16*>(c.A);
+    a.W = static_cast<const __bf16*>(c.B);
+    a.N = c.M;
+    a.K = c.K;
+    a.lda = c.lda;
+    a.ldb = c.ldb;
+    a.c0 = 0;
+    a.c_end = c.Ncols;
+    a.n_row_tiles = g.n_row_tiles;
+    a.n_col_tiles = g.n_col_tiles;
+    a.gr = g.gr;
+    a.gc = g.gc;
+    a.n_rg = g.n_rg;
+    a.n_sb = g.n_sb;
+    a.C = c.C;
+    a.ldc = c.ldc;
+    a.accumulate = c.accumulate ? 1 : 0;
+    hipLaunchKernelGGL(lce_tile<kTileGemm>, dim3((unsigned)g.blocks), dim3(kThreads), 0, c.stream, a);
     return hipGetLastError();
 }
 
@@ -612,13 +719,83 @@ namespace {
 __global__ __launch_bounds__(256) void fill_zero_f32(float* p, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
 }
+
+// dst[c][r] = src[r][c] for r < R, c < C, and 0 for R <= r < Rpad: one 64 x 64 block of
+// src per step of a 256-thread workgroup, staged through LDS (row pitch 72 elements, so
+// the 16-byte row pieces stay aligned).  C, lds and ldd are multiples of 8 and Rpad is
+// one too, so every 8-element piece is either wholly inside or wholly outside.
+constexpr int kTp = 64;
+constexpr int kTpPitch = kTp + 8;
+__global__ __launch_bounds__(256) void lce_transpose(const uint16_t* __restrict__ src, int64_t R, int64_t C,
+                                                     int64_t lds, uint16_t* __restrict__ dst, int64_t ldd,
+                                                     int64_t Rpad) {
+    __shared__ __attribute__((aligned(16))) uint16_t tile[kTp * kTpPitch];
+    const int64_t tr = (Rpad + kTp - 1) / kTp, tc = (C + kTp - 1) / kTp;
+    const int t = threadIdx.x;
+    for (int64_t b = blockIdx.x; b < tr * tc; b += gridDim.x) {
+        const int64_t r0 = (b / tc) * kTp, c0 = (b % tc) * kTp;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int id = t + 256 * k;
+            const int rr = id >> 3, cc = (id & 7) * 8;
+            const int64_t r = r0 + rr, c = c0 + cc;
+            U4 v = U4{{0u, 0u, 0u, 0u}};
+            if (r < R && c < C) v = *reinterpret_cast<const U4*>(src + r * lds + c);
+            *reinterpret_cast<U4*>(&tile[rr * kTpPitch + cc]) = v;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int id = t + 256 * k;
+            const int cc = id >> 3, rr = (id & 7) * 8;
+            const int64_t c = c0 + cc, r = r0 + rr;
+            if (c < C && r < Rpad) {
+                U4 v;
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    v.w[u] = (uint32_t)tile[(rr + 2 * u) * kTpPitch + cc] |
+                             ((uint32_t)tile[(rr + 2 * u + 1) * kTpPitch + cc] << 16);
+                *reinterpret_cast<U4*>(dst + c * ldd + r) = v;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// p[r][c] = 0 for r < rows, c_from <= c < c_to (row r at p + r * ld).
+__global__ __launch_bounds__(256) void zero_cols_bf16(uint16_t* p, int64_t rows, int64_t ld, int64_t c_from,
+                                                      int64_t c_to) {
+    const int64_t w = c_to - c_from;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < rows * w; i += (int64_t)gridDim.x * 256)
+        p[(i / w) * ld + c_from + i % w] = 0;
+}
+
+unsigned grid_for(int64_t items, int64_t per_block, int64_t cap) {
+    const int64_t want = (items + per_block - 1) / per_block;
+    return (unsigned)(want < 1 ? 1 : (want < cap ? want : cap));
+}
 }  // namespace
 
 hipError_t launch_fill_zero_f32(float* p, int64_t n, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
-    const int64_t want = (n + 255) / 256;
-    const unsigned blocks = (unsigned)(want < 16384 ? want : 16384);
-    hipLaunchKernelGGL(fill_zero_f32, dim3(blocks), dim3(256), 0, stream, p, n);
+    hipLaunchKernelGGL(fill_zero_f32, dim3(grid_for(n, 256, 16384)), dim3(256), 0, stream, p, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose_bf16(const void* src, int64_t R, int64_t C, int64_t lds, void* dst, int64_t ldd,
+                                 int64_t Rpad, hipStream_t stream) {
+    if (C <= 0 || Rpad <= 0) return hipSuccess;
+    const int64_t tiles = ((Rpad + kTp - 1) / kTp) * ((C + kTp - 1) / kTp);
+    hipLaunchKernelGGL(lce_transpose, dim3(grid_for(tiles, 1, 65536)), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(src), R, C, lds, static_cast<uint16_t*>(dst), ldd, Rpad);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_cols_bf16(void* p, int64_t rows, int64_t ld, int64_t c_from, int64_t c_to,
+                                 hipStream_t stream) {
+    if (rows <= 0 || c_to <= c_from) return hipSuccess;
+    hipLaunchKernelGGL(zero_cols_bf16, dim3(grid_for(rows * (c_to - c_from), 256, 4096)), dim3(256), 0, stream,
+                       static_cast<uint16_t*>(p), rows, ld, c_from, c_to);
     return hipGetLastError();
 }
 

@@ -178,7 +178,7 @@ def test_lce_rejects_bad_arguments():
     assert lce(ws=ctypes.c_void_p(7 * A + 256)) == ALIAS  # workspace inside W
 
 
-P_DH, P_DW = ctypes.c_void_p(A * 200), ctypes.c_void_p(A * 210)  # clear of the 65 MiB workspace
+P_DH, P_DW = ctypes.c_void_p(A * 200), ctypes.c_void_p(A * 210)  # clear of the workspace
 
 
 def lbw(H=P_LOGITS, W=P_W, t=P_T, lse=P_LSE, g=P_G, N=32, D=64, V=1000, dH=P_DH, dW=P_DW, ws=P_WS, wsb=None):
@@ -189,24 +189,33 @@ def lbw(H=P_LOGITS, W=P_W, t=P_T, lse=P_LSE, g=P_G, N=32, D=64, V=1000, dH=P_DH,
 
 def test_lce_backward_rejects_bad_arguments():
     need = abi.lce_backward_workspace_size(32, 64, 1000)
-    assert need == 2 * 32 * 8192 * 2 + (64 << 20)  # dZ chunk, row-major and transposed; GEMM scratch
+    # dZ chunk [32][8192] and its transpose [8192][32]; H^T [64][32]; W chunk^T [64][8192]
+    assert need == 2 * 32 * 8192 * 2 + 64 * 32 * 2 + 64 * 8192 * 2
+    # N = 33: the transposed buffers' rows are padded to 40 tokens, each buffer to 256 bytes
+    a256 = lambda x: (x + 255) // 256 * 256
+    assert abi.lce_backward_workspace_size(33, 64, 1000) == (a256(33 * 8192 * 2) + a256(8192 * 40 * 2) +
+                                                             a256(64 * 40 * 2) + a256(64 * 8192 * 2))
     assert abi.lce_backward_workspace_size(32, 60, 1000) == 0
-    assert abi.lce_backward_workspace_size(1 << 31, 64, 1000) == 0
+    assert abi.lce_backward_workspace_size((1 << 22) + 1, 64, 1000) == 0
+    assert abi.lce_backward_workspace_size(1 << 22, 64, 1000) > 0
     assert lbw(D=60) == SHAPE
     assert lbw(D=0) == SHAPE
     assert lbw(V=0) == SHAPE
     assert lbw(N=-1) == SHAPE
     assert lbw(N=1 << 31, wsb=1 << 40) == SHAPE
+    assert lbw(N=(1 << 22) + 1, wsb=1 << 40) == SHAPE
     assert lbw(D=(1 << 22) + 8) == SHAPE
     for name in ("H", "W", "t", "lse", "g", "dH", "dW"):
         assert lbw(**{name: None}) == NULL, name
     assert lbw(ws=None) == WORKSPACE
     assert lbw(wsb=need - 1) == WORKSPACE
     assert lbw(H=ctypes.c_void_p(A + 8)) == LAYOUT
+    assert lbw(dH=ctypes.c_void_p(200 * A + 4)) == LAYOUT   # dH and dW take 16-byte stores
+    assert lbw(dW=ctypes.c_void_p(210 * A + 8)) == LAYOUT
     assert lbw(lse=ctypes.c_void_p(4 * A + 4)) == LAYOUT
     assert lbw(ws=ctypes.c_void_p(8 * A + 64)) == LAYOUT
     assert lbw(dW=ctypes.c_void_p(7 * A + 1024)) == ALIAS   # dW inside W
-    assert lbw(dH=ctypes.c_void_p(20 * A)) == ALIAS         # dH inside the workspace
+    assert lbw(dH=ctypes.c_void_p(8 * A + 4096)) == ALIAS   # dH inside the workspace
     assert lbw(dH=ctypes.c_void_p(210 * A + 4096)) == ALIAS  # dH inside dW
     assert lbw(dW=ctypes.c_void_p(5 * A)) == ALIAS          # dW over g
 

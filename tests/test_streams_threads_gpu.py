@@ -1,8 +1,8 @@
 """GPU: the calls run on the caller's stream, and concurrent host threads get the same bits.
 
 Every entry point enqueues its work on the stream it is given (torch's current stream in
-the binding) and keeps no global mutable state but a per-device CU count; lce_backward
-keeps one rocBLAS handle per host thread and device.  ctypes releases the GIL during a
+the binding) and keeps no global mutable state but a per-device CU count (and the
+address of the allocation-free call's per-GPU array).  ctypes releases the GIL during a
 call, so two Python threads enter the library concurrently here.  Results are
 deterministic, so everything is compared bit for bit with the default-stream results.
 """
