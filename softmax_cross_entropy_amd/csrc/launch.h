@@ -263,6 +263,8 @@ struct LceGemm {
 };
 
 hipError_t launch_lce_gemm(const LceGemm& c);
+// Two independent products in one launch (both on p.stream).
+hipError_t launch_lce_gemm2(const LceGemm& p, const LceGemm& q);
 
 // bf16 dst[c][r] = src[r][c] for r < R, c < C, and 0 for R <= r < Rpad; C, lds, ldd and
 // Rpad are multiples of 8, both pointers 16-byte aligned.

@@ -21,36 +21,44 @@
 namespace ce {
 namespace {
 
-constexpr int64_t kChunk = 8192;  // vocabulary columns per chunk
+#ifndef LCE_BWD_MAX_CHUNK
+#define LCE_BWD_MAX_CHUNK 8192
+#endif
+constexpr int64_t kMaxChunk = LCE_BWD_MAX_CHUNK;  // vocabulary columns per chunk, at most
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 int64_t round8(int64_t x) { return (x + 7) & ~(int64_t)7; }
 
+int64_t chunk_cols(int64_t V) {
+    const int64_t v256 = (V + 255) & ~(int64_t)255;
+    return v256 < kMaxChunk ? v256 : kMaxChunk;
+}
+
 struct Layout {
+    int64_t chunk;
     size_t g, gt, ht, wt, total;  // byte offsets of the four bf16 buffers
 };
 
-// dZ chunk [N][kChunk]; its transpose [kChunk][N8]; H^T [D][N8]; W_c^T [D][kChunk].
-Layout layout(int64_t N, int64_t D) {
+// dZ chunk [N][chunk]; its transpose [chunk][N8]; H^T [D][N8]; W_c^T [D][chunk].
+Layout layout(int64_t N, int64_t D, int64_t V) {
     const int64_t n8 = round8(N);
     Layout l;
+    l.chunk = chunk_cols(V);
     l.g = 0;
-    l.gt = l.g + align256((size_t)N * kChunk * 2);
-    l.ht = l.gt + align256((size_t)kChunk * n8 * 2);
+    l.gt = l.g + align256((size_t)N * l.chunk * 2);
+    l.ht = l.gt + align256((size_t)l.chunk * n8 * 2);
     l.wt = l.ht + align256((size_t)D * n8 * 2);
-    l.total = l.wt + align256((size_t)D * kChunk * 2);
+    l.total = l.wt + align256((size_t)D * l.chunk * 2);
     return l;
 }
 
 }  // namespace
 
-size_t lce_backward_workspace_bytes(int64_t N, int64_t D, int64_t V) {
-    (void)V;
-    return layout(N, D).total;
-}
+size_t lce_backward_workspace_bytes(int64_t N, int64_t D, int64_t V) { return layout(N, D, V).total; }
 
 LceBackwardStatus run_lce_backward(const LceBackwardCall& c) {
-    const Layout l = layout(c.N, c.D);
+    const Layout l = layout(c.N, c.D, c.V);
+    const int64_t kChunk = l.chunk;
     char* ws = static_cast<char*>(c.workspace);
     void* G = ws + l.g;
     void* GT = ws + l.gt;
@@ -73,12 +81,11 @@ LceBackwardStatus run_lce_backward(const LceBackwardCall& c) {
         if (!ok(launch_transpose_bf16(Wb + c0 * c.D * 2, w, c.D, c.D, WT, kChunk, w8, c.stream)))
             return LceBackwardStatus::kHip;
         if (w8 > w && !ok(launch_zero_cols_bf16(G, c.N, kChunk, w, w8, c.stream))) return LceBackwardStatus::kHip;
-        // dH [N][D] (+)= dZ_c [N][w8] . (W_c^T [D][w8])^T
+        // dH [N][D] (+)= dZ_c [N][w8] . (W_c^T [D][w8])^T, and
+        // dW[c0 : c0 + w] [w][D] = dZ_c^T [w][N8] . (H^T [D][N8])^T, in one launch
         LceGemm p1{G, kChunk, WT, kChunk, c.N, c.D, w8, c.dH, c.D, c0 > 0, c.stream};
-        if (!ok(launch_lce_gemm(p1))) return LceBackwardStatus::kHip;
-        // dW[c0 : c0 + w] [w][D] = dZ_c^T [w][N8] . (H^T [D][N8])^T
         LceGemm p2{GT, n8, HT, n8, w, c.D, n8, c.dW + c0 * c.D, c.D, false, c.stream};
-        if (!ok(launch_lce_gemm(p2))) return LceBackwardStatus::kHip;
+        if (!ok(launch_lce_gemm2(p1, p2))) return LceBackwardStatus::kHip;
     }
     return LceBackwardStatus::kOk;
 }

@@ -104,9 +104,15 @@ struct TileArgs {
 // stores of 8 rows of a column.
 // kTileGemm: the tile stored (or added) into an fp32 matrix.
 template <int kMode>
-__global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a0, TileArgs a1, int split) {
     constexpr bool kGrad = kMode == kTileGrad;
     constexpr bool kGemm = kMode == kTileGemm;
+    // A plain-product launch may carry two independent products: workgroups below
+    // `split` compute the first, the rest the second (split is a multiple of 8, so both
+    // keep the XCD-aware tile order).  One grid of both products' tiles leaves fewer
+    // idle compute units at the end than two launches of two tiles per unit each.
+    const bool second = kGemm && (int)blockIdx.x >= split;
+    const TileArgs a = second ? a1 : a0;
     // One LDS object (the compiler then sees the DMA writes and the fragment reads as
     // one array and inserts no waits of its own): two stages of A and B (or, in the
     // gradient epilogue, the dZ staging blocks), then targets.
@@ -121,7 +127,7 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a) {
     // workgroups an XCD runs together share gr row tiles of H and gc column tiles of W
     // through its L2, and the 8 XCDs work on neighbouring super-blocks of the same W
     // columns at the same time.
-    const int b = blockIdx.x;
+    const int b = (int)blockIdx.x - (second ? split : 0);
     const int xcd = b % kXcds;
     const int local = b / kXcds;
     const int sb = (local / kTilesPerGroup) * kXcds + xcd;
@@ -654,7 +660,7 @@ hipError_t launch_lce_forward(const LceCall& c) {
     a.n_slabs = g.n_slabs;
     a.partial = partial;
     a.zy = zy;
-    hipLaunchKernelGGL(lce_tile<kTileFwd>, dim3((unsigned)g.blocks), dim3(kThreads), 0, c.stream, a);
+    hipLaunchKernelGGL(lce_tile<kTileFwd>, dim3((unsigned)g.blocks), dim3(kThreads), 0, c.stream, a, a, (int)g.blocks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     constexpr int kRowsPerBlock = kMergeThreads / kMergeLanes;
@@ -687,12 +693,12 @@ hipError_t launch_lce_grad_chunk(const LceGradChunk& c) {
     a.ldG = c.ldG;
     a.GT = static_cast<__bf16*>(c.GT);
     a.ldGT = c.ldGT;
-    hipLaunchKernelGGL(lce_tile<kTileGrad>, dim3((unsigned)g.blocks), dim3(kThreads), 0, c.stream, a);
+    hipLaunchKernelGGL(lce_tile<kTileGrad>, dim3((unsigned)g.blocks), dim3(kThreads), 0, c.stream, a, a, (int)g.blocks);
     return hipGetLastError();
 }
 
-hipError_t launch_lce_gemm(const LceGemm& c) {
-    const Geometry g = geometry(c.M, c.Ncols);
+namespace {
+TileArgs gemm_args(const LceGemm& c, const Geometry& g) {
     TileArgs a{};
     a.H = static_cast<const __bf16*>(c.A);
     a.W = static_cast<const __bf16*>(c.B);
@@ -711,7 +717,22 @@ hipError_t launch_lce_gemm(const LceGemm& c) {
     a.C = c.C;
     a.ldc = c.ldc;
     a.accumulate = c.accumulate ? 1 : 0;
-    hipLaunchKernelGGL(lce_tile<kTileGemm>, dim3((unsigned)g.blocks), dim3(kThreads), 0, c.stream, a);
+    return a;
+}
+}  // namespace
+
+hipError_t launch_lce_gemm(const LceGemm& c) {
+    const Geometry g = geometry(c.M, c.Ncols);
+    const TileArgs a = gemm_args(c, g);
+    hipLaunchKernelGGL(lce_tile<kTileGemm>, dim3((unsigned)g.blocks), dim3(kThreads), 0, c.stream, a, a,
+                       (int)g.blocks);
+    return hipGetLastError();
+}
+
+hipError_t launch_lce_gemm2(const LceGemm& p, const LceGemm& q) {
+    const Geometry gp = geometry(p.M, p.Ncols), gq = geometry(q.M, q.Ncols);
+    hipLaunchKernelGGL(lce_tile<kTileGemm>, dim3((unsigned)(gp.blocks + gq.blocks)), dim3(kThreads), 0, p.stream,
+                       gemm_args(p, gp), gemm_args(q, gq), (int)gp.blocks);
     return hipGetLastError();
 }
 

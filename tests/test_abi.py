@@ -189,12 +189,13 @@ def lbw(H=P_LOGITS, W=P_W, t=P_T, lse=P_LSE, g=P_G, N=32, D=64, V=1000, dH=P_DH,
 
 def test_lce_backward_rejects_bad_arguments():
     need = abi.lce_backward_workspace_size(32, 64, 1000)
-    # dZ chunk [32][8192] and its transpose [8192][32]; H^T [64][32]; W chunk^T [64][8192]
-    assert need == 2 * 32 * 8192 * 2 + 64 * 32 * 2 + 64 * 8192 * 2
+    # a chunk of V rounded up to 256 columns (1024) when V is below the chunk width:
+    # dZ chunk [32][1024] and its transpose [1024][32]; H^T [64][32]; W chunk^T [64][1024]
+    assert need == 2 * 32 * 1024 * 2 + 64 * 32 * 2 + 64 * 1024 * 2
     # N = 33: the transposed buffers' rows are padded to 40 tokens, each buffer to 256 bytes
     a256 = lambda x: (x + 255) // 256 * 256
-    assert abi.lce_backward_workspace_size(33, 64, 1000) == (a256(33 * 8192 * 2) + a256(8192 * 40 * 2) +
-                                                             a256(64 * 40 * 2) + a256(64 * 8192 * 2))
+    assert abi.lce_backward_workspace_size(33, 64, 1000) == (a256(33 * 1024 * 2) + a256(1024 * 40 * 2) +
+                                                             a256(64 * 40 * 2) + a256(64 * 1024 * 2))
     assert abi.lce_backward_workspace_size(32, 60, 1000) == 0
     assert abi.lce_backward_workspace_size((1 << 22) + 1, 64, 1000) == 0
     assert abi.lce_backward_workspace_size(1 << 22, 64, 1000) > 0
