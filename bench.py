@@ -114,6 +114,41 @@ def source_sha(kernel):
     return h.hexdigest()[:16]
 
 
+def environment(torch):
+    """Where the numbers were taken: GPU, ROCm/HIP and torch versions, the source tree."""
+    env = {"gpu": None, "arch": None, "hip": getattr(torch.version, "hip", None), "torch": torch.__version__,
+           "rocm": None, "git_sha": None, "source_sha256": None}
+    try:
+        prop = torch.cuda.get_device_properties(0)
+        env["gpu"] = prop.name
+        env["arch"] = getattr(prop, "gcnArchName", None)
+        env["cus"] = prop.multi_processor_count
+    except Exception:
+        pass
+    try:
+        with open("/opt/rocm/.info/version") as fh:
+            env["rocm"] = fh.read().strip()
+    except OSError:
+        pass
+    try:
+        import subprocess
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True, timeout=10)
+        if r.returncode == 0:
+            env["git_sha"] = r.stdout.strip()
+    except Exception:
+        pass
+    # the tree may travel without its git metadata: a digest of the sources that were built
+    h = hashlib.sha256()
+    for d in (CSRC, os.path.join(ROOT, "include")):
+        for f in sorted(os.listdir(d)):
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    with open(os.path.abspath(__file__), "rb") as fh:
+        h.update(fh.read())
+    env["source_sha256"] = h.hexdigest()[:16]
+    return env
+
+
 def traffic_for(kernel):
     t = TRAFFIC.get(kernel)
     if not t or t.get("source_sha") != source_sha(kernel):
@@ -288,12 +323,16 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--parts", default="ce,fused,lce,lbw,kl,js,opt,probs,shapes",
+    ap.add_argument("--parts", default="ce,fused,lce,lbw,kl,js,opt,probs,shapes,ceil",
                     help="comma list of ce, fused (ce_forward_vjp on the ce workload; needs ce), lce, lbw "
                          "(lce_backward), kl (kl_forward + kl_vjp), js (js_forward + "
                          "js_vjp), opt (ce_forward_ex + ce_vjp_ex), probs (ce_forward_probs + ce_vjp_probs), "
-                         "shapes (ce_forward + ce_vjp at the small-vocabulary, strided and huge-row shapes)")
+                         "shapes (ce_forward + ce_vjp at the small-vocabulary, strided and huge-row shapes), "
+                         "ceil (a same-GPU copy and read rate beside the HBM specification)")
     ap.add_argument("--bwd-steps", type=int, default=5, help="timed lce_backward calls")
+    ap.add_argument("--shape", default=None,
+                    help="with shapes: only the shapes whose label contains this text (one shape per "
+                         "profiler run keeps its counters apart from the other shapes)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run one elementwise copy (torch.neg) of MIB MiB fp32 first, so a counter "
                          "profile holds a kernel of known traffic")
@@ -571,6 +610,8 @@ def main():
             ("f32 [135266304 x 8]", plain(inputs.huge_rows)),
         )
         for label, build in shape_list:
+            if args.shape and args.shape not in label:
+                continue
             note(f"shapes: {label}")
             store, dt, view_of, tgt = build()
             ncopy = max(1, -(-(1 << 30) // store.nbytes))
@@ -609,6 +650,31 @@ def main():
         bwd_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in bev]))
         del dH, dW, bws
 
+    # A same-GPU streaming ceiling beside the 8 TB/s specification: torch's copy of 2 GiB
+    # of fp32 (2 GiB read + 2 GiB written) and its sum over them (2 GiB read), best of 5.
+    ceiling = None
+    if "ceil" in parts:
+        note("ceil")
+        src = torch.ones(1 << 29, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        acc = torch.empty((), dtype=torch.float32, device=dev)
+        t_copy, t_read = [], []
+        for i in range(6):
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            e0.record(stream)
+            dst.copy_(src)
+            e1.record(stream)
+            torch.sum(src, dim=0, out=acc)
+            e2.record(stream)
+            torch.cuda.synchronize()
+            if i:
+                t_copy.append(e0.elapsed_time(e1))
+                t_read.append(e1.elapsed_time(e2))
+        nb = src.numel() * 4
+        ceiling = {"copy_GB_s": 2 * nb / (min(t_copy) * 1e-3) / 1e9, "read_GB_s": nb / (min(t_read) * 1e-3) / 1e9,
+                   "bytes_read": nb, "method": "torch copy_ and sum over 2 GiB fp32, best of 5"}
+        del src, dst
+
     step_ms = float(np.mean(ms(0, 3)))
     out = {"metric": METRIC, "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": step_ms,
            "wall_ms_per_step": wall / K * 1e3, "higher_is_better": True, "scaling": "weak",
@@ -622,8 +688,10 @@ def main():
 
     def spread(ts):
         # per-step times of the K timed steps (ms): the value above is their mean
-        ts = sorted(ts)
-        return {"median_ms": float(ts[len(ts) // 2]), "min_ms": float(ts[0]), "max_ms": float(ts[-1])}
+        raw = [float(t) for t in ts]
+        ts = sorted(raw)
+        return {"median_ms": float(ts[len(ts) // 2]), "min_ms": float(ts[0]), "max_ms": float(ts[-1]),
+                "raw_ms": raw}
 
     def b2b_out(fb, vb, f, v):
         return {"fwd_ms": f, "vjp_ms": v, "ms": f + v, "GB_s": rate(fb + vb, f + v),
@@ -762,7 +830,14 @@ def main():
     out["roofline"] = dict(rooflines[dom], kernel=dom)
     out.setdefault("value", None)
     out.setdefault("unit", None)
+    if ceiling:
+        for r in rooflines.values():
+            if r["bound"] == "hbm":
+                r["frac_copy_ceiling"] = r["achieved"] / ceiling["copy_GB_s"]
+                r["frac_read_ceiling"] = r["achieved"] / ceiling["read_GB_s"]
     out["rooflines"] = rooflines
+    out["hbm_ceiling"] = ceiling
+    out["env"] = environment(torch)
     if calib:
         out["calibration"] = calib
     if not args.no_cpu and ce_batch is not None and lce_in is not None:
