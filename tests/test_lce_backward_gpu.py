@@ -172,3 +172,16 @@ def test_bench_size_sampled_rows_columns_and_column_sum(full_lce):
     colsum = dWd.sum(dim=0, dtype=torch.float64).cpu().numpy()
     lim = 2.0 ** -6 * (np.abs(g)[:, None] * np.abs(H64)).sum(axis=0) + 1e-3
     assert np.all(np.abs(colsum) <= lim), float((np.abs(colsum) / lim).max())
+
+
+def test_deepest_reduction():
+    """D = 2^22, the largest depth the call accepts: the regenerated logits take 65,536 K
+    stages, H^T and the W chunk's transpose have 2^22 rows, and dH and dW 2^22 columns."""
+    N, D, V = 3, 1 << 22, 5
+    H, W, y = inputs.linear_ce(N, D, V, seed_stream=23)
+    g = upstream(N, 3)
+    dH, dW = gpu_backward(H, W, y, g)
+    rH, rW, bH, bW = olce.grad(H, W, y, g, bounds=True)
+    eH = within(dH, rH, bH, "dH")
+    eW = within(dW, rW, bW, "dW")
+    print(f"D = 2^22: max |error| / bound: dH {eH:.2e}, dW {eW:.2e}")

@@ -98,3 +98,12 @@ def test_full_vocab_and_width_every_row(full_lce):
     assert np.any(y >= 151936 - 4480)
     _, _, err = check(H, W, y, ref=full_lce_oracle(full_lce))
     print(f"full size: all {len(y)} rows checked, max |dloss| = {err:.2e}")
+
+
+def test_deepest_reduction():
+    """D = 2^22, the largest depth the call accepts: 65,536 K stages in one tile, and row
+    strides of 2^23 bytes inside the tile's 32-bit buffer offsets."""
+    N, D, V = 3, 1 << 22, 5
+    H, W, y = inputs.linear_ce(N, D, V, seed_stream=22)
+    _, _, err = check(H, W, y)
+    print(f"D = 2^22: max |dloss| = {err:.2e}")
