@@ -331,6 +331,55 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a0, TileArgs a1
     // targets of this tile's rows, for the epilogue
     if constexpr (!kGemm) tile_targets[tid] = row0 + tid < a.N ? a.targets[row0 + tid] : -1;
     issue(0, 0);
+    if constexpr (kGemm) {
+        // An accumulating product starts from C's old values, loaded while the first
+        // stage's DMA is in flight, so its epilogue only stores.  (Read and added in the
+        // epilogue, every load waited for the store before it: the compiler does not move
+        // a load across a store to the same array.)  A row block's 16 vectors are loaded
+        // together, the next block's while this one moves into the accumulators.
+        if (a.accumulate) {
+            const int64_t r0w = row0 + wm * WT, c0w = col0 + wn * WT;
+            if (c0w + WT <= a.c_end) {
+                float4 buf[2][FB * 4];
+                auto load_block = [&](int i, float4 (&b)[FB * 4]) {
+                    const int64_t row = r0w + i * 32 + l32;
+                    const float* crow = a.C + (row < a.N ? row : a.N - 1) * a.ldc - a.c0 + c0w + 4 * h2;
+#pragma unroll
+                    for (int jq = 0; jq < FB * 4; ++jq)
+                        b[jq] = *reinterpret_cast<const float4*>(crow + (jq / 4) * 32 + 8 * (jq % 4));
+                };
+                load_block(0, buf[0]);
+#pragma unroll
+                for (int i = 0; i < FB; ++i) {
+                    if (i + 1 < FB) load_block(i + 1, buf[(i + 1) & 1]);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int jq = 0; jq < FB * 4; ++jq) {
+                        const float4 o = buf[i & 1][jq];
+                        const int j = jq / 4, q = jq % 4;
+                        acc[i][j][4 * q] = o.x;
+                        acc[i][j][4 * q + 1] = o.y;
+                        acc[i][j][4 * q + 2] = o.z;
+                        acc[i][j][4 * q + 3] = o.w;
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < FB; ++i) {
+                    const int64_t row = r0w + i * 32 + l32;
+                    const float* crow = a.C + (row < a.N ? row : a.N - 1) * a.ldc - a.c0;
+#pragma unroll
+                    for (int j = 0; j < FB; ++j)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) {
+                            const int64_t c = c0w + j * 32 + 8 * (e / 4) + 4 * h2 + e % 4;
+                            acc[i][j][e] = c < a.c_end ? crow[c] : 0.f;
+                        }
+                }
+            }
+        }
+    }
     wait_stage();
     zero_tail(0, 0);
     lds_barrier();
@@ -374,8 +423,10 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a0, TileArgs a1
     auto col_of = [&](int j, int e) { return j * 32 + 8 * (e / 4) + 4 * h2 + (e % 4); };
 
     if constexpr (kGemm) {
-        // acc[i][j][4q .. 4q + 3] are 4 consecutive columns of one row: 16-byte stores
-        // (or load, add, store), one row per lane, in a fixed order.
+        // acc[i][j][4q .. 4q + 3] are 4 consecutive columns of one row: 16-byte stores,
+        // one row per lane, in a fixed order (an accumulating product started from C's
+        // old values).
+        //
 #pragma unroll
         for (int i = 0; i < FB; ++i) {
             const int64_t row = wrow0 + i * 32 + l32;
@@ -388,19 +439,11 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a0, TileArgs a1
                     const int64_t c = wcol0 + j * 32 + 8 * q + 4 * h2;
                     float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
                     if (c + 3 < a.c_end) {
-                        float4* p = reinterpret_cast<float4*>(crow + c);
-                        if (a.accumulate) {
-                            const float4 o = *p;
-                            v[0] += o.x;
-                            v[1] += o.y;
-                            v[2] += o.z;
-                            v[3] += o.w;
-                        }
-                        *p = make_float4(v[0], v[1], v[2], v[3]);
+                        *reinterpret_cast<float4*>(crow + c) = make_float4(v[0], v[1], v[2], v[3]);
                     } else {
 #pragma unroll
                         for (int t = 0; t < 4; ++t)
-                            if (c + t < a.c_end) crow[c + t] = a.accumulate ? crow[c + t] + v[t] : v[t];
+                            if (c + t < a.c_end) crow[c + t] = v[t];
                     }
                 }
         }
@@ -411,6 +454,16 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a0, TileArgs a1
         // through this wave's LDS block first, so that it leaves in 16-byte stores of 8
         // rows of a column.  After the barrier no wave reads the stage buffers any more
         // (the last DMA has landed: wait_stage above).
+        // this lane's rows' saved (m, log s) and upstream gradients, loaded together
+        float2 lse_r[FB];
+        float g_r[FB];
+#pragma unroll
+        for (int i = 0; i < FB; ++i) {
+            const int64_t row = wrow0 + i * 32 + l32;
+            const int64_t rr = row < a.N ? row : a.N - 1;
+            lse_r[i] = a.lse[rr];
+            g_r[i] = a.g[rr];
+        }
         lds_barrier();
         char* const tblk = smem + wave * kWaveStaging;
         auto tput = [&](int cl, int rl, uint16_t v) {
@@ -422,10 +475,10 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a0, TileArgs a1
             const int64_t row = row0 + lr;
             if (row >= a.N) continue;
             const int32_t y = tile_targets[lr];
-            const float2 l = a.lse[row];
+            const float2 l = lse_r[i];
             const float m = (y >= 0 && (int64_t)y < a.V) ? l.x : __builtin_nanf("");
             const float nlsl = -l.y * kLog2e;
-            const float gr = a.g[row];
+            const float gr = g_r[i];
             __bf16* grow = a.G + row * a.ldG - a.c0;
             const int rl = i * 32 + l32;  // row within the wave's block
             auto dz = [&](float z) { return gr * __builtin_amdgcn_exp2f(__builtin_fmaf(z - m, kLog2e, nlsl)); };
