@@ -240,6 +240,8 @@ struct LceGradChunk {
     int64_t ldG;
     void* GT;     // the same chunk transposed, [width][ldGT]
     int64_t ldGT;
+    void* WT;     // W's rows c0 .. c0 + width - 1 transposed, [D][ldWT], zero up to the
+    int64_t ldWT; // next multiple of 8 columns
     hipStream_t stream;
 };
 

@@ -11,8 +11,9 @@
 //   dH        += dZ_c  W_c       (N x D, every chunk adds its share)
 //   dW[c0:c1]  = dZ_c^T H        (the chunk's own rows of dW)
 // The K loop reads both operands K-contiguous, so W_c and H enter these products
-// transposed: H^T once per call, W_c^T once per chunk (lce_transpose).  K is padded to
-// a multiple of 8 with zeros in both operands.  Everything runs on the caller's stream
+// transposed: H^T once per call (lce_transpose), W_c^T by the dZ tiles themselves from
+// the W rows they stage through LDS.  K is padded to a multiple of 8 with zeros in both
+// operands.  Everything runs on the caller's stream
 // in the caller's workspace; nothing is allocated and no state is kept between calls.
 #include <hip/hip_runtime.h>
 
@@ -70,16 +71,14 @@ LceBackwardStatus run_lce_backward(const LceBackwardCall& c) {
     // chunk (the tile kernel writes only columns below N): the K padding of dW's product
     if (!ok(launch_transpose_bf16(c.H, c.N, c.D, c.D, HT, n8, n8, c.stream))) return LceBackwardStatus::kHip;
     if (!ok(launch_zero_cols_bf16(GT, kChunk, n8, c.N, n8, c.stream))) return LceBackwardStatus::kHip;
-    const char* Wb = static_cast<const char*>(c.W);
     for (int64_t c0 = 0; c0 < c.V; c0 += kChunk) {
         const int64_t w = c.V - c0 < kChunk ? c.V - c0 : kChunk;
         const int64_t w8 = round8(w);
-        LceGradChunk gc{c.H, c.W, c.targets, c.lse, c.g, c.N, c.D, c.V, c0, w, G, kChunk, GT, n8, c.stream};
+        // dZ_c in both layouts, and W_c^T [D][w8] (zero past w) written by the same tiles
+        LceGradChunk gc{c.H, c.W, c.targets, c.lse, c.g, c.N, c.D, c.V, c0, w, G, kChunk, GT, n8, WT, kChunk, c.stream};
         if (!ok(launch_lce_grad_chunk(gc))) return LceBackwardStatus::kHip;
-        // W_c^T [D][w8], zero past w; and dZ_c's columns w .. w8 - 1 (stale from an earlier
-        // chunk) zeroed, so the padded K adds nothing
-        if (!ok(launch_transpose_bf16(Wb + c0 * c.D * 2, w, c.D, c.D, WT, kChunk, w8, c.stream)))
-            return LceBackwardStatus::kHip;
+        // dZ_c's columns w .. w8 - 1 (stale from an earlier chunk) zeroed, so the padded K
+        // adds nothing
         if (w8 > w && !ok(launch_zero_cols_bf16(G, c.N, kChunk, w, w8, c.stream))) return LceBackwardStatus::kHip;
         // dH [N][D] (+)= dZ_c [N][w8] . (W_c^T [D][w8])^T, and
         // dW[c0 : c0 + w] [w][D] = dZ_c^T [w][N8] . (H^T [D][N8])^T, in one launch

@@ -39,6 +39,8 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
 
 constexpr int BM = 256;              // rows of H per tile
 constexpr int BN = 256;              // rows of W (vocabulary columns) per tile
@@ -85,6 +87,8 @@ struct TileArgs {
     int64_t ldG;
     __bf16* GT;         // the same chunk transposed: [width][ldGT], column c as row c - c0
     int64_t ldGT;
+    __bf16* WT;         // the W chunk transposed: [K][ldWT], W row c as column c - c0, zero
+    int64_t ldWT;       // up to the next multiple of 8 columns
     // plain product: C[r][c - c0] (+)= Z[r][c], fp32, row r at C + r * ldc
     float* C;
     int64_t ldc;
@@ -311,13 +315,59 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a0, TileArgs a1
             (chunk(std::integral_constant<int, C>{}), ...);
         }(std::make_integer_sequence<int, 8>{});
     };
+    // kTileGrad also writes the W chunk transposed (the B operand of the dH product),
+    // from the stage buffers, so no separate transpose pass reads W again: stage s of
+    // the K loop is written by the tile whose row tile is s % n_row_tiles, so the row
+    // tiles of a column tile share the work.  ds_read_b64_tr_b16 transposes within each
+    // 16-lane group: output lane j, element e takes element j % 4 of the 8 bytes that
+    // lane j / 4 + 4 e addresses.  Lane j of group g addresses tile row cb + j / 4 and
+    // K values kb + 4 (j % 4) .. + 3, so it receives K value kb + j of tile rows
+    // cb .. cb + 3; a second read gives rows cb + 4 .. cb + 7, and the lane stores the 8
+    // of them as 16 bytes of WT row kb + j.  Columns past the chunk are stored as zeros
+    // up to the next multiple of 8 (the K padding of the dH product).  A stage is read
+    // for this when its loads have landed and before the barrier that frees its buffer,
+    // with no stage load in flight (the compiler waits for every LDS load in flight
+    // before a transposing read).
+    auto put_wt = [&](int s, int buf) {
+        const char* Bs = &lds[buf][1][0];
+        const int g4 = lane >> 4, j = lane & 15;
+        const int64_t wt_w8 = (a.c_end - a.c0 + 7) & ~(int64_t)7;
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int kb = 16 * (it >> 1);
+            const int cb = wave * 64 + 32 * (it & 1) + 8 * g4;
+            const int kk = kb + 4 * (j & 3);
+            auto off = [&](int row) { return row * 128 + (((kk >> 3) ^ ((row >> 1) & 7)) << 4) + (kk & 7) * 2; };
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(Bs + off(cb + (j >> 2))));
+            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(Bs + off(cb + 4 + (j >> 2))));
+            const int64_t kg = (int64_t)s * BK + kb + j;
+            const int64_t cg = col0 + cb;  // vocabulary column of the first of the 8
+            if (kg < a.K && cg - a.c0 < wt_w8) {
+                U4 v;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const uint32_t e0 = cg + 2 * t < a.c_end
+                        ? (uint16_t)(t < 2 ? lo[2 * t] : hi[2 * t - 4]) : 0u;
+                    const uint32_t e1 = cg + 2 * t + 1 < a.c_end
+                        ? (uint16_t)(t < 2 ? lo[2 * t + 1] : hi[2 * t - 3]) : 0u;
+                    v.w[t] = e0 | (e1 << 16);
+                }
+                store_u4(reinterpret_cast<uint16_t*>(a.WT) + kg * a.ldWT + (cg - a.c0), v);
+            }
+        }
+    };
+    auto owns_stage = [&](int s) { return s % a.n_row_tiles == row_tile; };
+
     auto sync_stage = [&](int kt, int cur, int nk) {
         // stage kt + 1 has landed (issued one stage earlier); after this barrier every
         // wave has finished reading buffer `cur`, which then takes stage kt + 2
         wait_stage();
         if (kt + 1 < nk) zero_tail(kt + 1, cur ^ 1);
+        if constexpr (kGrad)
+            if (owns_stage(kt)) put_wt(kt, cur);
         lds_barrier();
     };
+
 
     // Pipeline: the fragments of a K16 step are read from LDS two steps ahead, into four
     // rotating sets, so each wave keeps twice as many reads in flight (one wave per SIMD
@@ -414,6 +464,8 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a0, TileArgs a1
     }
     // the last loop iteration's (redundant) DMA must land before the workgroup can end
     wait_stage();
+    if constexpr (kGrad)
+        if (owns_stage(nk - 1)) put_wt(nk - 1, (nk - 1) & 1);
 
     // ---- epilogue: (m, s) per row over this wave's 128 columns ----------------
     // acc[i][j][e] holds Z[row = wrow0 + i*32 + l32][col = wcol0 + j*32 + 8*(e/4) + 4*h2 + e%4]:
@@ -746,6 +798,8 @@ hipError_t launch_lce_grad_chunk(const LceGradChunk& c) {
     a.ldG = c.ldG;
     a.GT = static_cast<__bf16*>(c.GT);
     a.ldGT = c.ldGT;
+    a.WT = static_cast<__bf16*>(c.WT);
+    a.ldWT = c.ldWT;
     hipLaunchKernelGGL(lce_tile<kTileGrad>, dim3((unsigned)g.blocks), dim3(kThreads), 0, c.stream, a, a, (int)g.blocks);
     return hipGetLastError();
 }

@@ -16,25 +16,35 @@ barrier after its wait) shares an epoch with a read of the same buffer.
 import pytest
 
 
-def schedule(nk):
-    """Per-wave events: ('dma', stage, buf), ('wait',), ('barrier',), ('read', stage, step, buf)."""
+def schedule(nk, grad=False):
+    """Per-wave events: ('dma', stage, buf), ('wait',), ('barrier',), ('read', stage, step, buf).
+
+    With grad, the gradient tiles' transposing reads of the W rows (step 'wt') are added
+    where the kernel makes them: a stage's, after the wait that lands the next stage and
+    before the barrier that frees the stage's buffer; the last stage's, after the final
+    wait."""
     ev = [("dma", 0, 0), ("wait",), ("barrier",)]
     if nk > 1:
         ev.append(("dma", 1, 1))
     ev += [("read", 0, 0, 0), ("read", 0, 1, 0)]
     for kt in range(nk - 1):
         cur = kt & 1
-        ev += [("read", kt, 2, cur), ("read", kt, 3, cur), ("wait",), ("barrier",)]
+        ev += [("read", kt, 2, cur), ("read", kt, 3, cur), ("wait",)]
+        if grad:
+            ev.append(("read", kt, "wt", cur))
+        ev.append(("barrier",))
         # the last iteration re-loads stage nk - 1 into the free buffer (never read)
         ev.append(("dma", min(kt + 2, nk - 1), cur))
         ev += [("read", kt + 1, 0, cur ^ 1), ("read", kt + 1, 1, cur ^ 1)]
     cur = (nk - 1) & 1
     ev += [("read", nk - 1, 2, cur), ("read", nk - 1, 3, cur), ("wait",)]
+    if grad:
+        ev.append(("read", nk - 1, "wt", cur))
     return ev
 
 
-def check(nk):
-    ev = schedule(nk)
+def check(nk, grad=False):
+    ev = schedule(nk, grad)
     epoch = 0
     pending = []          # DMAs issued and not yet waited for: (stage, buf, issue epoch)
     writes = []           # (buf, first epoch, last epoch) of each DMA's write window
@@ -71,16 +81,34 @@ def check(nk):
 
 
 @pytest.mark.parametrize("nk", [1, 2, 3, 4, 5, 64, 65])
-def test_two_ahead_pipeline_has_no_lds_race(nk):
-    check(nk)
+@pytest.mark.parametrize("grad", [False, True])
+def test_two_ahead_pipeline_has_no_lds_race(nk, grad):
+    check(nk, grad)
+
+
+def test_model_catches_transposing_reads_after_the_barrier():
+    """Reading a stage's W rows after its buffer is freed (past the barrier) is a race."""
+    real = schedule
+
+    def late(nk, grad=False):
+        ev = [e for e in real(nk) if e[0] != "read" or e[2] != "wt"]
+        k = [i for i, e in enumerate(ev) if e[0] == "barrier"][2]
+        return ev[:k + 2] + [("read", 1, "wt", 1)] + ev[k + 2:]
+
+    globals()["schedule"] = late
+    try:
+        with pytest.raises(AssertionError):
+            check(4)
+    finally:
+        globals()["schedule"] = real
 
 
 def test_model_catches_a_missing_barrier():
     """The checker itself: dropping the stage barrier must be reported."""
     real = schedule
 
-    def no_barrier(nk):
-        ev = real(nk)
+    def no_barrier(nk, grad=False):
+        ev = real(nk, grad)
         i = [k for k, e in enumerate(ev) if e[0] == "barrier"][1]
         return ev[:i] + ev[i + 1:]
 
@@ -96,8 +124,8 @@ def test_model_catches_reads_three_ahead_with_this_barrier():
     """Reading a third step ahead (stage kt + 1 step 2 before the barrier) is a race."""
     real = schedule
 
-    def too_far(nk):
-        ev = real(nk)
+    def too_far(nk, grad=False):
+        ev = real(nk, grad)
         k = [i for i, e in enumerate(ev) if e[0] == "wait"][1]
         return ev[:k] + [("read", 1, 2, 1)] + ev[k:]
 
