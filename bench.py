@@ -61,8 +61,8 @@ TRAFFIC = {
         "bytes": 1245011439
     },
     "lce_forward": {
-        "source_sha": "c9ff99abf2322c9a",
-        "bytes": 15158470975
+        "source_sha": "5de886ef8019db06",
+        "bytes": 15162380832
     },
     "kl_forward": {
         "source_sha": "42aeba87f95176d4",
@@ -97,8 +97,8 @@ TRAFFIC = {
         "bytes": 936533902
     },
     "lce_backward": {
-        "source_sha": "c9ff99abf2322c9a",
-        "bytes": 61966799543
+        "source_sha": "5de886ef8019db06",
+        "bytes": 58952536254
     },
     "ce_forward f32 [1048576 x 8]": {
         "source_sha": "99c755947d60a7be",
@@ -858,12 +858,12 @@ def main():
                                      "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS,
                                      "traffic": traffic_for("lce_backward"),
                                      "ms": bwd_ms, "algorithmic_flop": fl,
-                                     "kernels": "H transposed once; per 8192-column chunk: lce_tile (dZ epilogue), "
-                                                "the W chunk transposed, one lce_tile launch of both products "
-                                                "(one lce_backward call)",
-                                     "traffic_note": "FETCH_SIZE + WRITE_SIZE over the call's 58 launches; writes "
-                                                     "11.3 GB (two dZ copies, dH read and written per chunk, dW, "
-                                                     "the transposes)"}
+                                     "kernels": "H transposed once; per 8192-column chunk: lce_tile (dZ epilogue, "
+                                                "and the W chunk transposed from its LDS stages), one lce_tile "
+                                                "launch of both products (one lce_backward call)",
+                                     "traffic_note": "FETCH_SIZE + WRITE_SIZE over the call's 39 launches; writes "
+                                                     "11.4 GB (two dZ copies and the W chunk transposed, dH "
+                                                     "written per chunk, dW, H transposed)"}
         cfg["lce_backward"] = {"N": LCE_N, "D": LCE_D, "V": LCE_V, "out": "fp32 dH, dW", "timed": "apart"}
     for key, tms, (fb, vb), names, cfgv in (
             ("kl_fwd_vjp", kl_ms, kl_bytes(KL_ROWS, KL_V, 4), ("kl_forward", "kl_vjp"),
