@@ -31,9 +31,10 @@
  * - Every argument is checked on the host before any launch.  A failed check returns
  *   a negative ce_status and enqueues nothing.  n_rows == 0 (or N == 0) is a no-op
  *   that returns CE_OK, except that lce_backward still writes dW = 0.  A failed
- *   launch returns CE_ERR_LAUNCH.  No C++ exception crosses this boundary, and the
- *   library's only mutable state is per host thread, so the calls may be made from
- *   several host threads at once.
+ *   launch returns CE_ERR_LAUNCH.  No C++ exception crosses this boundary.  The
+ *   library's only mutable state is set once per GPU and then read (the GPU's compute
+ *   unit count, and the address of ce_forward_ex_noalloc's array), so the calls may be
+ *   made from several host threads at once.
  * - Rows are indexed with 64-bit integers end to end; no launch wraps a 32-bit
  *   grid, however many rows there are.  (MLX PR #4776 "fast.cross_entropy silently
  *   skips rows when the Metal grid gets too large", Issue: a 32-bit grid of
@@ -208,9 +209,11 @@ ce_status lce_forward(const void* H, const void* W, const int32_t* targets, int6
 
 /*
  * lce_backward_workspace_size: bytes of device workspace lce_backward needs for
- * (N, D, V): one 8192-column chunk of the logits gradient in bf16, row-major and
- * transposed (2 * N * 16 KiB), plus 64 MiB of GEMM scratch.  Returns 0 for arguments
- * lce_backward would reject.
+ * (N, D, V): with C = min(8192, V rounded up to 256) columns per chunk and N8 = N
+ * rounded up to 8, four bf16 arrays, each starting on a 256-byte boundary: the logits
+ * gradient chunk [N][C], its transpose [C][N8], H^T [D][N8] and the W chunk's transpose
+ * [D][C] (384 MiB at N = 8192, D = 4096).  Returns 0 for arguments lce_backward would
+ * reject.
  */
 size_t lce_backward_workspace_size(int64_t N, int64_t D, int64_t V);
 
@@ -224,11 +227,13 @@ size_t lce_backward_workspace_size(int64_t N, int64_t D, int64_t V);
  * chunk of 8192 vocabulary columns (the page's tile width), the forward's MFMA tile
  * kernel recomputes the chunk of Z and its epilogue writes
  * dZ = g_i (exp((z - m_i) - log s_i) - [col == y_i]) in bf16 (round to nearest even)
- * into the workspace, row-major and transposed.  The same MFMA K loop then adds
- * dZ_c W_c into dH and writes dZ_c^T H into the chunk's rows of dW, both with float32
- * accumulation; it reads W_c and H through transposed bf16 copies in the workspace (H
- * once per call, W_c once per chunk).  The call is made of kernels only (no library
- * calls, no memsets), so it can be captured in a HIP graph.
+ * into the workspace, row-major and transposed, and the same tiles write the W chunk
+ * transposed from the W rows they stage.  The same MFMA K loop then adds dZ_c W_c into
+ * dH and writes dZ_c^T H into the chunk's rows of dW, both with float32 accumulation
+ * (dH is one sequential sum over the vocabulary: each chunk's tiles start from its
+ * previous value); H enters through a transposed copy made once per call.  The call is
+ * made of kernels only (no library calls, no memsets), so it can be captured in a HIP
+ * graph.
  *
  *   H, W, targets  as in lce_forward.
  *   lse      float32 [N][2], the (m, log s) pairs lce_forward wrote for the same H, W.
@@ -256,7 +261,9 @@ ce_status lce_backward(const void* H, const void* W, const int32_t* targets, con
  * of the student and teacher logits), and section "Sixty-four floats" (one pass per
  * row with an online log-sum-exp per distribution, combined across waves through
  * shared memory).  Each lane keeps (m_q, s_q), (m_p, s_p) and
- * t = sum_j exp(p_j - m_p) (p_j - q_j); then kl = t / s_p - (m_p + log s_p) + (m_q + log s_q).
+ * t = sum_j exp(p_j - m_p) ((p_j - m_p) - (q_j - m_q)), every term taken against its own
+ * row's running maximum (and t moved with them when either maximum rises), so rows
+ * with different offsets lose nothing to cancellation; then kl = t / s_p + log s_q - log s_p.
  *
  *   q, p     student and teacher logits, [n_rows rows of V] of dtype `dt`, each
  *            addressed through its own layout (as the logits of ce_forward).
