@@ -343,13 +343,14 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a0, TileArgs a1
             const int64_t kg = (int64_t)s * BK + kb + j;
             const int64_t cg = col0 + cb;  // vocabulary column of the first of the 8
             if (kg < a.K && cg - a.c0 < wt_w8) {
+                // the 8 columns cg .. cg + 7: lo holds the first 4, hi the next 4; columns
+                // at or past the chunk's end are stored as 0
+                const short e[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 U4 v;
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    const uint32_t e0 = cg + 2 * t < a.c_end
-                        ? (uint16_t)(t < 2 ? lo[2 * t] : hi[2 * t - 4]) : 0u;
-                    const uint32_t e1 = cg + 2 * t + 1 < a.c_end
-                        ? (uint16_t)(t < 2 ? lo[2 * t + 1] : hi[2 * t - 3]) : 0u;
+                    const uint32_t e0 = cg + 2 * t < a.c_end ? (uint16_t)e[2 * t] : 0u;
+                    const uint32_t e1 = cg + 2 * t + 1 < a.c_end ? (uint16_t)e[2 * t + 1] : 0u;
                     v.w[t] = e0 | (e1 << 16);
                 }
                 store_u4(reinterpret_cast<uint16_t*>(a.WT) + kg * a.ldWT + (cg - a.c0), v);
