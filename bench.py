@@ -61,7 +61,7 @@ TRAFFIC = {
         "bytes": 1245011439
     },
     "lce_forward": {
-        "source_sha": "5de886ef8019db06",
+        "source_sha": "8fae8629243acc1a",
         "bytes": 15162380832
     },
     "kl_forward": {
@@ -97,7 +97,7 @@ TRAFFIC = {
         "bytes": 936533902
     },
     "lce_backward": {
-        "source_sha": "5de886ef8019db06",
+        "source_sha": "8fae8629243acc1a",
         "bytes": 58952536254
     },
     "ce_forward f32 [1048576 x 8]": {
