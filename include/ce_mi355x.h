@@ -136,6 +136,8 @@ ce_status ce_forward(const void* logits, ce_layout in, ce_dtype dt, const int32_
  *   g       float32 [n_rows], contiguous.
  *   dlogits [n_rows rows of V] of dtype `dt`, addressed through `out` (written).
  *           Values are computed in float32 and rounded to dt to nearest, ties to even.
+ *           bf16 results in the subnormal range (below 2^-126) are delivered too,
+ *           for |g| < 2^103; this holds for every VJP in this header that writes bf16.
  * dlogits may be the logits themselves (an in-place VJP) only with an identical
  * layout; otherwise it must not overlap the logits, targets, lse or g (CE_ERR_ALIAS).
  * The output is always the caller's buffer: no library temporary is ever shared

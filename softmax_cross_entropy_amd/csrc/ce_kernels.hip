@@ -211,33 +211,45 @@ __global__ __launch_bounds__(64 * NW) void ce_fwd_rowwg(FwdArgs a) {
 
 // ---- VJP ------------------------------------------------------------------------
 
+// Per-row constants of the gradient, on the output type's exponent shift S (out_shift):
+// the kernels form g p as (g 2^-S) (2^S p) and g (p - 1) as (g 2^-S) (2^S p - 2^S).
 struct RowGrad {
     float m;    // row maximum, or NaN for a row whose target is out of range
-    float lsl;  // log(s) * log2(e)
-    float g;
+    float c;    // S - log(s) log2(e)
+    float g;    // g 2^-S
+    float one;  // 2^S
     int32_t y;
 };
 
+template <typename T>
+__device__ __forceinline__ void set_row_scale(RowGrad& rg, float ls, float g) {
+    const int S = out_shift<T>(g);
+    rg.c = (float)S - ls * kLog2e;
+    rg.g = __builtin_ldexpf(g, -S);
+    rg.one = __builtin_ldexpf(1.0f, S);
+}
+
+template <typename T>
 __device__ __forceinline__ RowGrad load_row_grad(const VjpArgs& a, int64_t r) {
     RowGrad rg;
     rg.y = a.targets[r];
     const float2 l = a.lse[r];
     rg.m = target_ok(rg.y, a.V) ? l.x : __builtin_nanf("");
-    rg.lsl = l.y * kLog2e;
-    rg.g = a.g[r];
+    set_row_scale<T>(rg, l.y, a.g[r]);
     return rg;
 }
 
-// softmax probability of logit z: exp((z - m) - log s) = 2^((z - m) log2 e - log s log2 e).
-// z - m is formed first (exact for nearby logits), and one fused multiply-add applies
-// log2 e and subtracts log s: no large magnitude ever meets the small gap.
+// softmax probability of logit z, times 2^S: exp((z - m) - log s) 2^S = 2^((z - m) log2 e +
+// S - log s log2 e).  z - m is formed first (exact for nearby logits), and one fused
+// multiply-add applies log2 e and the row's constant: no large magnitude ever meets the
+// small gap.
 __device__ __forceinline__ float prob(float z, const RowGrad& rg) {
-    return __builtin_amdgcn_exp2f(__builtin_fmaf(z - rg.m, kLog2e, -rg.lsl));
+    return __builtin_amdgcn_exp2f(__builtin_fmaf(z - rg.m, kLog2e, rg.c));
 }
 
 __device__ __forceinline__ float grad_elem(float z, const RowGrad& rg, bool is_target) {
     const float p = prob(z, rg);
-    return rg.g * (is_target ? p - 1.0f : p);
+    return rg.g * (is_target ? p - rg.one : p);
 }
 
 // Gradient of one 16-byte vector of logits, written to `dst` inside output row `orow`.  Every element is
@@ -279,7 +291,7 @@ __global__ __launch_bounds__(kBlock) void ce_vjp_narrow(VjpArgs a) {
                 const char* row = reinterpret_cast<const char*>(base + row_offset(r, a.in));
 #pragma unroll
                 for (int v = 0; v < NV; ++v) buf[u][v] = load_u4_stream(row + v * 16);
-                rg[u] = load_row_grad(a, r);
+                rg[u] = load_row_grad<T>(a, r);
             }
         }
 #pragma unroll
@@ -338,7 +350,7 @@ __global__ __launch_bounds__(G > kBlock ? G : kBlock) void ce_vjp_lanes(VjpArgs 
     for (int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / G; r < a.n_rows; r += stride) {
         const T* row = static_cast<const T*>(a.logits) + row_offset(r, a.in);
         T* orow = static_cast<T*>(a.dlogits) + row_offset(r, a.out);
-        grad_row<T, G, U>(row, orow, a.V, lane, load_row_grad(a, r));
+        grad_row<T, G, U>(row, orow, a.V, lane, load_row_grad<T>(a, r));
     }
 }
 
@@ -359,7 +371,7 @@ __global__ __launch_bounds__(kBlock) void ce_vjp_chunks(VjpArgs a, int64_t chunk
         const int64_t c = w - r * chunks_per_row;
         const T* row = static_cast<const T*>(a.logits) + row_offset(r, a.in);
         T* orow = static_cast<T*>(a.dlogits) + row_offset(r, a.out);
-        const RowGrad rg = load_row_grad(a, r);
+        const RowGrad rg = load_row_grad<T>(a, r);
         if (((((uintptr_t)row) ^ ((uintptr_t)orow)) & 15u) == 0) {
             RowSplit<T> sp(row, a.V);
             const char* vb = reinterpret_cast<const char*>(row + sp.head);
@@ -419,6 +431,7 @@ struct FusedArgs {
 
 // Writes the row's loss and pair and returns what the gradient needs, as the forward's
 // store and the VJP's reading of the pair would give them.
+template <typename T>
 __device__ __forceinline__ RowGrad fused_finish(const FusedArgs& a, int64_t r, MS st, float zy, int32_t y,
                                                 bool ok, bool writer) {
     const float ls = log_e(st.s);
@@ -429,8 +442,7 @@ __device__ __forceinline__ RowGrad fused_finish(const FusedArgs& a, int64_t r, M
     RowGrad rg;
     rg.y = y;
     rg.m = ok ? st.m : __builtin_nanf("");
-    rg.lsl = ls * kLog2e;
-    rg.g = a.g[r];
+    set_row_scale<T>(rg, ls, a.g[r]);
     return rg;
 }
 
@@ -472,7 +484,7 @@ __global__ __launch_bounds__(kBlock) void ce_fused_narrow(FusedArgs a) {
                 float zy = 0.0f;
 #pragma unroll
                 for (int k = 0; k < kN; ++k) zy = (y == k) ? f[k] : zy;
-                const RowGrad rg = fused_finish(a, r, st, zy, y, target_ok(y, kN), true);
+                const RowGrad rg = fused_finish<T>(a, r, st, zy, y, target_ok(y, kN), true);
                 // the row is still in registers: no second read
                 char* orow = reinterpret_cast<char*>(obase + row_offset(r, a.out));
 #pragma unroll
@@ -522,7 +534,7 @@ __global__ __launch_bounds__(G > kBlock ? G : kBlock) void ce_fused_rows(FusedAr
             t = ms_group_reduce<NW>(t);
             st = MS{__shfl(t.m, 0), __shfl(t.s, 0)};
         }
-        grad_row<T, G, U>(row, orow, a.V, lane, fused_finish(a, r, st, zy, y, ok, lane == 0));
+        grad_row<T, G, U>(row, orow, a.V, lane, fused_finish<T>(a, r, st, zy, y, ok, lane == 0));
     }
 }
 
@@ -652,7 +664,7 @@ __global__ __launch_bounds__(G) void ce_fused_regs(FusedArgs a) {
         s = 0.0f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) s += sum_slots[w];
-        const RowGrad rg = fused_finish(a, r, MS{m, s}, zy, y, ok, tid == 0);
+        const RowGrad rg = fused_finish<T>(a, r, MS{m, s}, zy, y, ok, tid == 0);
         // pass 3: the gradient from the held registers; each register then takes the
         // next row's vector
         opaque(buf);

@@ -365,12 +365,11 @@ struct OVjpArgs {
 
 struct ORow {
     float m;    // row max, NaN for an invalid index target
-    float lsl;  // log s * log2(e)
-    float g;    // upstream gradient of this row
-    float gW;   // g W (probability targets)
+    float c;    // S - log s * log2(e), S the output type's exponent shift (out_shift)
+    float g;    // coefficient of p times 2^-S: g (index targets) or g W (probability targets)
     float gk;   // g (1 - eps) (probability targets)
     float ge;   // g eps / V, 0 when eps is 0
-    float cy;   // target weight (1 - eps) + eps / V (index targets)
+    float cy;   // target weight ((1 - eps) + eps / V) 2^S (index targets)
     int32_t y;
     int32_t zero;  // ignored row: the gradient is 0 whatever the logits hold
 };
@@ -383,32 +382,37 @@ __device__ __forceinline__ float shared_upstream(const OVjpArgs& a) {
     return (float)((double)a.g[0] / (double)a.count[0]);
 }
 
-template <bool kProbs>
+// The row's constants.  oprob returns 2^S p, so every product with p takes g 2^-S, and
+// every term that p is compared with on its own scale (the target weight) takes 2^S.
+template <typename T, bool kProbs>
 __device__ __forceinline__ ORow load_orow(const OVjpArgs& a, int64_t r, float gs) {
     ORow o;
     const float2 l = a.lse[r];
-    o.lsl = l.y * kLog2e;
-    o.g = a.reduction == 0 ? a.g[r] : gs;
-    o.cy = a.keep + a.eps_v;
+    const float g = a.reduction == 0 ? a.g[r] : gs;
     // eps = 0 leaves g p - 0 = g p, bit for bit, even for an infinite g
-    o.ge = a.eps_v == 0.f ? 0.f : o.g * a.eps_v;
-    o.gk = o.g * a.keep;
+    o.ge = a.eps_v == 0.f ? 0.f : g * a.eps_v;
+    o.gk = g * a.keep;
     o.zero = 0;
-    o.gW = 0.f;
     o.y = -1;
+    float gp = g;
     if constexpr (kProbs) {
         o.m = l.x;
-        o.gW = o.g * a.wsum[r];
+        gp = g * a.wsum[r];
     } else {
         o.y = a.y[r];
         o.zero = a.has_ignore && o.y == a.ignore_index;
         o.m = target_in(o.y, a.V) ? l.x : __builtin_nanf("");
     }
+    const int S = out_shift<T>(gp);
+    o.c = (float)S - l.y * kLog2e;
+    o.g = __builtin_ldexpf(gp, -S);
+    o.cy = __builtin_ldexpf(a.keep + a.eps_v, S);
     return o;
 }
 
+// 2^S p: the softmax probability of z on the row's exponent shift.
 __device__ __forceinline__ float oprob(float z, const ORow& o) {
-    return __builtin_amdgcn_exp2f(__builtin_fmaf(z - o.m, kLog2e, -o.lsl));
+    return __builtin_amdgcn_exp2f(__builtin_fmaf(z - o.m, kLog2e, o.c));
 }
 
 // Gradient of one element, with g folded into the per-row constants: index targets
@@ -418,7 +422,7 @@ template <bool kProbs>
 __device__ __forceinline__ float ograd(float z, float t, const ORow& o) {
     const float p = oprob(z, o);
     if constexpr (kProbs)
-        return __builtin_fmaf(o.gW, p, -__builtin_fmaf(o.gk, t, o.ge));
+        return __builtin_fmaf(o.g, p, -__builtin_fmaf(o.gk, t, o.ge));
     else
         return __builtin_fmaf(o.g, p, -o.ge);
 }
@@ -497,7 +501,7 @@ __global__ __launch_bounds__(G > kBlock ? G : kBlock) void ceo_vjp_lanes(OVjpArg
         const T* z = static_cast<const T*>(a.z) + row_offset(r, a.zl);
         const T* t = kProbs ? static_cast<const T*>(a.t) + row_offset(r, a.tl) : nullptr;
         T* d = static_cast<T*>(a.d) + row_offset(r, a.dl);
-        const ORow o = load_orow<kProbs>(a, r, gs);
+        const ORow o = load_orow<T, kProbs>(a, r, gs);
         if (o.zero) {
             ozero(d, 0, a.V, lane, G);
         } else if (ophases<T, kProbs>(z, t, d)) {
@@ -545,7 +549,7 @@ __global__ __launch_bounds__(kBlock) void ceo_vjp_chunks(OVjpArgs a, int64_t chu
         const T* z = static_cast<const T*>(a.z) + row_offset(r, a.zl);
         const T* t = kProbs ? static_cast<const T*>(a.t) + row_offset(r, a.tl) : nullptr;
         T* d = static_cast<T*>(a.d) + row_offset(r, a.dl);
-        const ORow o = load_orow<kProbs>(a, r, gs);
+        const ORow o = load_orow<T, kProbs>(a, r, gs);
         if (o.zero) {
             // the same element ranges as the path for rows in different 16-byte phases
             const int64_t e0 = c * kChunkVec * kVec;

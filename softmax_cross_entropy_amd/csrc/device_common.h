@@ -30,6 +30,29 @@ __device__ __forceinline__ float log_e(float x) {
     return __builtin_amdgcn_logf(x) * kLn2;
 }
 
+// Exponent shift S for gradients written in bfloat16.  bfloat16 shares float32's exponent
+// range, so its subnormals [2^-133, 2^-126) lie below the smallest normal float32, where
+// v_exp_f32 returns 0.  A bf16 gradient g p is therefore formed as (g 2^-S) (2^S p): the
+// shift goes into the exponent's constant, the factor into g, and the product rounds once,
+// into float32's subnormal range where it must.  With e = floor(log2 |g|) and a further
+// factor of up to 2^7 on p when extra = 8, every product of at least 2^-134 (half the
+// smallest bf16 subnormal) needs p >= 2^(-135 - e - extra), which 2^S p keeps normal when
+// S = e + 9 + extra; g 2^-S is then about 2^(-9 - extra) and exact.  S is clamped to
+// [0, 120]: at 0 the needed p are normal already, and at 120 the scaled values (times 2^7)
+// stay below float32's overflow, which covers every |g| < 2^(111 - extra).  Other output
+// types use S = 0, which leaves their arithmetic bit for bit as without it.
+template <typename T>
+__device__ __forceinline__ int out_shift(float g, int extra = 0) {
+    if constexpr (__is_same(T, __bf16)) {
+        // frexp's exponent is floor(log2 |g|) + 1; zero, infinities and NaN give 0, and any
+        // shift serves them
+        const int s = __builtin_amdgcn_frexp_expf(g) + 8 + extra;
+        return s < 0 ? 0 : (s > 120 ? 120 : s);
+    } else {
+        return 0;
+    }
+}
+
 // Reference point for rescaling.  A state that has seen only -inf (or nothing) has
 // m = -inf and s = 0; rescaling against -inf would form exp(-inf - -inf) = NaN, so it
 // rescales against 0 instead, which leaves s = 0 and keeps the state an identity.

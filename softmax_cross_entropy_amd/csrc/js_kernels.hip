@@ -258,15 +258,24 @@ struct JSVjpArgs {
 struct JSGrad {
     JSRow r;
     float H2;  // H in bits
-    float gl;  // g ln 2
+    float gl;  // g ln 2 (times 2^-S)
 };
 
+// The row's constants on the output type's exponent shift S (out_shift, with room for the
+// factor h2 - H2, below 2^7 in size wherever 2^S Q is nonzero): both log2-probabilities
+// carry + S, so Q comes out times 2^S while their difference d keeps its value, and g ln 2
+// is taken times 2^-S.
+template <typename T>
 __device__ __forceinline__ JSGrad js_grad_row(const JSVjpArgs& a, int64_t r) {
     const float2 lq = a.lse_q[r], lp = a.lse_p[r];
-    return JSGrad{JSRow{lq.x, lq.y * kLog2e, lp.x, lp.y * kLog2e}, a.hq[r] * kLog2e, a.g[r] * kLn2};
+    const float gl = a.g[r] * kLn2;
+    const int S = out_shift<T>(gl, 8);
+    return JSGrad{JSRow{lq.x, lq.y * kLog2e - (float)S, lp.x, lp.y * kLog2e - (float)S}, a.hq[r] * kLog2e,
+                  __builtin_ldexpf(gl, -S)};
 }
 
-// g Q (h - H) = g ln 2 Q (h2 - H2), h2 = (1 - sp2(d)) / 2 in bits; 0 where Q = 0.
+// g Q (h - H) = g ln 2 Q (h2 - H2), h2 = (1 - sp2(d)) / 2 in bits; 0 where Q = 0.  uq and up
+// are the log2-probabilities plus S, so Q here is 2^S Q.
 __device__ __forceinline__ float js_grad(float q, float p, const JSGrad& w) {
     const float uq = __builtin_fmaf(q - w.r.mq, kLog2e, -w.r.lq2);
     const float up = __builtin_fmaf(p - w.r.mp, kLog2e, -w.r.lp2);
@@ -303,7 +312,7 @@ __global__ __launch_bounds__(G > kBlock ? G : kBlock) void js_vjp_lanes(JSVjpArg
         const T* q = static_cast<const T*>(a.q) + row_offset(r, a.ql);
         const T* p = static_cast<const T*>(a.p) + row_offset(r, a.pl);
         T* d = static_cast<T*>(a.dq) + row_offset(r, a.dl);
-        const JSGrad w = js_grad_row(a, r);
+        const JSGrad w = js_grad_row<T>(a, r);
         if (js_phases(q, p, d)) {
             RowSplit<T> sp(q, a.V);
             const char* qb = reinterpret_cast<const char*>(q + sp.head);
@@ -345,7 +354,7 @@ __global__ __launch_bounds__(kBlock) void js_vjp_chunks(JSVjpArgs a, int64_t chu
         const T* q = static_cast<const T*>(a.q) + row_offset(r, a.ql);
         const T* p = static_cast<const T*>(a.p) + row_offset(r, a.pl);
         T* d = static_cast<T*>(a.dq) + row_offset(r, a.dl);
-        const JSGrad w = js_grad_row(a, r);
+        const JSGrad w = js_grad_row<T>(a, r);
         if (js_phases(q, p, d)) {
             RowSplit<T> sp(q, a.V);
             const char* qb = reinterpret_cast<const char*>(q + sp.head);

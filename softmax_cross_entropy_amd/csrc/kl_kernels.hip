@@ -241,19 +241,27 @@ struct KLVjpArgs {
     RowLayout dl;
 };
 
+// Per-row constants on the output type's exponent shift S (out_shift): both softmax
+// values come out times 2^S and g is taken times 2^-S.
 struct KLRow {
-    float mq, lqs;  // student max, log s_q * log2(e)
-    float mp, lps;  // teacher max, log s_p * log2(e)
-    float g;
+    float mq, cq;  // student max, S - log s_q * log2(e)
+    float mp, cp;  // teacher max, S - log s_p * log2(e)
+    float g;       // g 2^-S
 };
 
-// softmax value from (z - m) and the pre-scaled log-sum: (z - m) is formed first.
-__device__ __forceinline__ float soft(float z, float m, float ls2) {
-    return __builtin_amdgcn_exp2f(__builtin_fmaf(z - m, kLog2e, -ls2));
+template <typename T>
+__device__ __forceinline__ KLRow kl_row(float2 lq, float2 lp, float g) {
+    const int S = out_shift<T>(g);
+    return KLRow{lq.x, (float)S - lq.y * kLog2e, lp.x, (float)S - lp.y * kLog2e, __builtin_ldexpf(g, -S)};
+}
+
+// softmax value times 2^S from (z - m) and the row's constant: (z - m) is formed first.
+__device__ __forceinline__ float soft(float z, float m, float c) {
+    return __builtin_amdgcn_exp2f(__builtin_fmaf(z - m, kLog2e, c));
 }
 
 __device__ __forceinline__ float kl_grad(float q, float p, const KLRow& r) {
-    return r.g * (soft(q, r.mq, r.lqs) - soft(p, r.mp, r.lps));
+    return r.g * (soft(q, r.mq, r.cq) - soft(p, r.mp, r.cp));
 }
 
 template <typename T, int G, int U>
@@ -268,7 +276,7 @@ __global__ __launch_bounds__(G > kBlock ? G : kBlock) void kl_vjp_lanes(KLVjpArg
         const T* p = static_cast<const T*>(a.p) + row_offset(r, a.pl);
         T* d = static_cast<T*>(a.dq) + row_offset(r, a.dl);
         const float2 lq = a.lse_q[r], lp = a.lse_p[r];
-        const KLRow rw{lq.x, lq.y * kLog2e, lp.x, lp.y * kLog2e, a.g[r]};
+        const KLRow rw = kl_row<T>(lq, lp, a.g[r]);
         const uintptr_t aq = (uintptr_t)q, ap = (uintptr_t)p, ad = (uintptr_t)d;
         if (((aq ^ ap) & 15u) == 0 && ((aq ^ ad) & 15u) == 0) {
             RowSplit<T> sp(q, a.V);
@@ -331,7 +339,7 @@ __global__ __launch_bounds__(kBlock) void kl_vjp_chunks(KLVjpArgs a, int64_t chu
         const T* p = static_cast<const T*>(a.p) + row_offset(r, a.pl);
         T* d = static_cast<T*>(a.dq) + row_offset(r, a.dl);
         const float2 lq = a.lse_q[r], lp = a.lse_p[r];
-        const KLRow rw{lq.x, lq.y * kLog2e, lp.x, lp.y * kLog2e, a.g[r]};
+        const KLRow rw = kl_row<T>(lq, lp, a.g[r]);
         const uintptr_t aq = (uintptr_t)q, ap = (uintptr_t)p, ad = (uintptr_t)d;
         if (((aq ^ ap) & 15u) == 0 && ((aq ^ ad) & 15u) == 0) {
             RowSplit<T> sp(q, a.V);
