@@ -49,104 +49,104 @@ CSRC = os.path.join(ROOT, "softmax_cross_entropy_amd", "csrc")
 # and headers at measurement time: a changed kernel reports traffic null until it is measured again.
 TRAFFIC = {
     "ce_forward_vjp": {
-        "source_sha": "99c755947d60a7be",
-        "bytes": 1278932614
+        "source_sha": "30f4ec33c2551876",
+        "bytes": 1290949953
     },
     "ce_forward": {
-        "source_sha": "99c755947d60a7be",
-        "bytes": 622630005
+        "source_sha": "30f4ec33c2551876",
+        "bytes": 622592051
     },
     "ce_vjp": {
-        "source_sha": "99c755947d60a7be",
-        "bytes": 1245011439
+        "source_sha": "30f4ec33c2551876",
+        "bytes": 1244996369
     },
     "lce_forward": {
-        "source_sha": "8fae8629243acc1a",
-        "bytes": 15162380832
+        "source_sha": "f933e14941467e33",
+        "bytes": 15159317237
     },
     "kl_forward": {
-        "source_sha": "42aeba87f95176d4",
-        "bytes": 622480790
+        "source_sha": "8178fcf06dbd3aed",
+        "bytes": 622484945
     },
     "kl_vjp": {
-        "source_sha": "42aeba87f95176d4",
-        "bytes": 933633265
+        "source_sha": "8178fcf06dbd3aed",
+        "bytes": 933637420
     },
     "ce_forward_ex": {
-        "source_sha": "af1d336c6740cfcc",
-        "bytes": 622626980
+        "source_sha": "9c57c5ac9d01527f",
+        "bytes": 622630759
     },
     "ce_vjp_ex": {
-        "source_sha": "af1d336c6740cfcc",
-        "bytes": 1206054219
+        "source_sha": "9c57c5ac9d01527f",
+        "bytes": 1206070147
     },
     "ce_forward_probs": {
-        "source_sha": "af1d336c6740cfcc",
-        "bytes": 622461195
+        "source_sha": "9c57c5ac9d01527f",
+        "bytes": 622466014
     },
     "ce_vjp_probs": {
-        "source_sha": "af1d336c6740cfcc",
-        "bytes": 933597170
+        "source_sha": "9c57c5ac9d01527f",
+        "bytes": 933601325
     },
     "js_forward": {
-        "source_sha": "f1f68c852e71124b",
-        "bytes": 1224732231
+        "source_sha": "f78dc0c5b2112634",
+        "bytes": 1224837065
     },
     "js_vjp": {
-        "source_sha": "f1f68c852e71124b",
-        "bytes": 936533902
+        "source_sha": "f78dc0c5b2112634",
+        "bytes": 936688206
     },
     "lce_backward": {
-        "source_sha": "8fae8629243acc1a",
-        "bytes": 58952536254
+        "source_sha": "f933e14941467e33",
+        "bytes": 58958544838
     },
     "ce_forward f32 [1048576 x 8]": {
-        "source_sha": "99c755947d60a7be",
-        "bytes": 50499204
+        "source_sha": "30f4ec33c2551876",
+        "bytes": 50514266
     },
     "ce_vjp f32 [1048576 x 8]": {
-        "source_sha": "99c755947d60a7be",
-        "bytes": 83946231
+        "source_sha": "30f4ec33c2551876",
+        "bytes": 83946277
     },
     "ce_forward f32 [65536 x 1024] offsets and -inf rows": {
-        "source_sha": "99c755947d60a7be",
-        "bytes": 270328699
+        "source_sha": "30f4ec33c2551876",
+        "bytes": 270324543
     },
     "ce_vjp f32 [65536 x 1024] offsets and -inf rows": {
-        "source_sha": "99c755947d60a7be",
-        "bytes": 540176116
+        "source_sha": "30f4ec33c2551876",
+        "bytes": 540184772
     },
     "ce_forward f16 [65536 x 1024] offsets and -inf rows": {
-        "source_sha": "99c755947d60a7be",
-        "bytes": 135597295
+        "source_sha": "30f4ec33c2551876",
+        "bytes": 135597030
     },
     "ce_vjp f16 [65536 x 1024] offsets and -inf rows": {
-        "source_sha": "99c755947d60a7be",
-        "bytes": 270106975
+        "source_sha": "30f4ec33c2551876",
+        "bytes": 270105646
     },
     "ce_forward f32 view [10, 119, 32768][:, :-1] (1180 rows)": {
-        "source_sha": "99c755947d60a7be",
-        "bytes": 154859434
+        "source_sha": "30f4ec33c2551876",
+        "bytes": 154859895
     },
     "ce_vjp f32 view [10, 119, 32768][:, :-1] (1180 rows)": {
-        "source_sha": "99c755947d60a7be",
-        "bytes": 309565526
+        "source_sha": "30f4ec33c2551876",
+        "bytes": 309565595
     },
     "ce_forward bf16 [8192 x 32000]": {
-        "source_sha": "99c755947d60a7be",
-        "bytes": 525190108
+        "source_sha": "30f4ec33c2551876",
+        "bytes": 525188798
     },
     "ce_vjp bf16 [8192 x 32000]": {
-        "source_sha": "99c755947d60a7be",
-        "bytes": 1049702958
+        "source_sha": "30f4ec33c2551876",
+        "bytes": 1049704907
     },
     "ce_forward f32 [135266304 x 8]": {
-        "source_sha": "99c755947d60a7be",
-        "bytes": 6600352755
+        "source_sha": "30f4ec33c2551876",
+        "bytes": 6600453393
     },
     "ce_vjp f32 [135266304 x 8]": {
-        "source_sha": "99c755947d60a7be",
-        "bytes": 10824620827
+        "source_sha": "30f4ec33c2551876",
+        "bytes": 10826872504
     }
 }
 
@@ -154,13 +154,14 @@ TRAFFIC = {
 def source_sha(kernel):
     """sha256 (first 16 hex digits) of the kernel's source file and the two headers its
     code depends on (device helpers; launch plans and the constants kernels are built
-    around)."""
+    around), and for lce_backward also the source that lays out its chunks."""
     fname = ("lce_kernels.hip" if kernel.startswith("lce") else
              "kl_kernels.hip" if kernel.startswith("kl") else
              "js_kernels.hip" if kernel.startswith("js") else
              "ce_options.hip" if kernel.endswith(("_ex", "_probs")) else "ce_kernels.hip")
     h = hashlib.sha256()
-    for f in (fname, "device_common.h", "plan.h"):
+    extra = ("lce_backward.cpp",) if kernel == "lce_backward" else ()
+    for f in (fname, "device_common.h", "plan.h") + extra:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -718,19 +719,27 @@ def main():
         G_up = torch.from_numpy(np.random.default_rng([5, 0]).uniform(0.25, 2.0, LCE_N).astype(np.float32)).to(dev)
         dH = torch.empty(LCE_N, LCE_D, dtype=torch.float32, device=dev)
         dW = torch.empty(LCE_V, LCE_D, dtype=torch.float32, device=dev)
-        bws = torch.empty(abi.lce_backward_workspace_size(LCE_N, LCE_D, LCE_V), dtype=torch.uint8, device=dev)
-        for _ in range(2):
-            abi.lce_backward(Hd, Wd, Yd, llse, G_up, dH=dH, dW=dW, workspace=bws)
-        torch.cuda.synchronize()
-        bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.bwd_steps)]
-        for e0, e1 in bev:
-            e0.record(stream)
-            abi.lce_backward(Hd, Wd, Yd, llse, G_up, dH=dH, dW=dW, workspace=bws)
-            e1.record(stream)
-        torch.cuda.synchronize()
-        bwd_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in bev]))
-        del dH, dW, bws
+        # the whole vocabulary as one chunk (the workspace holds all of dZ), then chunks of
+        # 8192 columns (the least workspace the call accepts): same results, both timed
+        bwd_layouts = {}
+        for layout, size in (("one_pass", abi.lce_backward_workspace_size_one_pass),
+                             ("chunks_8192", abi.lce_backward_workspace_size)):
+            bws = torch.empty(size(LCE_N, LCE_D, LCE_V), dtype=torch.uint8, device=dev)
+            for _ in range(2):
+                abi.lce_backward(Hd, Wd, Yd, llse, G_up, dH=dH, dW=dW, workspace=bws)
+            torch.cuda.synchronize()
+            bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.bwd_steps)]
+            for e0, e1 in bev:
+                e0.record(stream)
+                abi.lce_backward(Hd, Wd, Yd, llse, G_up, dH=dH, dW=dW, workspace=bws)
+                e1.record(stream)
+            torch.cuda.synchronize()
+            bwd_layouts[layout] = {"ms": float(np.mean([e0.elapsed_time(e1) for e0, e1 in bev])),
+                                   "workspace_bytes": bws.numel()}
+            del bws
+        bwd_ms = bwd_layouts["one_pass"]["ms"]
+        del dH, dW
 
     # A same-GPU streaming rate beside the 8 TB/s specification: torch's copy of 2 GiB of
     # fp32 (2 GiB read + 2 GiB written), best of 5.  (torch's reductions read well below
@@ -852,19 +861,25 @@ def main():
     if bwd_ms is not None:
         fl = 3 * lce_flops(LCE_N, LCE_D, LCE_V)
         tf = fl / (bwd_ms * 1e-3) / 1e12
+        ch = bwd_layouts["chunks_8192"]
         parts_out["lce_backward"] = {"ms": bwd_ms, "TFLOP_s": tf, "frac_mfma_bf16_peak": tf / MFMA_BF16_PEAK_TFLOPS,
-                                     "flop": fl, "calls": args.bwd_steps, "in_step": False}
+                                     "flop": fl, "calls": args.bwd_steps, "in_step": False,
+                                     "layout": "one chunk over the whole vocabulary",
+                                     "workspace_bytes": bwd_layouts["one_pass"]["workspace_bytes"],
+                                     "chunks_8192": {"ms": ch["ms"], "TFLOP_s": fl / (ch["ms"] * 1e-3) / 1e12,
+                                                     "workspace_bytes": ch["workspace_bytes"],
+                                                     "note": "the least workspace the call accepts; same results"}}
         rooflines["lce_backward"] = {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS,
                                      "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS,
                                      "traffic": traffic_for("lce_backward"),
                                      "ms": bwd_ms, "algorithmic_flop": fl,
-                                     "kernels": "H transposed once; per 8192-column chunk: lce_tile (dZ epilogue, "
-                                                "and the W chunk transposed from its LDS stages), one lce_tile "
+                                     "kernels": "H transposed once; the whole vocabulary as one chunk: lce_tile "
+                                                "(dZ epilogue, and W transposed from its LDS stages), one lce_tile "
                                                 "launch of both products (one lce_backward call)",
-                                     "traffic_note": "FETCH_SIZE + WRITE_SIZE over the call's 39 launches; writes "
-                                                     "11.4 GB (two dZ copies and the W chunk transposed, dH "
-                                                     "written per chunk, dW, H transposed)"}
-        cfg["lce_backward"] = {"N": LCE_N, "D": LCE_D, "V": LCE_V, "out": "fp32 dH, dW", "timed": "apart"}
+                                     "traffic_note": "FETCH_SIZE + WRITE_SIZE over the call's launches; writes "
+                                                     "two dZ copies and W transposed, dH once, dW, H transposed"}
+        cfg["lce_backward"] = {"N": LCE_N, "D": LCE_D, "V": LCE_V, "out": "fp32 dH, dW", "timed": "apart",
+                               "workspace": "one chunk over the whole vocabulary"}
     for key, tms, (fb, vb), names, cfgv in (
             ("kl_fwd_vjp", kl_ms, kl_bytes(KL_ROWS, KL_V, 4), ("kl_forward", "kl_vjp"),
              {"rows": KL_ROWS, "V": KL_V, "dtype": "f32", "scale": 4.0, "timed": "apart"}),

@@ -30,7 +30,8 @@ CE_NO_IGNORE = -(2 ** 31)
 
 # every symbol include/ce_mi355x.h declares
 EXPORTS = ("ce_forward", "ce_vjp", "ce_forward_vjp", "lce_workspace_size",
-           "lce_forward", "lce_backward_workspace_size", "lce_backward", "kl_forward",
+           "lce_forward", "lce_backward_workspace_size", "lce_backward_workspace_size_one_pass", "lce_backward",
+           "kl_forward",
            "kl_vjp", "js_forward", "js_vjp",
            "ce_reduce_workspace_size", "ce_forward_ex", "ce_forward_ex_noalloc", "ce_vjp_ex", "ce_forward_probs",
            "ce_vjp_probs", "ce_status_string")
@@ -85,6 +86,8 @@ def lib() -> ctypes.CDLL:
         L.lce_forward.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _sz, _vp]
         L.lce_backward_workspace_size.argtypes = [_i64, _i64, _i64]
         L.lce_backward_workspace_size.restype = _sz
+        L.lce_backward_workspace_size_one_pass.argtypes = [_i64, _i64, _i64]
+        L.lce_backward_workspace_size_one_pass.restype = _sz
         L.lce_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _sz, _vp]
         L.kl_forward.argtypes = [_vp, CELayout, _vp, CELayout, ctypes.c_int, _i64, _i64, _vp, _vp, _vp, _vp]
         L.kl_forward_lanes.argtypes = [_vp, CELayout, _vp, CELayout, ctypes.c_int, _i64, _i64, _vp, _vp, _vp,
@@ -446,9 +449,15 @@ def lce_backward_workspace_size(N: int, D: int, V: int) -> int:
     return int(lib().lce_backward_workspace_size(N, D, V))
 
 
+def lce_backward_workspace_size_one_pass(N: int, D: int, V: int) -> int:
+    return int(lib().lce_backward_workspace_size_one_pass(N, D, V))
+
+
 def lce_backward(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: torch.Tensor, g: torch.Tensor,
-                 dH=None, dW=None, workspace=None):
-    """(dH [N, D], dW [V, D]) float32 of sum_i g_i loss_i, from lce_forward's lse [N, 2]."""
+                 dH=None, dW=None, workspace=None, one_pass: bool = False):
+    """(dH [N, D], dW [V, D]) float32 of sum_i g_i loss_i, from lce_forward's lse [N, 2].
+    Without a workspace, one of lce_backward_workspace_size bytes is allocated (chunks of
+    8192 columns), or of lce_backward_workspace_size_one_pass bytes with one_pass."""
     if H.dtype != torch.bfloat16 or W.dtype != torch.bfloat16 or H.dim() != 2 or W.dim() != 2:
         raise ValueError("H and W must be 2-D bfloat16 tensors")
     if not H.is_contiguous() or not W.is_contiguous() or H.shape[1] != W.shape[1]:
@@ -463,7 +472,7 @@ def lce_backward(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: t
         dH = torch.empty(N, D, dtype=torch.float32, device=H.device)
     if dW is None:
         dW = torch.empty(V, D, dtype=torch.float32, device=H.device)
-    need = lce_backward_workspace_size(N, D, V)
+    need = (lce_backward_workspace_size_one_pass if one_pass else lce_backward_workspace_size)(N, D, V)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=H.device)
     st = lib().lce_backward(_ptr(H), _ptr(W), _ptr(targets), _ptr(lse), _ptr(g), N, D, V, _ptr(dH), _ptr(dW),

@@ -588,6 +588,11 @@ size_t lce_backward_workspace_size(int64_t N, int64_t D, int64_t V) {
     return ce::lce_backward_workspace_bytes(N, D, V);
 }
 
+size_t lce_backward_workspace_size_one_pass(int64_t N, int64_t D, int64_t V) {
+    if (N < 0 || N > kMaxBackwardN || D < 1 || D % 8 != 0 || V < 1 || V > kMaxV || D > (int64_t)1 << 22) return 0;
+    return ce::lce_backward_workspace_bytes_one_pass(N, D, V);
+}
+
 ce_status lce_backward(const void* H, const void* W, const int32_t* targets, const float* lse, const float* g,
                        int64_t N, int64_t D, int64_t V, float* dH, float* dW, void* workspace,
                        size_t workspace_bytes, hipStream_t stream) {
@@ -606,7 +611,7 @@ ce_status lce_backward(const void* H, const void* W, const int32_t* targets, con
     if (overlaps(ex_dW, ex_W)) return CE_ERR_ALIAS;
     if (N > 0) {
         const Extent ex_dH = flat_extent(dH, N * D * 4);
-        const Extent ex_ws = flat_extent(workspace, (int64_t)need);
+        const Extent ex_ws = flat_extent(workspace, (int64_t)ce::lce_backward_workspace_used(N, D, V, workspace_bytes));
         const Extent ins[5] = {flat_extent(H, N * D * 2), ex_W, flat_extent(targets, N * 4),
                                flat_extent(lse, N * 8), flat_extent(g, N * 4)};
         for (const Extent& e : ins)
@@ -616,7 +621,7 @@ ce_status lce_backward(const void* H, const void* W, const int32_t* targets, con
     int cus = 0;
     if (ce_status s = device_cus(&cus)) return s;
     if (N == 0) return from_hip(ce::launch_fill_zero_f32(dW, V * D, stream));
-    ce::LceBackwardCall c{H, W, targets, lse, g, N, D, V, dH, dW, workspace, stream};
+    ce::LceBackwardCall c{H, W, targets, lse, g, N, D, V, dH, dW, workspace, workspace_bytes, stream};
     return ce::run_lce_backward(c) == ce::LceBackwardStatus::kOk ? CE_OK : CE_ERR_LAUNCH;
 }
 

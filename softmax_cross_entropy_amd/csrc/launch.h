@@ -291,12 +291,18 @@ struct LceBackwardCall {
     float* dH;
     float* dW;
     void* workspace;
+    size_t workspace_bytes;  // at least lce_backward_workspace_bytes; with
+                             // lce_backward_workspace_bytes_one_pass or more, one chunk
     hipStream_t stream;
 };
 
 enum class LceBackwardStatus { kOk, kHip };
 
+// Workspace of chunks of 8192 vocabulary columns (the least a call needs), of one chunk
+// over the whole vocabulary, and the part of `workspace_bytes` a call uses.
 size_t lce_backward_workspace_bytes(int64_t N, int64_t D, int64_t V);
+size_t lce_backward_workspace_bytes_one_pass(int64_t N, int64_t D, int64_t V);
+size_t lce_backward_workspace_used(int64_t N, int64_t D, int64_t V, size_t workspace_bytes);
 LceBackwardStatus run_lce_backward(const LceBackwardCall& c);
 
 }  // namespace ce

@@ -3,37 +3,41 @@
 //
 // Ineshin, "A fused linear cross-entropy forward kernel for Apple GPUs", section 1:
 // training saves the forward's log-sum-exp and a chunked backward regenerates the
-// logits it needs tile by tile.  Here each chunk of 8192 vocabulary columns (the
-// page's dispatch tile) is one launch of the MFMA tile kernel whose epilogue turns the
-// regenerated logits straight into dZ (bf16, from the saved (m, log s) pair), written
-// both row-major and transposed, followed by two products on the same MFMA K loop,
-// accumulated in fp32:
+// logits it needs tile by tile.  Here each chunk of vocabulary columns is one launch of
+// the MFMA tile kernel whose epilogue turns the regenerated logits straight into dZ
+// (bf16, from the saved (m, log s) pair), written both row-major and transposed,
+// followed by two products on the same MFMA K loop, accumulated in fp32:
 //   dH        += dZ_c  W_c       (N x D, every chunk adds its share)
 //   dW[c0:c1]  = dZ_c^T H        (the chunk's own rows of dW)
 // The K loop reads both operands K-contiguous, so W_c and H enter these products
 // transposed: H^T once per call (lce_transpose), W_c^T by the dZ tiles themselves from
 // the W rows they stage through LDS.  K is padded to a multiple of 8 with zeros in both
-// operands.  Everything runs on the caller's stream
-// in the caller's workspace; nothing is allocated and no state is kept between calls.
+// operands.
+//
+// Two chunk widths, chosen by the workspace the caller passes: 8192 columns (the page's
+// tile; the workspace holds one chunk's dZ, about 2 x 128 MiB at N = 8192), or the
+// whole vocabulary as one chunk when the workspace holds all of dZ (about 5.9 GiB at
+// N = 8192, V = 151,936).  One chunk writes dH once instead of reading and rewriting it
+// per chunk, and launches each product once; its results are the same bit for bit,
+// since a chunk's tiles start from the float32 dH the previous chunk stored and the
+// float32 additions run in the same order.  Everything runs on the caller's stream in
+// the caller's workspace; nothing is allocated and no state is kept between calls.
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 
 #include "launch.h"
 
 namespace ce {
 namespace {
 
-#ifndef LCE_BWD_MAX_CHUNK
-#define LCE_BWD_MAX_CHUNK 8192
-#endif
-constexpr int64_t kMaxChunk = LCE_BWD_MAX_CHUNK;  // vocabulary columns per chunk, at most
+constexpr int64_t kChunkCols = 8192;  // the page's tile: vocabulary columns per chunk
+// One chunk over the whole vocabulary reads dZ and W^T rows of 2 * round256(V) bytes
+// through a buffer descriptor of 256 such rows and 32-bit offsets: V at most 2^22.
+constexpr int64_t kMaxOnePassV = (int64_t)1 << 22;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 int64_t round8(int64_t x) { return (x + 7) & ~(int64_t)7; }
-
-int64_t chunk_cols(int64_t V) {
-    const int64_t v256 = (V + 255) & ~(int64_t)255;
-    return v256 < kMaxChunk ? v256 : kMaxChunk;
-}
+int64_t round256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
 struct Layout {
     int64_t chunk;
@@ -41,24 +45,47 @@ struct Layout {
 };
 
 // dZ chunk [N][chunk]; its transpose [chunk][N8]; H^T [D][N8]; W_c^T [D][chunk].
-Layout layout(int64_t N, int64_t D, int64_t V) {
+Layout layout(int64_t N, int64_t D, int64_t chunk) {
     const int64_t n8 = round8(N);
     Layout l;
-    l.chunk = chunk_cols(V);
+    l.chunk = chunk;
     l.g = 0;
-    l.gt = l.g + align256((size_t)N * l.chunk * 2);
-    l.ht = l.gt + align256((size_t)l.chunk * n8 * 2);
+    l.gt = l.g + align256((size_t)N * chunk * 2);
+    l.ht = l.gt + align256((size_t)chunk * n8 * 2);
     l.wt = l.ht + align256((size_t)D * n8 * 2);
-    l.total = l.wt + align256((size_t)D * l.chunk * 2);
+    l.total = l.wt + align256((size_t)D * chunk * 2);
     return l;
+}
+
+Layout chunked(int64_t N, int64_t D, int64_t V) {
+    const int64_t v256 = round256(V);
+    return layout(N, D, v256 < kChunkCols ? v256 : kChunkCols);
+}
+
+// The layout a call with `bytes` of workspace runs: the whole vocabulary as one chunk
+// when the workspace holds it, else chunks of 8192 columns.
+Layout pick(int64_t N, int64_t D, int64_t V, size_t bytes) {
+    if (V <= kMaxOnePassV) {
+        const Layout one = layout(N, D, round256(V));
+        if (bytes >= one.total) return one;
+    }
+    return chunked(N, D, V);
 }
 
 }  // namespace
 
-size_t lce_backward_workspace_bytes(int64_t N, int64_t D, int64_t V) { return layout(N, D, V).total; }
+size_t lce_backward_workspace_bytes(int64_t N, int64_t D, int64_t V) { return chunked(N, D, V).total; }
+
+size_t lce_backward_workspace_bytes_one_pass(int64_t N, int64_t D, int64_t V) {
+    return pick(N, D, V, SIZE_MAX).total;
+}
+
+size_t lce_backward_workspace_used(int64_t N, int64_t D, int64_t V, size_t workspace_bytes) {
+    return pick(N, D, V, workspace_bytes).total;
+}
 
 LceBackwardStatus run_lce_backward(const LceBackwardCall& c) {
-    const Layout l = layout(c.N, c.D, c.V);
+    const Layout l = pick(c.N, c.D, c.V, c.workspace_bytes);
     const int64_t kChunk = l.chunk;
     char* ws = static_cast<char*>(c.workspace);
     void* G = ws + l.g;
@@ -77,8 +104,8 @@ LceBackwardStatus run_lce_backward(const LceBackwardCall& c) {
         // dZ_c in both layouts, and W_c^T [D][w8] (zero past w) written by the same tiles
         LceGradChunk gc{c.H, c.W, c.targets, c.lse, c.g, c.N, c.D, c.V, c0, w, G, kChunk, GT, n8, WT, kChunk, c.stream};
         if (!ok(launch_lce_grad_chunk(gc))) return LceBackwardStatus::kHip;
-        // dZ_c's columns w .. w8 - 1 (stale from an earlier chunk) zeroed, so the padded K
-        // adds nothing
+        // dZ_c's columns w .. w8 - 1 (stale from an earlier chunk, or never written) zeroed,
+        // so the padded K adds nothing
         if (w8 > w && !ok(launch_zero_cols_bf16(G, c.N, kChunk, w, w8, c.stream))) return LceBackwardStatus::kHip;
         // dH [N][D] (+)= dZ_c [N][w8] . (W_c^T [D][w8])^T, and
         // dW[c0 : c0 + w] [w][D] = dZ_c^T [w][N8] . (H^T [D][N8])^T, in one launch

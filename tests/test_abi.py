@@ -2,7 +2,8 @@
 rejects invalid arguments on the host with the documented status before any launch.
 
 Pointers below are fake addresses that are never dereferenced: every call here fails
-validation first.
+validation first, or, with valid arguments, the device lookup (no GPU is visible where
+this module runs).
 """
 
 import ctypes
@@ -10,6 +11,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from softmax_cross_entropy_amd import abi
 
@@ -19,7 +21,11 @@ TESTING_HEADER = os.path.join(ROOT, "include", "ce_mi355x_testing.h")
 
 OK, NULL, SHAPE, DTYPE, LAYOUT, WORKSPACE, LAUNCH, ALIAS, DEVICE, OPTION = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 
-pytestmark = pytest.mark.skipif(not os.path.exists(abi.LIB_PATH), reason="library not built")
+# The pointers are fake device addresses, so a call that passes validation must not reach a
+# GPU: the module runs only where none is visible, and such calls stop at the device lookup
+# with CE_ERR_DEVICE.
+pytestmark = [pytest.mark.skipif(not os.path.exists(abi.LIB_PATH), reason="library not built"),
+              pytest.mark.skipif(torch.cuda.device_count() > 0, reason="fake device addresses: host only")]
 
 
 def declared_functions(path=HEADER):
@@ -221,10 +227,35 @@ def test_lce_backward_rejects_bad_arguments():
     assert lbw(dW=ctypes.c_void_p(5 * A)) == ALIAS          # dW over g
 
 
+def test_lce_backward_one_pass_workspace():
+    """The workspace of one chunk over the whole vocabulary, and the call's overlap check
+    against the part of the workspace it uses."""
+    a256 = lambda x: (x + 255) // 256 * 256
+    size = lambda C, N=32, D=8, n8=32: a256(N * C * 2) + a256(C * n8 * 2) + a256(D * n8 * 2) + a256(D * C * 2)
+    N, D, V = 32, 8, 9000
+    chunked, one = abi.lce_backward_workspace_size(N, D, V), abi.lce_backward_workspace_size_one_pass(N, D, V)
+    assert chunked == size(8192) and one == size(9216)   # 9000 columns rounded up to 256
+    assert abi.lce_backward_workspace_size_one_pass(33, 64, 20000) == (a256(33 * 20224 * 2) + a256(20224 * 40 * 2) +
+                                                                       a256(64 * 40 * 2) + a256(64 * 20224 * 2))
+    # a vocabulary of one chunk already, or above 2^22 columns: the chunked size
+    assert abi.lce_backward_workspace_size_one_pass(32, 64, 1000) == abi.lce_backward_workspace_size(32, 64, 1000)
+    big = (1 << 22) + 1
+    assert abi.lce_backward_workspace_size_one_pass(32, 64, big) == abi.lce_backward_workspace_size(32, 64, big)
+    assert abi.lce_backward_workspace_size_one_pass(32, 64, 1 << 22) > abi.lce_backward_workspace_size(32, 64, 1 << 22)
+    assert abi.lce_backward_workspace_size_one_pass(32, 60, 1000) == 0
+    assert abi.lce_backward_workspace_size_one_pass((1 << 22) + 1, 64, 1000) == 0
+    # dH just past the chunked layout but inside the one-chunk layout: an overlap only when
+    # the workspace is large enough for one chunk
+    dH = ctypes.c_void_p(8 * A + chunked + 256)
+    assert lbw(N=N, D=D, V=V, dH=dH, wsb=chunked) == DEVICE
+    assert lbw(N=N, D=D, V=V, dH=dH, wsb=one) == ALIAS
+    assert lbw(N=N, D=D, V=V, dH=dH, wsb=one - 1) == DEVICE
+
+
 def test_lce_backward_empty_batch_needs_only_w_and_dw():
     """N == 0 still writes dW (= 0); H, targets, lse, g, dH and the workspace may be NULL."""
     st = lbw(H=None, t=None, lse=None, g=None, dH=None, ws=None, N=0, wsb=0)
-    assert st in (OK, DEVICE)
+    assert st == DEVICE
     assert lbw(N=0, dW=None) == NULL
 
 
@@ -257,7 +288,7 @@ def test_kl_rejects_bad_arguments():
     assert klv(dq=ctypes.c_void_p(300 * A)) == ALIAS  # dq over p
     assert klv(dq=ctypes.c_void_p(A + 64)) == ALIAS  # dq overlapping q, not in place
     assert klv(dq=ctypes.c_void_p(5 * A)) == ALIAS  # dq over g
-    assert klv(dq=P_LOGITS) in (OK, DEVICE)  # in place, identical layout
+    assert klv(dq=P_LOGITS) == DEVICE  # in place, identical layout
 
 
 P_HQ = ctypes.c_void_p(A * 350)
@@ -282,7 +313,7 @@ def test_js_rejects_bad_arguments():
     assert jsf(hq=ctypes.c_void_p(350 * A + 2)) == LAYOUT
     assert jsf(hq=P_KL) == ALIAS and jsf(hq=P_P) == ALIAS
     assert jsv(dq=P_HQ) == ALIAS and jsv(dq=P_P) == ALIAS
-    assert jsv(dq=P_LOGITS) in (OK, DEVICE)
+    assert jsv(dq=P_LOGITS) == DEVICE
 
 
 P_TOT, P_CNT, P_RWS, P_PR, P_WSUM, P_GR = (ctypes.c_void_p(A * k) for k in (400, 401, 402, 410, 420, 421))
@@ -328,19 +359,19 @@ def test_options_reject_bad_arguments():
     assert fex(tot=None) == NULL and fex(cnt=None) == NULL and fex(ws=None) == NULL
     assert fex(wsb=WSB - 1) == WORKSPACE
     assert fex(cnt=ctypes.c_void_p(400 * A + 4)) == LAYOUT
-    assert fex(o=opts(red="none"), tot=None, cnt=None, ws=None, wsb=0) in (OK, DEVICE)
+    assert fex(o=opts(red="none"), tot=None, cnt=None, ws=None, wsb=0) == DEVICE
     for name in ("logits", "t", "loss", "lse"):
         assert fex(**{name: None}) == NULL, name
     assert fpr(pr=None) == NULL and fpr(ws_=None) == NULL
-    assert vex(cnt=None) == NULL and vex(o=opts(red="sum"), cnt=None) in (OK, DEVICE)
+    assert vex(cnt=None) == NULL and vex(o=opts(red="sum"), cnt=None) == DEVICE
     assert vpr(ws_=None) == NULL and vpr(pr=None) == NULL
     # aliasing among the outputs and with the inputs
     assert fex(tot=P_LOSS) == ALIAS and fex(ws=ctypes.c_void_p(A + 8)) == ALIAS and fex(cnt=P_RWS) == ALIAS
     assert fpr(ws_=P_PR) == ALIAS and fpr(loss=P_WSUM) == ALIAS
     assert vex(d=P_GR) == ALIAS and vex(d=P_CNT) == ALIAS and vpr(d=P_PR) == ALIAS and vpr(d=P_WSUM) == ALIAS
-    assert vex(d=P_LOGITS) in (OK, DEVICE)  # in place
+    assert vex(d=P_LOGITS) == DEVICE  # in place
     # an empty batch with a reduction still writes total and count; without one it is a no-op
-    assert fex(n=0, logits=None, t=None, loss=None, lse=None) in (OK, DEVICE)
+    assert fex(n=0, logits=None, t=None, loss=None, lse=None) == DEVICE
     assert fex(n=0, tot=P_RWS) == ALIAS
     assert fex(n=0, logits=None, o=opts(red="none"), tot=None, cnt=None, ws=None) == OK
     assert vex(n=0, logits=None, d=None) == OK and vpr(n=0, pr=None, d=None) == OK

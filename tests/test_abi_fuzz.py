@@ -13,11 +13,16 @@ import ctypes
 import os
 
 import pytest
+import torch
 from hypothesis import given, settings, strategies as st
 
 from softmax_cross_entropy_amd import abi
 
-pytestmark = pytest.mark.skipif(not os.path.exists(abi.LIB_PATH), reason="library not built")
+# The pointers are fake device addresses, so a call that passes validation must not reach a
+# GPU: the module runs only where none is visible, and such calls stop at the device lookup
+# with CE_ERR_DEVICE.
+pytestmark = [pytest.mark.skipif(not os.path.exists(abi.LIB_PATH), reason="library not built"),
+              pytest.mark.skipif(torch.cuda.device_count() > 0, reason="fake device addresses: host only")]
 
 OK, LAYOUT, ALIAS, DEVICE = 0, -4, -7, -8
 ES = 4  # fp32
@@ -67,8 +72,8 @@ def test_dlogits_overlapping_the_logits_is_refused(n, V, shift_elems):
     b_lo, b_hi = out, out + n * V * ES
     overlap = a_lo < b_hi and b_lo < a_hi
     if shift_elems == 0:
-        assert st_ in (OK, DEVICE), st_           # in place, same layout
+        assert st_ == DEVICE, st_           # in place, same layout
     elif overlap:
         assert st_ in (ALIAS, LAYOUT), (st_, shift_elems)
     else:
-        assert st_ in (OK, DEVICE), (st_, shift_elems)
+        assert st_ == DEVICE, (st_, shift_elems)

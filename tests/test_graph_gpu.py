@@ -1,9 +1,9 @@
 """GPU: a step of the library's calls captured in a HIP graph replays to the eager bits.
 
 The kernels allocate nothing and issue no memset, so a caller can capture them.  One step
-(cross-entropy forward and VJP, lce_forward and lce_backward, KL and Jensen-Shannon forward
-and VJP, the options with a mean through both the workspace and the allocation-free
-forward) is captured through torch.cuda.CUDAGraph after a warm-up, then replayed several
+(cross-entropy forward and VJP, lce_forward and lce_backward in both chunk layouts, KL and
+Jensen-Shannon forward and VJP, the options with a mean through both the workspace and the
+allocation-free forward) is captured through torch.cuda.CUDAGraph after a warm-up, then replayed several
 times; before each replay the graph's outputs are cleared and the eager step runs again,
 and every replay must match the eager results bit for bit.
 """
@@ -33,6 +33,11 @@ def test_captured_step_replays_match_eager():
     q, p = to_dev(q_np, "f32"), to_dev(p_np, "f32")
     gk = torch.from_numpy(np.linspace(1.0, 2.0, 48).astype(np.float32)).cuda()
     gl = torch.from_numpy(np.linspace(0.25, 2.0, 256).astype(np.float32)).cuda()
+    # lce_backward in one chunk over a vocabulary wider than the 8192-column chunk
+    h2, w2, y2 = inputs.linear_ce(64, 64, 9000, seed_stream=4)
+    H2, W2, Y2 = to_dev(h2, "bf16"), to_dev(w2, "bf16"), torch.from_numpy(y2).cuda()
+    _, lse2 = abi.lce_forward(H2, W2, Y2)
+    g2 = torch.from_numpy(np.linspace(0.5, 1.5, 64).astype(np.float32)).cuda()
     na_loss = torch.empty(128, device="cuda")
     na_lse = torch.empty(128, 2, device="cuda")
     na_tot = torch.empty(1, device="cuda")
@@ -47,10 +52,12 @@ def test_captured_step_replays_match_eager():
         l2, s2, tot, cnt = abi.ce_forward_ex(x, ti, 0.1, -100, "mean")
         d2 = abi.ce_vjp_ex(x, ti, s2, g1, 0.1, -100, "mean", count=cnt)
         dH, dW = abi.lce_backward(H, W, Y, llse, gl)
+        dH2, dW2 = abi.lce_backward(H2, W2, Y2, lse2, g2, one_pass=True)
         js, jq, jp, jh = abi.js_forward(q, p)
         jd = abi.js_vjp(q, p, jq, jp, jh, gk)
         abi.ce_forward_ex_noalloc(x, ti, 0.5, -100, "sum", na_loss, na_lse, na_tot, na_cnt)
-        return [loss, lse, d, ll, llse, kl, dq, l2, tot, cnt, d2, dH, dW, js, jd, na_loss, na_lse, na_tot, na_cnt]
+        return [loss, lse, d, ll, llse, kl, dq, l2, tot, cnt, d2, dH, dW, dH2, dW2, js, jd, na_loss, na_lse, na_tot,
+                na_cnt]
 
     eager = [o.clone() for o in step()]
     torch.cuda.synchronize()

@@ -27,11 +27,11 @@ def dev_bf16(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def gpu_backward(H, W, y, g):
+def gpu_backward(H, W, y, g, one_pass=False):
     Hd, Wd = dev_bf16(H), dev_bf16(W)
     yd = torch.from_numpy(np.ascontiguousarray(y, np.int32)).cuda()
     _, lse = abi.lce_forward(Hd, Wd, yd)
-    dH, dW = abi.lce_backward(Hd, Wd, yd, lse, torch.from_numpy(np.asarray(g, np.float32)).cuda())
+    dH, dW = abi.lce_backward(Hd, Wd, yd, lse, torch.from_numpy(np.asarray(g, np.float32)).cuda(), one_pass=one_pass)
     torch.cuda.synchronize()
     return dH.cpu().numpy().astype(np.float64), dW.cpu().numpy().astype(np.float64)
 
@@ -135,8 +135,25 @@ def test_full_vocab_and_width_one_row_tile():
     within(dW[cols], rW, np.abs(dZc).T @ np.abs(H64), "dW columns")
 
 
+@pytest.mark.parametrize("N,D,V", [(100, 64, 20000), (513, 128, 8193), (37, 40, 16385), (300, 72, 24577)])
+def test_one_pass_matches_chunks(N, D, V):
+    """A workspace of lce_backward_workspace_size_one_pass bytes runs the whole vocabulary
+    as one chunk: dH written once, one launch of each product.  Its dH and dW equal the
+    chunked call's bit for bit, and the oracle's within the bound."""
+    H, W, y = inputs.linear_ce(N, D, V, seed_stream=N * 7 + D + V)
+    g = upstream(N, N + 2 * V)
+    assert abi.lce_backward_workspace_size_one_pass(N, D, V) > abi.lce_backward_workspace_size(N, D, V)
+    cH, cW = gpu_backward(H, W, y, g)
+    oH, oW = gpu_backward(H, W, y, g, one_pass=True)
+    assert np.array_equal(cH, oH) and np.array_equal(cW, oW)
+    rH, rW, bH, bW = olce.grad(H, W, y, g, bounds=True)
+    within(oH, rH, bH, "dH")
+    within(oW, rW, bW, "dW")
+
+
 def test_bench_size_sampled_rows_columns_and_column_sum(full_lce):
     """N = 8192, D = 4096, V = 151,936 as bench.py runs it:
+    * the call in chunks of 8192 columns and in one chunk (bench.py's layout), bit for bit;
     * dH on 64 sampled rows against the oracle, entry by entry;
     * dW on 72 sampled vocabulary rows against the oracle, entry by entry: the first and
       last columns of every 8192-column chunk boundary they touch, targets, and 24
@@ -150,8 +167,14 @@ def test_bench_size_sampled_rows_columns_and_column_sum(full_lce):
     Hd, Wd = dev_bf16(H), dev_bf16(W)
     yd = torch.from_numpy(np.ascontiguousarray(y, np.int32)).cuda()
     _, lse = abi.lce_forward(Hd, Wd, yd)
-    dHd, dWd = abi.lce_backward(Hd, Wd, yd, lse, torch.from_numpy(g.astype(np.float32)).cuda())
+    gd = torch.from_numpy(g.astype(np.float32)).cuda()
+    dHd, dWd = abi.lce_backward(Hd, Wd, yd, lse, gd)
+    # one chunk over the whole vocabulary (the layout bench.py times) gives the same bits
+    oH, oW = abi.lce_backward(Hd, Wd, yd, lse, gd, one_pass=True)
     torch.cuda.synchronize()
+    assert torch.equal(oH.view(torch.int32), dHd.view(torch.int32))
+    assert torch.equal(oW.view(torch.int32), dWd.view(torch.int32))
+    del oH, oW
     dH = dHd.cpu().numpy().astype(np.float64)
     assert np.isfinite(dH).all() and torch.isfinite(dWd).all().item()
     rng = np.random.default_rng(1)
