@@ -50,103 +50,103 @@ CSRC = os.path.join(ROOT, "softmax_cross_entropy_amd", "csrc")
 TRAFFIC = {
     "ce_forward_vjp": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 1290949953
+        "bytes": 1290974879
     },
     "ce_forward": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 622592051
+        "bytes": 622592558
     },
     "ce_vjp": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 1244996369
+        "bytes": 1244996898
     },
     "lce_forward": {
         "source_sha": "f933e14941467e33",
-        "bytes": 15159317237
+        "bytes": 15162830132
     },
     "kl_forward": {
         "source_sha": "8178fcf06dbd3aed",
-        "bytes": 622484945
+        "bytes": 622485321
     },
     "kl_vjp": {
         "source_sha": "8178fcf06dbd3aed",
-        "bytes": 933637420
+        "bytes": 933637939
     },
     "ce_forward_ex": {
         "source_sha": "9c57c5ac9d01527f",
-        "bytes": 622630759
+        "bytes": 622631175
     },
     "ce_vjp_ex": {
         "source_sha": "9c57c5ac9d01527f",
-        "bytes": 1206070147
+        "bytes": 1206070618
     },
     "ce_forward_probs": {
         "source_sha": "9c57c5ac9d01527f",
-        "bytes": 622466014
+        "bytes": 622466637
     },
     "ce_vjp_probs": {
         "source_sha": "9c57c5ac9d01527f",
-        "bytes": 933601325
+        "bytes": 933601845
     },
     "js_forward": {
         "source_sha": "f78dc0c5b2112634",
-        "bytes": 1224837065
+        "bytes": 1224823487
     },
     "js_vjp": {
         "source_sha": "f78dc0c5b2112634",
-        "bytes": 936688206
+        "bytes": 936623402
     },
     "lce_backward": {
-        "source_sha": "f933e14941467e33",
-        "bytes": 58958544838
+        "source_sha": "699e198a7e1f149d",
+        "bytes": 61143499835
     },
     "ce_forward f32 [1048576 x 8]": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 50514266
+        "bytes": 50484930
     },
     "ce_vjp f32 [1048576 x 8]": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 83946277
+        "bytes": 83946291
     },
     "ce_forward f32 [65536 x 1024] offsets and -inf rows": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 270324543
+        "bytes": 270328891
     },
     "ce_vjp f32 [65536 x 1024] offsets and -inf rows": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 540184772
+        "bytes": 540187535
     },
     "ce_forward f16 [65536 x 1024] offsets and -inf rows": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 135597030
+        "bytes": 135597114
     },
     "ce_vjp f16 [65536 x 1024] offsets and -inf rows": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 270105646
+        "bytes": 270105742
     },
     "ce_forward f32 view [10, 119, 32768][:, :-1] (1180 rows)": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 154859895
+        "bytes": 154859683
     },
     "ce_vjp f32 view [10, 119, 32768][:, :-1] (1180 rows)": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 309565595
+        "bytes": 309565384
     },
     "ce_forward bf16 [8192 x 32000]": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 525188798
+        "bytes": 525190380
     },
     "ce_vjp bf16 [8192 x 32000]": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 1049704907
+        "bytes": 1049705173
     },
     "ce_forward f32 [135266304 x 8]": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 6600453393
+        "bytes": 6599689798
     },
     "ce_vjp f32 [135266304 x 8]": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 10826872504
+        "bytes": 10826846859
     }
 }
 
