@@ -152,8 +152,13 @@ ce_status make_plan(bool narrow_ok, int64_t V, int es, int64_t n_rows, int32_t l
         per_block = threads / p.lanes;
     }
     const int64_t needed = (n_rows + per_block - 1) / per_block;
+    // 256-thread plans (one lane per row, or up to 256 lanes per row) launch one workgroup
+    // per block of rows, up to 2^30 of them.  At fp32 [135,266,304 x 8] that ran the
+    // forward 11% and the VJP 19% faster than four rounds of resident workgroups looping
+    // over the rows; the other measured shapes stayed within 1%.  Wider workgroups keep
+    // four rounds.
     const int64_t resident = (int64_t)cus * (2048 / threads);
-    const int64_t cap = resident * 4;
+    const int64_t cap = threads == 256 ? (int64_t)1 << 30 : resident * 4;
     p.blocks = needed < cap ? needed : cap;
     if (p.blocks < 1) p.blocks = 1;
     *plan = p;
