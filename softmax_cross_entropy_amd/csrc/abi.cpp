@@ -152,13 +152,16 @@ ce_status make_plan(bool narrow_ok, int64_t V, int es, int64_t n_rows, int32_t l
         per_block = threads / p.lanes;
     }
     const int64_t needed = (n_rows + per_block - 1) / per_block;
-    // 256-thread plans (one lane per row, or up to 256 lanes per row) launch one workgroup
-    // per block of rows, up to 2^30 of them.  At fp32 [135,266,304 x 8] that ran the
-    // forward 11% and the VJP 19% faster than four rounds of resident workgroups looping
-    // over the rows; the other measured shapes stayed within 1%.  Wider workgroups keep
-    // four rounds.
+    // 256-thread plans whose workgroups move at least 8 KB per pass (one lane per row, one
+    // or two lanes per row, or two or more vectors per lane) launch one workgroup per block
+    // of rows, up to 2^30 of them, instead of four rounds of resident workgroups looping
+    // over the rows.  Measured on 512 MiB batches: fp32 [135,266,304 x 8] forward 11% and
+    // VJP 19% faster, the 4- and 8-class rows 6-13%, rows of 2+ vectors per lane about 4%;
+    // rows of one vector per lane over 4 or 8 lanes ran 6-10% slower that way (each
+    // workgroup then moves only 4 KB), so they, and wider workgroups, keep four rounds.
     const int64_t resident = (int64_t)cus * (2048 / threads);
-    const int64_t cap = threads == 256 ? (int64_t)1 << 30 : resident * 4;
+    const bool open_grid = threads == 256 && (p.narrow_nv > 0 || p.lanes <= 2 || nvec >= 2 * p.lanes);
+    const int64_t cap = open_grid ? (int64_t)1 << 30 : resident * 4;
     p.blocks = needed < cap ? needed : cap;
     if (p.blocks < 1) p.blocks = 1;
     *plan = p;
