@@ -102,51 +102,51 @@ TRAFFIC = {
     },
     "ce_forward f32 [1048576 x 8]": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 50484930
+        "bytes": 50504821
     },
     "ce_vjp f32 [1048576 x 8]": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 83946291
+        "bytes": 83947084
     },
     "ce_forward f32 [65536 x 1024] offsets and -inf rows": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 270328891
+        "bytes": 270328956
     },
     "ce_vjp f32 [65536 x 1024] offsets and -inf rows": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 540187535
+        "bytes": 540164057
     },
     "ce_forward f16 [65536 x 1024] offsets and -inf rows": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 135597114
+        "bytes": 135597331
     },
     "ce_vjp f16 [65536 x 1024] offsets and -inf rows": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 270105742
+        "bytes": 270106831
     },
     "ce_forward f32 view [10, 119, 32768][:, :-1] (1180 rows)": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 154859683
+        "bytes": 154859484
     },
     "ce_vjp f32 view [10, 119, 32768][:, :-1] (1180 rows)": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 309565384
+        "bytes": 309565545
     },
     "ce_forward bf16 [8192 x 32000]": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 525190380
+        "bytes": 525190978
     },
     "ce_vjp bf16 [8192 x 32000]": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 1049705173
+        "bytes": 1049705504
     },
     "ce_forward f32 [135266304 x 8]": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 6599689798
+        "bytes": 6567347952
     },
     "ce_vjp f32 [135266304 x 8]": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 10826846859
+        "bytes": 10821186773
     }
 }
 
