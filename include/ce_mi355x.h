@@ -9,7 +9,8 @@
  *   lce_forward   per-row loss and log-sum-exp of H.W^T, streamed over vocabulary
  *                 tiles without materialising the N x V logits
  *   lce_backward  dH and dW of sum_i g_i loss_i for lce_forward's loss; the logits
- *                 are regenerated chunk by chunk, and the two products with the
+ *                 are regenerated chunk by chunk (8192 columns, or the whole vocabulary
+ *                 when the workspace holds it), and the two products with the
  *                 regenerated gradient chunk run on the same MFMA tile kernel
  *   kl_forward    per-row KL divergence of a teacher logits row from a student row
  *   kl_vjp        dq = g_i * (softmax(q_i) - softmax(p_i)) from the saved pairs
