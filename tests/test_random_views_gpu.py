@@ -1,5 +1,6 @@
-"""GPU: seeded random views against the float64 oracle: ce_forward and ce_vjp; kl_forward,
-kl_vjp, js_forward and js_vjp; the options calls with index and probability targets.
+"""GPU: seeded random views against the float64 oracle: ce_forward and ce_vjp, and
+ce_forward_vjp on the same views; kl_forward, kl_vjp, js_forward and js_vjp; the options
+calls with index and probability targets.
 
 Each case draws a dtype, a vocabulary size (log-uniform up to 70,000, so it lands in
 every layout: one lane per row, lanes per row, a workgroup per row, the chunked VJP),
@@ -57,6 +58,12 @@ def test_random_view(seed):
     check_loss(loss.cpu().numpy(), rl, dtype)
     check_lse(lse.cpu().numpy(), rm, rls, dtype)
     check_grad(from_dev(d).reshape(-1, V), rd, dtype, targets=y, g=gr)
+    # the same in one kernel: its dlogits equal ce_vjp's for the lse it writes
+    fl, fs, fd = abi.ce_forward_vjp(x, t, torch.from_numpy(gr).cuda())
+    torch.cuda.synchronize()
+    check_loss(fl.cpu().numpy(), rl, dtype, "ce_forward_vjp loss")
+    check_lse(fs.cpu().numpy(), rm, rls, dtype)
+    check_grad(from_dev(fd).reshape(-1, V), rd, dtype, "ce_forward_vjp dlogits", targets=y, g=gr)
     print(f"seed {seed}: {dtype} V={V} view {tuple(x.shape)} strides {tuple(x.stride())}")
 
 
