@@ -61,7 +61,7 @@ TRAFFIC = {
         "bytes": 1244996898
     },
     "lce_forward": {
-        "source_sha": "f933e14941467e33",
+        "source_sha": "8d869c11a4c94fa7",
         "bytes": 15162830132
     },
     "kl_forward": {
@@ -97,7 +97,7 @@ TRAFFIC = {
         "bytes": 936623402
     },
     "lce_backward": {
-        "source_sha": "699e198a7e1f149d",
+        "source_sha": "409a840e62f92f80",
         "bytes": 61143499835
     },
     "ce_forward f32 [1048576 x 8]": {

@@ -479,7 +479,6 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a0, TileArgs a1
         // acc[i][j][4q .. 4q + 3] are 4 consecutive columns of one row: 16-byte stores,
         // one row per lane, in a fixed order (an accumulating product started from C's
         // old values).
-        //
 #pragma unroll
         for (int i = 0; i < FB; ++i) {
             const int64_t row = wrow0 + i * 32 + l32;
