@@ -203,8 +203,10 @@ size_t lce_workspace_size(int64_t N, int64_t D, int64_t V);
  *            bytes, 256-byte aligned; its contents on entry are ignored.
  * The product accumulates in float32 on the matrix cores (bf16 in, fp32 out).  The
  * target logit is taken from the same float32 accumulator that feeds (m, s).
- * Requires D % 8 == 0 (16-byte rows), D <= 2^22 and V < 2^31; N may be any
- * non-negative size.
+ * Requires D % 8 == 0 (16-byte rows), D <= 2^22 and V < 2^31, and a tile grid that
+ * fits one dispatch: one 256-thread workgroup per 256 x 256 tile of N x V, in whole
+ * groups of 256 tiles, under 2^32 work-items (up to 2^24 tiles, about N V <= 2^40).
+ * Larger shapes return CE_ERR_SHAPE.
  */
 ce_status lce_forward(const void* H, const void* W, const int32_t* targets, int64_t N, int64_t D,
                       int64_t V, float* loss, float* lse, void* workspace, size_t workspace_bytes,
@@ -226,8 +228,9 @@ size_t lce_backward_workspace_size(int64_t N, int64_t D, int64_t V);
  * at N = 8192, D = 4096, V = 151,936).  One chunk writes dH once instead of reading and
  * rewriting it per chunk, which measured 3% faster at that shape, with identical
  * results.  For V > 2^22 (the one-chunk layout addresses rows of 2 C bytes with 32-bit
- * offsets) and for V <= 8192 it equals lce_backward_workspace_size.  Returns 0 for
- * arguments lce_backward would reject.
+ * offsets), for V <= 8192, and where the one-chunk grids would not fit one dispatch
+ * (N x V, or N x D and V x D together, past 2^24 tiles as in lce_forward) it equals
+ * lce_backward_workspace_size.  Returns 0 for arguments lce_backward would reject.
  * Source: the chunk width is a choice of the implementation; Ineshin (above), section 1,
  * fixes only that the backward regenerates the logits chunk by chunk.
  */
@@ -265,8 +268,9 @@ size_t lce_backward_workspace_size_one_pass(int64_t N, int64_t D, int64_t V);
  * A row whose target lies outside [0, V) has a NaN loss, so its dZ row is NaN: its
  * dH row and every entry of dW come out NaN.  dH and dW must not overlap the inputs,
  * the workspace or each other (CE_ERR_ALIAS).  Requirements on N, D, V as in
- * lce_forward, and N <= 2^22 (the product over the tokens addresses rows of 2 N bytes
- * with 32-bit offsets).
+ * lce_forward, N <= 2^22 (the product over the tokens addresses rows of 2 N bytes
+ * with 32-bit offsets), and the two products' tiles (N x D and 8192 x D, in groups of
+ * 256 as in lce_forward) together under 2^24; larger shapes return CE_ERR_SHAPE.
  */
 ce_status lce_backward(const void* H, const void* W, const int32_t* targets, const float* lse,
                        const float* g, int64_t N, int64_t D, int64_t V, float* dH, float* dW,

@@ -154,14 +154,16 @@ ce_status make_plan(bool narrow_ok, int64_t V, int es, int64_t n_rows, int32_t l
     const int64_t needed = (n_rows + per_block - 1) / per_block;
     // 256-thread plans whose workgroups move at least 8 KB per pass (one lane per row, one
     // or two lanes per row, or two or more vectors per lane) launch one workgroup per block
-    // of rows, up to 2^30 of them, instead of four rounds of resident workgroups looping
-    // over the rows.  Measured on 512 MiB batches: fp32 [135,266,304 x 8] forward 11% and
-    // VJP 19% faster, the 4- and 8-class rows 6-13%, rows of 2+ vectors per lane about 4%;
-    // rows of one vector per lane over 4 or 8 lanes ran 6-10% slower that way (each
-    // workgroup then moves only 4 KB), so they, and wider workgroups, keep four rounds.
+    // of rows, up to 2^31 work-items (the dispatch packet holds the grid size in work-items
+    // in 32 bits; the kernels loop over whatever rows remain), instead of four rounds of
+    // resident workgroups looping over the rows.  Measured on 512 MiB batches: fp32
+    // [135,266,304 x 8] forward 11% and VJP 19% faster, the 4- and 8-class rows 6-13%, rows
+    // of 2+ vectors per lane about 4%; rows of one vector per lane over 4 or 8 lanes ran
+    // 6-10% slower that way (each workgroup then moves only 4 KB), so they, and wider
+    // workgroups, keep four rounds.
     const int64_t resident = (int64_t)cus * (2048 / threads);
     const bool open_grid = threads == 256 && (p.narrow_nv > 0 || p.lanes <= 2 || nvec >= 2 * p.lanes);
-    const int64_t cap = open_grid ? (int64_t)1 << 30 : resident * 4;
+    const int64_t cap = open_grid ? ((int64_t)1 << 31) / threads : resident * 4;
     p.blocks = needed < cap ? needed : cap;
     if (p.blocks < 1) p.blocks = 1;
     *plan = p;
@@ -564,14 +566,19 @@ ce_status ce_forward_vjp_lanes(const void* logits, ce_layout in, ce_dtype dt, co
     return fused_impl(logits, in, dt, targets, g, n_rows, V, loss, lse, dlogits, out, lanes_per_row, stream);
 }
 
+// The tile kernels take one workgroup per 256 x 256 tile and a dispatch holds at most
+// 2^32 - 1 work-items: N x V (or N x D, V x D in the backward's products) is bounded.
+bool lce_grid_fits(int64_t N, int64_t V) { return ce::lce_tile_grid_items(N, V) <= ce::kMaxGridItems; }
+
 size_t lce_workspace_size(int64_t N, int64_t D, int64_t V) {
-    if (N < 0 || D < 1 || D % 8 != 0 || V < 1 || V > kMaxV) return 0;
+    if (N < 0 || D < 1 || D % 8 != 0 || V < 1 || V > kMaxV || !lce_grid_fits(N, V)) return 0;
     return ce::lce_workspace_bytes(N, D, V);
 }
 
 ce_status lce_forward(const void* H, const void* W, const int32_t* targets, int64_t N, int64_t D, int64_t V,
                       float* loss, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (N < 0 || D < 1 || D % 8 != 0 || V < 1 || V > kMaxV || D > (int64_t)1 << 22) return CE_ERR_SHAPE;
+    if (!lce_grid_fits(N, V)) return CE_ERR_SHAPE;
     if (N == 0) return CE_OK;
     if (!H || !W || !targets || !loss || !lse) return CE_ERR_NULL;
     if (!workspace || workspace_bytes < ce::lce_workspace_bytes(N, D, V)) return CE_ERR_WORKSPACE;
@@ -591,21 +598,25 @@ ce_status lce_forward(const void* H, const void* W, const int32_t* targets, int6
     return from_hip(ce::launch_lce_forward(c));
 }
 
+bool lce_backward_shape_ok(int64_t N, int64_t D, int64_t V) {
+    return N >= 0 && N <= kMaxBackwardN && D >= 1 && D % 8 == 0 && V >= 1 && V <= kMaxV && D <= (int64_t)1 << 22 &&
+           ce::lce_backward_grids_fit(N, D, V);
+}
+
 size_t lce_backward_workspace_size(int64_t N, int64_t D, int64_t V) {
-    if (N < 0 || N > kMaxBackwardN || D < 1 || D % 8 != 0 || V < 1 || V > kMaxV || D > (int64_t)1 << 22) return 0;
+    if (!lce_backward_shape_ok(N, D, V)) return 0;
     return ce::lce_backward_workspace_bytes(N, D, V);
 }
 
 size_t lce_backward_workspace_size_one_pass(int64_t N, int64_t D, int64_t V) {
-    if (N < 0 || N > kMaxBackwardN || D < 1 || D % 8 != 0 || V < 1 || V > kMaxV || D > (int64_t)1 << 22) return 0;
+    if (!lce_backward_shape_ok(N, D, V)) return 0;
     return ce::lce_backward_workspace_bytes_one_pass(N, D, V);
 }
 
 ce_status lce_backward(const void* H, const void* W, const int32_t* targets, const float* lse, const float* g,
                        int64_t N, int64_t D, int64_t V, float* dH, float* dW, void* workspace,
                        size_t workspace_bytes, hipStream_t stream) {
-    if (N < 0 || N > kMaxBackwardN || D < 1 || D % 8 != 0 || V < 1 || V > kMaxV || D > (int64_t)1 << 22)
-        return CE_ERR_SHAPE;
+    if (!lce_backward_shape_ok(N, D, V)) return CE_ERR_SHAPE;
     if (!W || !dW) return CE_ERR_NULL;
     if (N > 0 && (!H || !targets || !lse || !g || !dH)) return CE_ERR_NULL;
     const size_t need = ce::lce_backward_workspace_bytes(N, D, V);

@@ -223,6 +223,11 @@ struct LceCall {
 
 size_t lce_workspace_bytes(int64_t N, int64_t D, int64_t V);
 hipError_t launch_lce_forward(const LceCall& c);
+// Work-items of an MFMA tile launch over rows x cols (one workgroup per 256 x 256 tile,
+// in whole super-blocks).  A dispatch holds at most kMaxGridItems; the tile kernels do
+// not loop over tiles, so a larger product is rejected before any launch.
+constexpr int64_t kMaxGridItems = ((int64_t)1 << 32) - 1;
+int64_t lce_tile_grid_items(int64_t rows, int64_t cols);
 
 // dZ for vocabulary columns [c0, c0 + width) of all N rows, bf16, row r at G + r * ldG.
 struct LceGradChunk {
@@ -302,6 +307,8 @@ enum class LceBackwardStatus { kOk, kHip };
 // over the whole vocabulary, and the part of `workspace_bytes` a call uses.
 size_t lce_backward_workspace_bytes(int64_t N, int64_t D, int64_t V);
 size_t lce_backward_workspace_bytes_one_pass(int64_t N, int64_t D, int64_t V);
+// Whether the chunked layout's launches fit a dispatch (see kMaxGridItems).
+bool lce_backward_grids_fit(int64_t N, int64_t D, int64_t V);
 size_t lce_backward_workspace_used(int64_t N, int64_t D, int64_t V, size_t workspace_bytes);
 LceBackwardStatus run_lce_backward(const LceBackwardCall& c);
 

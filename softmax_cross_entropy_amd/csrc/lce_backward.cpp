@@ -62,10 +62,17 @@ Layout chunked(int64_t N, int64_t D, int64_t V) {
     return layout(N, D, v256 < kChunkCols ? v256 : kChunkCols);
 }
 
+// Whether a call with chunks of `chunk` columns fits the dispatches: the gradient tiles
+// over N x chunk, and the two products over N x D and chunk x D in one launch.
+bool grids_fit(int64_t N, int64_t D, int64_t chunk) {
+    return lce_tile_grid_items(N, chunk) <= kMaxGridItems &&
+           lce_tile_grid_items(N, D) + lce_tile_grid_items(chunk, D) <= kMaxGridItems;
+}
+
 // The layout a call with `bytes` of workspace runs: the whole vocabulary as one chunk
-// when the workspace holds it, else chunks of 8192 columns.
+// when the workspace holds it (and its grids fit a dispatch), else chunks of 8192 columns.
 Layout pick(int64_t N, int64_t D, int64_t V, size_t bytes) {
-    if (V <= kMaxOnePassV) {
+    if (V <= kMaxOnePassV && grids_fit(N, D, round256(V))) {
         const Layout one = layout(N, D, round256(V));
         if (bytes >= one.total) return one;
     }
@@ -75,6 +82,8 @@ Layout pick(int64_t N, int64_t D, int64_t V, size_t bytes) {
 }  // namespace
 
 size_t lce_backward_workspace_bytes(int64_t N, int64_t D, int64_t V) { return chunked(N, D, V).total; }
+
+bool lce_backward_grids_fit(int64_t N, int64_t D, int64_t V) { return grids_fit(N, D, chunked(N, D, V).chunk); }
 
 size_t lce_backward_workspace_bytes_one_pass(int64_t N, int64_t D, int64_t V) {
     return pick(N, D, V, SIZE_MAX).total;

@@ -736,6 +736,14 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
+int64_t lce_tile_grid_items(int64_t rows, int64_t cols) {
+    // geometry() in 64-bit arithmetic, for sizes whose grid may not fit a dispatch
+    const int64_t rt = (rows + BM - 1) / BM, ct = (cols + BN - 1) / BN;
+    const int64_t gr = rt >= 4 ? 4 : (rt >= 2 ? 2 : 1), gc = kTilesPerGroup / gr;
+    const int64_t sb = ((rt + gr - 1) / gr) * ((ct + gc - 1) / gc);
+    return (sb + kXcds - 1) / kXcds * kXcds * kTilesPerGroup * kThreads;
+}
+
 size_t lce_workspace_bytes(int64_t N, int64_t D, int64_t V) {
     (void)D;
     const Geometry g = geometry(N, V);

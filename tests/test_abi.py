@@ -184,6 +184,30 @@ def test_lce_rejects_bad_arguments():
     assert lce(ws=ctypes.c_void_p(7 * A + 256)) == ALIAS  # workspace inside W
 
 
+def test_lce_tile_grid_bound():
+    """One workgroup of 256 work-items per 256 x 256 tile, in super-blocks of 4 x 8 tiles
+    (N of 1024 rows by 2048 columns) and whole rounds of 8 super-blocks: a dispatch holds
+    under 2^32 work-items, so a call takes at most 65535 rounds (524,280 super-blocks).  N = 8192 (8 super-block
+    rows) by V = 2048 x 65535 is the largest such shape; one more row is rejected."""
+    V = 2048 * 65535
+    assert abi.lce_workspace_size(8192, 8, V) > 0
+    assert abi.lce_workspace_size(8193, 8, V) == 0
+    assert abi.lce_workspace_size(8193, 8, 2048 * 58253) > 0   # 9 x 58253 = 524277 super-blocks
+    assert abi.lce_workspace_size(8193, 8, 2048 * 58254) == 0
+    assert lce(N=8193, D=8, V=V, wsb=1 << 50) == SHAPE
+    # the backward's two products share one launch: N x D and 8192 x D.  At N = 2^22
+    # (4096 super-block rows) and D = 2048 k they take 512 k + k rounds: k <= 127.
+    assert abi.lce_backward_workspace_size(1 << 22, 2048 * 127, 1000) > 0
+    assert abi.lce_backward_workspace_size(1 << 22, 2048 * 128, 1000) == 0
+    assert abi.lce_backward_workspace_size_one_pass(1 << 22, 2048 * 128, 1000) == 0
+    assert lbw(N=1 << 22, D=2048 * 128, wsb=1 << 50) == SHAPE
+    # one chunk over N = 2^22 rows by V = 2^22 columns would need 4096 x 2048 super-blocks:
+    # that call keeps chunks of 8192 columns
+    n, v = 1 << 22, 1 << 22
+    assert abi.lce_backward_workspace_size_one_pass(n, 8, v) == abi.lce_backward_workspace_size(n, 8, v) > 0
+    assert abi.lce_backward_workspace_size_one_pass(1 << 12, 8, v) > abi.lce_backward_workspace_size(1 << 12, 8, v)
+
+
 P_DH, P_DW = ctypes.c_void_p(A * 200), ctypes.c_void_p(A * 210)  # clear of the workspace
 
 
