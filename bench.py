@@ -61,7 +61,7 @@ TRAFFIC = {
         "bytes": 1244996898
     },
     "lce_forward": {
-        "source_sha": "8d869c11a4c94fa7",
+        "source_sha": "3835350e1272f8ac",
         "bytes": 15162830132
     },
     "kl_forward": {
@@ -97,7 +97,7 @@ TRAFFIC = {
         "bytes": 936623402
     },
     "lce_backward": {
-        "source_sha": "409a840e62f92f80",
+        "source_sha": "4022bc70b5db195f",
         "bytes": 61143499835
     },
     "ce_forward f32 [1048576 x 8]": {
