@@ -487,6 +487,22 @@ def main():
     def clean_cache():
         torch.sum(CLEAN, dim=0, out=clean_out)
 
+    # Events bracket GPU time only if the timed calls are already queued when the first
+    # event runs.  The host side of a call (argument checks, ctypes marshalling) takes tens
+    # of microseconds, more than a small batch's kernel, so before each timed region a GPU
+    # spin (torch.cuda._sleep) holds the stream while the host queues the events and the
+    # calls behind them.  The spin touches no memory: the cache state is unchanged.
+    spin_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda._sleep(1000)
+    spin_ev[0].record(stream)
+    torch.cuda._sleep(1 << 20)
+    spin_ev[1].record(stream)
+    torch.cuda.synchronize()
+    spin_cycles_per_ms = (1 << 20) / max(spin_ev[0].elapsed_time(spin_ev[1]), 1e-3)
+
+    def hold(ms_):
+        torch.cuda._sleep(int(spin_cycles_per_ms * ms_))
+
     def timed_pair(fwd, vjp, reps=K, pre=None):
         for i in range(3):
             if pre:
@@ -498,6 +514,7 @@ def main():
         for i in range(reps):
             if pre:
                 pre()
+            hold(0.5)
             pev[i][0].record(stream)
             fwd(i)
             pev[i][1].record(stream)
@@ -520,6 +537,7 @@ def main():
         for i in range(reps):
             if pre:
                 pre()
+            hold(0.5)
             pev[i][0].record(stream)
             fn(i)
             pev[i][1].record(stream)
@@ -535,6 +553,7 @@ def main():
             per_batch = []
             for _ in range(batches):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                hold(0.15 * iters)
                 e0.record(stream)
                 for i in range(iters):
                     fn(i)
@@ -924,7 +943,9 @@ def main():
     cfg["timing"] = ("CE parts: inside the step (after the previous step's lce_forward); parts timed apart: each "
                      "fwd+VJP pair after a 512 MiB read that leaves the Infinity Cache clean, as in the step, "
                      "and again back to back (each call also writes back the previous call's cached "
-                     "gradient lines); HBM rooflines: the back-to-back times")
+                     "gradient lines); HBM rooflines: the back-to-back times; every timed region of the "
+                     "parts starts behind a GPU spin that holds the stream until the host has queued it, so "
+                     "the events measure GPU time, not the host's launch cost")
     out["config"] = cfg
     out["parts"] = parts_out
     # the dominant kernel of the step by time (the parts timed apart count only without a step)
