@@ -8,8 +8,8 @@
 //
 // Kernels:
 //   lce_tile<kTileFwd>   one 256 x 256 tile of Z per workgroup (bf16 MFMA 32x32x16, fp32
-//                    accumulate, K streamed through LDS in 64-wide double-buffered
-//                    stages).  Its epilogue turns the fp32 accumulators straight into one
+//                    accumulate, K streamed through LDS in 64-wide stages, two buffers
+//                    for H's rows and three for W's).  Its epilogue turns the fp32 accumulators straight into one
 //                    (m, s) pair per row for each 128-column slab (exact slab maximum,
 //                    then one exponential per logit), and stores the target logit from
 //                    the same accumulator when the target column is in the slab.
@@ -49,7 +49,12 @@ constexpr int kThreads = 256;        // 4 waves as 2 x 2, each owning 128 x 128 
 constexpr int WT = 128;              // wave tile edge
 constexpr int FB = WT / 32;          // 4 x 4 MFMA 32x32 blocks per wave
 constexpr int kStageBytes = BM * BK * 2;  // 32 KiB per operand per stage
-constexpr int kStageArea = 2 * 2 * kStageBytes;  // two stages of A and B
+// LDS rings: two stages of A and three of B (160 KiB, all of a compute unit's LDS).  The
+// third B buffer lets a stage's B rows be loaded a whole stage earlier than its A rows,
+// so the loads spread over all four K16 steps of a stage (see the K loop).
+constexpr int kBufA = 2;
+constexpr int kBufB = 3;
+constexpr int kStageArea = (kBufA + kBufB) * kStageBytes;
 // The gradient epilogue stages each wave's 128 x 128 bf16 block of dZ through LDS,
 // column-major with a column pitch of 136 elements (272 bytes: 16-byte aligned columns,
 // and the two half-waves' columns four apart land in different banks).
@@ -118,12 +123,12 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a0, TileArgs a1
     const bool second = kGemm && (int)blockIdx.x >= split;
     const TileArgs a = second ? a1 : a0;
     // One LDS object (the compiler then sees the DMA writes and the fragment reads as
-    // one array and inserts no waits of its own): two stages of A and B (or, in the
-    // gradient epilogue, the dZ staging blocks), then targets.
+    // one array and inserts no waits of its own): the A and B stage rings (or, in the
+    // gradient epilogue, the dZ staging blocks).
     constexpr int kData = kGrad && kStagingBytes > kStageArea ? kStagingBytes : kStageArea;
-    __shared__ __attribute__((aligned(16))) char smem[kData + BM * 4];
-    char (*lds)[2][kStageBytes] = reinterpret_cast<char (*)[2][kStageBytes]>(smem);
-    int32_t* tile_targets = reinterpret_cast<int32_t*>(smem + kData);
+    __shared__ __attribute__((aligned(16))) char smem[kData];
+    auto lds_a = [&](int buf) { return smem + buf * kStageBytes; };
+    auto lds_b = [&](int buf) { return smem + (kBufA + buf) * kStageBytes; };
 
     // ---- which tile: XCD-aware super-blocks ----------------------------------
     // Consecutive workgroups go to the 8 XCDs in turn.  The k-th workgroup an XCD
@@ -184,9 +189,10 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a0, TileArgs a1
     // The LDS destination of group q is the group-0 slot plus q * 1 KiB; the instruction's
     // immediate offset moves the LDS and the global address together, so every group
     // shares one LDS base (M0) and the global address is pre-biased by -q KiB.
-    // DMA of one stage, group by group: groups 0..7 load A rows, 8..15 load W rows.
-    // Group q fills LDS rows wave * 64 + (q % 8) * 8 .. + 7.  The byte offset into the
-    // tile is row * 2D + K bytes, below (valid rows) * 2D.
+    // DMA of one stage, group by group: groups 0..7 load A rows, 8..15 load W rows, into
+    // A buffer `buf` or B buffer `buf` of the rings.  Group q fills LDS rows
+    // wave * 64 + (q % 8) * 8 .. + 7.  The byte offset into the tile is row * 2D + K
+    // bytes, below (valid rows) * 2D.
     auto dma_group = [&](auto qc, int kt, int buf) {
         constexpr int q = decltype(qc)::value % 8;
         constexpr bool is_b = decltype(qc)::value >= 8;
@@ -197,25 +203,34 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a0, TileArgs a1
         // K tail: past K, re-read this row's last chunk; zeroed in LDS once it lands
         const uint32_t kb = (uint32_t)(k0 + koff[q & 1] < a.K ? koff[q & 1] : a.K - 8 - k0) * 2;
         const uint32_t voff = (uint32_t)(k0 * 2) + ((uint32_t)rr * (is_b ? b_row_bytes : a_row_bytes) + kb);
-        char* dst = &lds[buf][is_b ? 1 : 0][(wave * 64 + q * 8) * 128];
+        char* dst = (is_b ? lds_b(buf) : lds_a(buf)) + (wave * 64 + q * 8) * 128;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(is_b ? rsrc_b : rsrc_a, (lds_void_t*)dst, 16, voff, 0, 0, 0);
     };
-    auto issue = [&](int kt, int buf) {
+    // all of stage kt's A rows (groups 0..7) or B rows (8..15)
+    auto issue = [&](auto bc, int kt, int buf) {
+        constexpr int q0 = decltype(bc)::value ? 8 : 0;
         [&]<int... Q>(std::integer_sequence<int, Q...>) {
-            (dma_group(std::integral_constant<int, Q>{}, kt, buf), ...);
-        }(std::make_integer_sequence<int, 16>{});
+            (dma_group(std::integral_constant<int, q0 + Q>{}, kt, buf), ...);
+        }(std::make_integer_sequence<int, 8>{});
     };
     // Waits are written with the builtin, which the compiler's own wait insertion sees
     // (an inline-asm wait is opaque to it, so it added lgkmcnt(0) waits of its own after
     // the barrier); the empty asm statements keep LDS accesses from moving across them.
     // s_waitcnt immediates on gfx9: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8.
     constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0)
+    constexpr int kWaitVm8 = 0x0F78;    // vmcnt(8): one operand's loads of a stage pending
     constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
-    // Waits until the DMA of stage s has landed (loads retire in order; nothing else is
-    // in flight by then).
-    auto wait_stage = [&]() {
+    // Waits until every DMA issued has landed (loads retire in order).
+    auto wait_all = [&]() {
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        asm volatile("" ::: "memory");
+    };
+    // Waits until all but the last 8 loads issued have landed: in the loop, those 8 are
+    // the B rows of the stage after next, issued during this stage's first two steps.
+    auto wait_but_next_b = [&]() {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(kWaitVm8);
         asm volatile("" ::: "memory");
     };
     auto lds_barrier = [&]() {
@@ -226,16 +241,16 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a0, TileArgs a1
     };
     // In a K-tail stage the chunks past D hold copies of a valid chunk: overwrite this
     // lane's slots with zeros after its loads have landed, before the barrier that
-    // publishes the stage.
-    auto zero_tail = [&](int kt, int buf) {
+    // publishes the stage (A buffer abuf, B buffer bbuf).
+    auto zero_tail = [&](int kt, int abuf, int bbuf) {
         const int64_t k0 = (int64_t)kt * BK;
         if (k0 + BK <= a.K) return;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             if (k0 + koff[q & 1] >= a.K) {
                 const int o = (wave * 64 + q * 8) * 128 + lane * 16;
-                *reinterpret_cast<U4*>(&lds[buf][0][o]) = U4{{0u, 0u, 0u, 0u}};
-                *reinterpret_cast<U4*>(&lds[buf][1][o]) = U4{{0u, 0u, 0u, 0u}};
+                *reinterpret_cast<U4*>(lds_a(abuf) + o) = U4{{0u, 0u, 0u, 0u}};
+                *reinterpret_cast<U4*>(lds_b(bbuf) + o) = U4{{0u, 0u, 0u, 0u}};
             }
         }
     };
@@ -262,9 +277,9 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a0, TileArgs a1
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) off[kk] = l32 * 128 + (((kk * 2 + h2) ^ sw) << 4);
 
-    auto read_frags = [&](int buf, int kk, bf16x8 (&fa)[FB], bf16x8 (&fb)[FB]) {
-        const char* As = &lds[buf][0][wm * WT * 128];
-        const char* Bs = &lds[buf][1][wn * WT * 128];
+    auto read_frags = [&](int abuf, int bbuf, int kk, bf16x8 (&fa)[FB], bf16x8 (&fb)[FB]) {
+        const char* As = lds_a(abuf) + wm * WT * 128;
+        const char* Bs = lds_b(bbuf) + wn * WT * 128;
 #pragma unroll
         for (int i = 0; i < FB; ++i) {
             fa[i] = *reinterpret_cast<const bf16x8*>(As + i * 32 * 128 + off[kk]);
@@ -286,19 +301,20 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a0, TileArgs a1
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
         }
     };
-    // A K16 step after a stage's barrier: its 16 MFMAs (on fa, fb) in 8 chunks of 2, each
-    // chunk followed by one LDS read of a later step's fragments (into na, nb from buffer
-    // rbuf, K16 step rkk) and one DMA load, group q0 + chunk, of stage kt_load into buffer
-    // lbuf.  The scheduler keeps the chunk order, so the DMA issue never idles the
-    // matrix pipe.  The stage's 16 DMA loads are split over the two steps after the
-    // barrier: issued in one step, they filled the vector-memory address queues (the
-    // counters showed them full a tenth of the kernel's time) and stalled the MFMAs
-    // queued behind them.
-    auto step_dma = [&](auto q0c, const bf16x8 (&fa)[FB], const bf16x8 (&fb)[FB], int rbuf, int rkk,
-                        bf16x8 (&na)[FB], bf16x8 (&nb)[FB], int kt_load, int lbuf) {
+    // One K16 step: its 16 MFMAs (on fa, fb) in 8 chunks of 2, each chunk followed by one
+    // LDS read of a later step's fragments (into na, nb from A buffer rabuf and B buffer
+    // rbbuf, K16 step rkk), and every other chunk by one DMA load, group q0 + chunk / 2,
+    // of stage kt_load into buffer lbuf of that group's ring.  The scheduler keeps the
+    // chunk order, so the DMA issue never idles the matrix pipe.  A stage's 16 loads are
+    // spread over all four K16 steps, 4 per step: B rows in the two steps before the
+    // barrier, A rows in the two after.  Issued 16 to a step they filled the
+    // vector-memory address queues (the counters showed them full a tenth of the
+    // kernel's time) and stalled the MFMAs queued behind them.
+    auto step = [&](auto q0c, const bf16x8 (&fa)[FB], const bf16x8 (&fb)[FB], int rabuf, int rbbuf, int rkk,
+                    bf16x8 (&na)[FB], bf16x8 (&nb)[FB], int kt_load, int lbuf) {
         constexpr int q0 = decltype(q0c)::value;
-        const char* As = &lds[rbuf][0][wm * WT * 128];
-        const char* Bs = &lds[rbuf][1][wn * WT * 128];
+        const char* As = lds_a(rabuf) + wm * WT * 128;
+        const char* Bs = lds_b(rbbuf) + wn * WT * 128;
         auto chunk = [&](auto cc) {
             constexpr int c = decltype(cc)::value;
             constexpr int i = c / 2, j0 = 2 * (c % 2);
@@ -308,7 +324,7 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a0, TileArgs a1
                 na[c] = *reinterpret_cast<const bf16x8*>(As + c * 32 * 128 + off[rkk]);
             else
                 nb[c - 4] = *reinterpret_cast<const bf16x8*>(Bs + (c - 4) * 32 * 128 + off[rkk]);
-            dma_group(std::integral_constant<int, q0 + c>{}, kt_load, lbuf);
+            if constexpr (c % 2 == 1) dma_group(std::integral_constant<int, q0 + c / 2>{}, kt_load, lbuf);
             __builtin_amdgcn_sched_barrier(0);
         };
         [&]<int... C>(std::integer_sequence<int, C...>) {
@@ -329,7 +345,7 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a0, TileArgs a1
     // with no stage load in flight (the compiler waits for every LDS load in flight
     // before a transposing read).
     auto put_wt = [&](int s, int buf) {
-        const char* Bs = &lds[buf][1][0];
+        const char* Bs = lds_b(buf);
         const int g4 = lane >> 4, j = lane & 15;
         const int64_t wt_w8 = (a.c_end - a.c0 + 7) & ~(int64_t)7;
 #pragma unroll
@@ -359,29 +375,32 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a0, TileArgs a1
     };
     auto owns_stage = [&](int s) { return s % a.n_row_tiles == row_tile; };
 
-    auto sync_stage = [&](int kt, int cur, int nk) {
-        // stage kt + 1 has landed (issued one stage earlier); after this barrier every
-        // wave has finished reading buffer `cur`, which then takes stage kt + 2
-        wait_stage();
-        if (kt + 1 < nk) zero_tail(kt + 1, cur ^ 1);
+    // The barrier of stage kt (A buffer ca, B buffer cb): stage kt + 1 (A buffer na, B
+    // buffer nb) has landed, with only the B rows of stage kt + 2 still in flight; after
+    // it every wave has finished reading stage kt's buffers, which then take the A rows
+    // of stage kt + 2 and the B rows of stage kt + 3.
+    auto sync_stage = [&](int kt, int cb, int na, int nb, int nk) {
+        wait_but_next_b();
+        if (kt + 1 < nk) zero_tail(kt + 1, na, nb);
         if constexpr (kGrad)
-            if (owns_stage(kt)) put_wt(kt, cur);
+            if (owns_stage(kt)) put_wt(kt, cb);
         lds_barrier();
     };
-
 
     // Pipeline: the fragments of a K16 step are read from LDS two steps ahead, into four
     // rotating sets, so each wave keeps twice as many reads in flight (one wave per SIMD
     // is bound by LDS read latency).  A stage's single barrier sits between its steps 1
     // and 2: by then every wave has read all four steps of the stage (steps 2 and 3 during
-    // steps 0 and 1), so the DMA of stage kt + 2 can go into its buffer, and stage kt + 1
-    // has landed, so steps 2 and 3 can read the next stage's first two steps.  The DMA,
-    // issued during steps 2 and 3, has two to three K16 steps to land.
+    // steps 0 and 1), so its buffers are free, and stage kt + 1 has landed, so steps 2
+    // and 3 can read the next stage's first two steps.  The A rows of stage kt + 2 are
+    // loaded during steps 2 and 3 into stage kt's A buffer, and have two to three K16
+    // steps to land.  The B rows of stage kt + 2 are loaded during steps 0 and 1, into
+    // the third B buffer (stage kt - 1's, free since the previous barrier), and have five
+    // to six steps.  So each K16 step issues 4 of a stage's 16 loads.
     const int nk = (int)((a.K + BK - 1) / BK);
     bf16x8 fa0[FB], fb0[FB], fa1[FB], fb1[FB], fa2[FB], fb2[FB], fa3[FB], fb3[FB];
-    // targets of this tile's rows, for the epilogue
-    if constexpr (!kGemm) tile_targets[tid] = row0 + tid < a.N ? a.targets[row0 + tid] : -1;
-    issue(0, 0);
+    issue(std::false_type{}, 0, 0);
+    issue(std::true_type{}, 0, 0);
     if constexpr (kGemm) {
         // An accumulating product starts from C's old values, loaded while the first
         // stage's DMA is in flight, so its epilogue only stores.  (Read and added in the
@@ -431,42 +450,54 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a0, TileArgs a1
             }
         }
     }
-    wait_stage();
-    zero_tail(0, 0);
+    wait_all();
+    zero_tail(0, 0, 0);
     lds_barrier();
-    if (nk > 1) issue(1, 1);
-    read_frags(0, 0, fa0, fb0);
-    read_frags(0, 1, fa1, fb1);
+    // stage 1: B rows, then A rows (the loop's first wait leaves only later loads pending)
+    if (nk > 1) {
+        issue(std::true_type{}, 1, 1);
+        issue(std::false_type{}, 1, 1);
+    }
+    read_frags(0, 0, 0, fa0, fb0);
+    read_frags(0, 0, 1, fa1, fb1);
+    int cb = 0;  // B buffer of stage kt: kt % 3
     for (int kt = 0; kt + 1 < nk; ++kt) {
-        const int cur = kt & 1;
-        read_frags(cur, 2, fa2, fb2);
-        mfma_all(fa0, fb0);
-        interleave();
-        read_frags(cur, 3, fa3, fb3);
-        mfma_all(fa1, fb1);
-        interleave();
-        sync_stage(kt, cur, nk);
-        // the last stage re-issues stage nk - 1 into the free buffer, which is never read:
-        // no branch around the DMA, so it can interleave with the MFMAs
+        const int ca = kt & 1;
+        const int b_next = cb == 2 ? 0 : cb + 1, b_load = b_next == 2 ? 0 : b_next + 1;
+        // the last iteration re-issues stage nk - 1 into free buffers, which are never
+        // read: no branch around the DMA, so it can interleave with the MFMAs
         const int kt_load = kt + 2 < nk ? kt + 2 : nk - 1;
-        step_dma(std::integral_constant<int, 0>{}, fa2, fb2, cur ^ 1, 0, fa0, fb0, kt_load, cur);
-        step_dma(std::integral_constant<int, 8>{}, fa3, fb3, cur ^ 1, 1, fa1, fb1, kt_load, cur);
+        step(std::integral_constant<int, 8>{}, fa0, fb0, ca, cb, 2, fa2, fb2, kt_load, b_load);
+        step(std::integral_constant<int, 12>{}, fa1, fb1, ca, cb, 3, fa3, fb3, kt_load, b_load);
+        sync_stage(kt, cb, ca ^ 1, b_next, nk);
+        step(std::integral_constant<int, 0>{}, fa2, fb2, ca ^ 1, b_next, 0, fa0, fb0, kt_load, ca);
+        step(std::integral_constant<int, 4>{}, fa3, fb3, ca ^ 1, b_next, 1, fa1, fb1, kt_load, ca);
+        cb = b_next;
     }
     {
-        const int cur = (nk - 1) & 1;
-        read_frags(cur, 2, fa2, fb2);
+        const int ca = (nk - 1) & 1;
+        read_frags(ca, cb, 2, fa2, fb2);
         mfma_all(fa0, fb0);
         interleave();
-        read_frags(cur, 3, fa3, fb3);
+        read_frags(ca, cb, 3, fa3, fb3);
         mfma_all(fa1, fb1);
         interleave();
         mfma_all(fa2, fb2);
         mfma_all(fa3, fb3);
     }
     // the last loop iteration's (redundant) DMA must land before the workgroup can end
-    wait_stage();
+    wait_all();
     if constexpr (kGrad)
-        if (owns_stage(nk - 1)) put_wt(nk - 1, (nk - 1) & 1);
+        if (owns_stage(nk - 1)) put_wt(nk - 1, cb);
+    // targets of this lane's four rows, for the epilogue
+    int32_t ytile[FB] = {-1, -1, -1, -1};
+    if constexpr (!kGemm) {
+#pragma unroll
+        for (int i = 0; i < FB; ++i) {
+            const int64_t row = row0 + wm * WT + i * 32 + l32;
+            ytile[i] = row < a.N ? a.targets[row] : -1;
+        }
+    }
 
     // ---- epilogue: (m, s) per row over this wave's 128 columns ----------------
     // acc[i][j][e] holds Z[row = wrow0 + i*32 + l32][col = wcol0 + j*32 + 8*(e/4) + 4*h2 + e%4]:
@@ -505,7 +536,7 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a0, TileArgs a1
         // row-major copy is stored directly, 4 columns per store; the transposed copy goes
         // through this wave's LDS block first, so that it leaves in 16-byte stores of 8
         // rows of a column.  After the barrier no wave reads the stage buffers any more
-        // (the last DMA has landed: wait_stage above).
+        // (the last DMA has landed: wait_all above).
         // this lane's rows' saved (m, log s) and upstream gradients, loaded together
         float2 lse_r[FB];
         float g_r[FB];
@@ -526,7 +557,7 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a0, TileArgs a1
             const int lr = wm * WT + i * 32 + l32;
             const int64_t row = row0 + lr;
             if (row >= a.N) continue;
-            const int32_t y = tile_targets[lr];
+            const int32_t y = ytile[i];
             const float2 l = lse_r[i];
             const float m = (y >= 0 && (int64_t)y < a.V) ? l.x : __builtin_nanf("");
             const float nlsl = -l.y * kLog2e;
@@ -609,7 +640,7 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a0, TileArgs a1
     #pragma unroll
         for (int i = 0; i < FB; ++i) {
             const int lr = wm * WT + i * 32 + l32;
-            const int64_t yrel = (int64_t)tile_targets[lr] - wcol0;
+            const int64_t yrel = (int64_t)ytile[i] - wcol0;
             if (yrel >= 0 && yrel < WT && (((int)yrel >> 2) & 1) == h2) {
                 const int c = (int)yrel;
                 const int jj = c >> 5, ee = (((c >> 3) & 3) << 2) | (c & 3);
