@@ -474,6 +474,11 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a0, TileArgs a1
         step(std::integral_constant<int, 4>{}, fa3, fb3, ca ^ 1, b_next, 1, fa1, fb1, kt_load, ca);
         cb = b_next;
     }
+    // The forward's epilogue takes its rows' targets from LDS once the K loop is done
+    // (held in registers through the epilogue, they pushed it into spills): thread t loads
+    // row t's before the last stage, and stores it once every wave is past the loop.
+    int32_t my_target = -1;
+    if constexpr (kMode == kTileFwd) my_target = row0 + tid < a.N ? a.targets[row0 + tid] : -1;
     {
         const int ca = (nk - 1) & 1;
         read_frags(ca, cb, 2, fa2, fb2);
@@ -489,9 +494,15 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a0, TileArgs a1
     wait_all();
     if constexpr (kGrad)
         if (owns_stage(nk - 1)) put_wt(nk - 1, cb);
-    // targets of this lane's four rows, for the epilogue
+    int32_t* const tile_targets = reinterpret_cast<int32_t*>(smem);
+    if constexpr (kMode == kTileFwd) {
+        lds_barrier();  // every wave is done with the stage buffers
+        tile_targets[tid] = my_target;
+        lds_barrier();
+    }
+    // the gradient epilogue's targets: this lane's four rows, in registers
     int32_t ytile[FB] = {-1, -1, -1, -1};
-    if constexpr (!kGemm) {
+    if constexpr (kGrad) {
 #pragma unroll
         for (int i = 0; i < FB; ++i) {
             const int64_t row = row0 + wm * WT + i * 32 + l32;
@@ -640,7 +651,7 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a0, TileArgs a1
     #pragma unroll
         for (int i = 0; i < FB; ++i) {
             const int lr = wm * WT + i * 32 + l32;
-            const int64_t yrel = (int64_t)ytile[i] - wcol0;
+            const int64_t yrel = (int64_t)tile_targets[lr] - wcol0;
             if (yrel >= 0 && yrel < WT && (((int)yrel >> 2) & 1) == h2) {
                 const int c = (int)yrel;
                 const int jj = c >> 5, ee = (((c >> 3) & 3) << 2) | (c & 3);
