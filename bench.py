@@ -50,55 +50,55 @@ CSRC = os.path.join(ROOT, "softmax_cross_entropy_amd", "csrc")
 TRAFFIC = {
     "ce_forward_vjp": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 1290974879
+        "bytes": 1290959823
     },
     "ce_forward": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 622592558
+        "bytes": 622592095
     },
     "ce_vjp": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 1244996898
+        "bytes": 1244996458
     },
     "lce_forward": {
-        "source_sha": "3835350e1272f8ac",
-        "bytes": 15162830132
+        "source_sha": "e0817ec8beddf69f",
+        "bytes": 15151778255
     },
     "kl_forward": {
         "source_sha": "8178fcf06dbd3aed",
-        "bytes": 622485321
+        "bytes": 622485068
     },
     "kl_vjp": {
         "source_sha": "8178fcf06dbd3aed",
-        "bytes": 933637939
+        "bytes": 933637494
     },
     "ce_forward_ex": {
         "source_sha": "9c57c5ac9d01527f",
-        "bytes": 622631175
+        "bytes": 622630829
     },
     "ce_vjp_ex": {
         "source_sha": "9c57c5ac9d01527f",
-        "bytes": 1206070618
+        "bytes": 1206070281
     },
     "ce_forward_probs": {
         "source_sha": "9c57c5ac9d01527f",
-        "bytes": 622466637
+        "bytes": 622465832
     },
     "ce_vjp_probs": {
         "source_sha": "9c57c5ac9d01527f",
-        "bytes": 933601845
+        "bytes": 933601400
     },
     "js_forward": {
         "source_sha": "f78dc0c5b2112634",
-        "bytes": 1224823487
+        "bytes": 1224833887
     },
     "js_vjp": {
         "source_sha": "f78dc0c5b2112634",
-        "bytes": 936623402
+        "bytes": 936620827
     },
     "lce_backward": {
-        "source_sha": "4022bc70b5db195f",
-        "bytes": 61143499835
+        "source_sha": "0fc202e2245eff94",
+        "bytes": 55028917917
     },
     "ce_forward f32 [1048576 x 8]": {
         "source_sha": "30f4ec33c2551876",
@@ -149,6 +149,8 @@ TRAFFIC = {
         "bytes": 10821186773
     }
 }
+
+
 
 
 def source_sha(kernel):
