@@ -40,7 +40,6 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
 
 constexpr int BM = 256;              // rows of H per tile
 constexpr int BN = 256;              // rows of W (vocabulary columns) per tile
@@ -341,9 +340,11 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a0, TileArgs a1
     // cb .. cb + 3; a second read gives rows cb + 4 .. cb + 7, and the lane stores the 8
     // of them as 16 bytes of WT row kb + j.  Columns past the chunk are stored as zeros
     // up to the next multiple of 8 (the K padding of the dH product).  A stage is read
-    // for this when its loads have landed and before the barrier that frees its buffer,
-    // with no stage load in flight (the compiler waits for every LDS load in flight
-    // before a transposing read).
+    // for this when its loads have landed and before the barrier that frees its buffer.
+    // The two reads of a step are inline assembly that waits for them in the same
+    // statement: through the builtin, the compiler waited for every stage load in flight
+    // first (vmcnt(0)), since it cannot tell which LDS bytes the builtin reads, and the B
+    // rows of the stage after next are always in flight here (into another buffer).
     auto put_wt = [&](int s, int buf) {
         const char* Bs = lds_b(buf);
         const int g4 = lane >> 4, j = lane & 15;
@@ -354,8 +355,13 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a0, TileArgs a1
             const int cb = wave * 64 + 32 * (it & 1) + 8 * g4;
             const int kk = kb + 4 * (j & 3);
             auto off = [&](int row) { return row * 128 + (((kk >> 3) ^ ((row >> 1) & 7)) << 4) + (kk & 7) * 2; };
-            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(Bs + off(cb + (j >> 2))));
-            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(Bs + off(cb + 4 + (j >> 2))));
+            v4i16 lo, hi;
+            {
+                const uint32_t alo = (uint32_t)(uintptr_t)(Bs + off(cb + (j >> 2)));
+                const uint32_t ahi = (uint32_t)(uintptr_t)(Bs + off(cb + 4 + (j >> 2)));
+                asm volatile("ds_read_b64_tr_b16 %0, %2\n\tds_read_b64_tr_b16 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                             : "=&v"(lo), "=&v"(hi) : "v"(alo), "v"(ahi) : "memory");
+            }
             const int64_t kg = (int64_t)s * BK + kb + j;
             const int64_t cg = col0 + cb;  // vocabulary column of the first of the 8
             if (kg < a.K && cg - a.c0 < wt_w8) {
