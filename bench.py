@@ -50,55 +50,55 @@ CSRC = os.path.join(ROOT, "softmax_cross_entropy_amd", "csrc")
 TRAFFIC = {
     "ce_forward_vjp": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 1290959823
+        "bytes": 1290970676
     },
     "ce_forward": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 622592095
+        "bytes": 622591131
     },
     "ce_vjp": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 1244996458
+        "bytes": 1244995483
     },
     "lce_forward": {
-        "source_sha": "e0817ec8beddf69f",
-        "bytes": 15151778255
+        "source_sha": "bfeba56b6b1dbc19",
+        "bytes": 15152087151
     },
     "kl_forward": {
         "source_sha": "8178fcf06dbd3aed",
-        "bytes": 622485068
+        "bytes": 622483971
     },
     "kl_vjp": {
         "source_sha": "8178fcf06dbd3aed",
-        "bytes": 933637494
+        "bytes": 933636530
     },
     "ce_forward_ex": {
         "source_sha": "9c57c5ac9d01527f",
-        "bytes": 622630829
+        "bytes": 622629769
     },
     "ce_vjp_ex": {
         "source_sha": "9c57c5ac9d01527f",
-        "bytes": 1206070281
+        "bytes": 1206069424
     },
     "ce_forward_probs": {
         "source_sha": "9c57c5ac9d01527f",
-        "bytes": 622465832
+        "bytes": 622464816
     },
     "ce_vjp_probs": {
         "source_sha": "9c57c5ac9d01527f",
-        "bytes": 933601400
+        "bytes": 933600435
     },
     "js_forward": {
         "source_sha": "f78dc0c5b2112634",
-        "bytes": 1224833887
+        "bytes": 1224776799
     },
     "js_vjp": {
         "source_sha": "f78dc0c5b2112634",
-        "bytes": 936620827
+        "bytes": 936653344
     },
     "lce_backward": {
-        "source_sha": "0fc202e2245eff94",
-        "bytes": 55028917917
+        "source_sha": "cd1c39439981c775",
+        "bytes": 55428326203
     },
     "ce_forward f32 [1048576 x 8]": {
         "source_sha": "30f4ec33c2551876",
@@ -149,6 +149,7 @@ TRAFFIC = {
         "bytes": 10821186773
     }
 }
+
 
 
 
