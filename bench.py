@@ -61,7 +61,7 @@ TRAFFIC = {
         "bytes": 1244995483
     },
     "lce_forward": {
-        "source_sha": "bfeba56b6b1dbc19",
+        "source_sha": "c2ead97c2bc90bde",
         "bytes": 15152087151
     },
     "kl_forward": {
@@ -97,7 +97,7 @@ TRAFFIC = {
         "bytes": 936653344
     },
     "lce_backward": {
-        "source_sha": "cd1c39439981c775",
+        "source_sha": "1e37de0f87323df7",
         "bytes": 55428326203
     },
     "ce_forward f32 [1048576 x 8]": {

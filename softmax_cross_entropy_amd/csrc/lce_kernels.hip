@@ -9,10 +9,11 @@
 // Kernels:
 //   lce_tile<kTileFwd>   one 256 x 256 tile of Z per workgroup (bf16 MFMA 32x32x16, fp32
 //                    accumulate, K streamed through LDS in 64-wide stages, two buffers
-//                    for H's rows and three for W's).  Its epilogue turns the fp32 accumulators straight into one
-//                    (m, s) pair per row for each 128-column slab (exact slab maximum,
-//                    then one exponential per logit), and stores the target logit from
-//                    the same accumulator when the target column is in the slab.
+//                    for H's rows and three for W's).  Its epilogue turns the fp32
+//                    accumulators straight into one (m, s) pair per row for each
+//                    128-column slab (exact slab maximum, then one exponential per
+//                    logit), and stores the target logit from the same accumulator when
+//                    the target column is in the slab.
 //   lce_merge        folds the slabs of each row in slab order into (m, s), then
 //                    loss = (m - z_y) + log s and lse = (m, log s).
 //   lce_tile<kTileGrad>  the same tile of Z turned into the bf16 gradient of the logits (the
@@ -188,8 +189,8 @@ __global__ __launch_bounds__(kThreads, 1) void lce_tile(TileArgs a0, TileArgs a1
     // The LDS destination of group q is the group-0 slot plus q * 1 KiB; the instruction's
     // immediate offset moves the LDS and the global address together, so every group
     // shares one LDS base (M0) and the global address is pre-biased by -q KiB.
-    // DMA of one stage, group by group: groups 0..7 load A rows, 8..15 load W rows, into
-    // A buffer `buf` or B buffer `buf` of the rings.  Group q fills LDS rows
+    // DMA of one stage, group by group: groups 0..7 load A rows into buffer `buf` of the A
+    // ring, 8..15 load W rows into buffer `buf` of the B ring.  Group q fills LDS rows
     // wave * 64 + (q % 8) * 8 .. + 7.  The byte offset into the tile is row * 2D + K
     // bytes, below (valid rows) * 2D.
     auto dma_group = [&](auto qc, int kt, int buf) {
