@@ -116,7 +116,7 @@ int narrow_rows_per_thread(int nv) { return nv == 1 ? 4 : nv == 2 ? 2 : 1; }
 // Picks the row-to-lane mapping and the (capped) grid.  The grid never needs to
 // cover every row: all kernels loop over 64-bit row indices.
 ce_status make_plan(bool narrow_ok, int64_t V, int es, int64_t n_rows, int32_t lanes_req, bool vjp,
-                    int cus, Plan* plan) {
+                    int cus, Plan* plan, bool four_per_lane = false) {
     const int vec = 16 / es;
     const int64_t nvec = (V + vec - 1) / vec;
     Plan p{0, 0, 0, 0, 0};
@@ -125,16 +125,21 @@ ce_status make_plan(bool narrow_ok, int64_t V, int es, int64_t n_rows, int32_t l
         p.narrow_nv = (int)(V / vec);
     } else if (lanes_req == 0) {
         // One lane per row only where that measured fastest: forward rows of up to two
-        // vectors, VJP rows of one.  Otherwise about 8 vectors per lane, and at least
-        // min(nvec, 8) lanes per row, so that the lanes of a row cover whole 128-byte
-        // lines in each load and store instruction (a VJP with one lane per 4-vector row
-        // ran 1.6x slower, per 8-vector row 2.2x).
+        // vectors, VJP rows of one.  Otherwise about 8 vectors per lane (4 with
+        // four_per_lane, up to 64 lanes), and at least min(nvec, 8) lanes per row, so that
+        // the lanes of a row cover whole 128-byte lines in each load and store instruction
+        // (a VJP with one lane per 4-vector row ran 1.6x slower, per 8-vector row 2.2x).
+        // ce_vjp with 4 vectors per lane instead of 8 ran 7-13% faster VJP after VJP on
+        // 512 MiB batches of rows of 64 to 256 vectors (fp32 and bf16), and the same after a
+        // clean cache or a forward; ce_forward gained nothing from it.
         if (narrow_ok && nvec <= (vjp ? 1 : 2)) {
             p.narrow_nv = (int)(V / vec);
         } else {
             const int spread = pow2_ceil(nvec < 8 ? nvec : 8);
             const int per8 = pow2_ceil((nvec + 7) / 8);
-            p.lanes = per8 > spread ? per8 : spread;
+            const int per4 = pow2_ceil((nvec + 3) / 4);
+            const int per = four_per_lane && per4 <= 64 ? per4 : per8;
+            p.lanes = per > spread ? per : spread;
         }
     } else {
         if (lanes_req < 1 || lanes_req > 1024 || (lanes_req & (lanes_req - 1)) != 0) return CE_ERR_SHAPE;
@@ -254,7 +259,7 @@ ce_status vjp_impl(const void* logits, ce_layout in, ce_dtype dt, const int32_t*
                            V % vec == 0 && (V / vec == 1 || V / vec == 2 || V / vec == 4 || V / vec == 8);
     Plan plan;
     if (lanes != 0 || !chunk_plan(V, es, n_rows, cus, &plan))
-        if (ce_status s = make_plan(narrow_ok, V, es, n_rows, lanes, true, cus, &plan)) return s;
+        if (ce_status s = make_plan(narrow_ok, V, es, n_rows, lanes, true, cus, &plan, true)) return s;
     ce::VjpCall c{logits, host_layout(in, n_rows), (Dt)dt, targets, lse, g, n_rows, V, dlogits,
                   host_layout(out, n_rows), plan, stream};
     return from_hip(ce::launch_ce_vjp(c));
