@@ -110,19 +110,19 @@ TRAFFIC = {
     },
     "ce_forward f32 [65536 x 1024] offsets and -inf rows": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 270328956
+        "bytes": 270329035
     },
     "ce_vjp f32 [65536 x 1024] offsets and -inf rows": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 540164057
+        "bytes": 543236176
     },
     "ce_forward f16 [65536 x 1024] offsets and -inf rows": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 135597331
+        "bytes": 135597286
     },
     "ce_vjp f16 [65536 x 1024] offsets and -inf rows": {
         "source_sha": "30f4ec33c2551876",
-        "bytes": 270106831
+        "bytes": 271687663
     },
     "ce_forward f32 view [10, 119, 32768][:, :-1] (1180 rows)": {
         "source_sha": "30f4ec33c2551876",
@@ -149,6 +149,7 @@ TRAFFIC = {
         "bytes": 10821186773
     }
 }
+
 
 
 
