@@ -52,6 +52,9 @@ def upstream(N, seed):
 @pytest.mark.parametrize("N,D,V", [
     (1, 8, 1), (3, 8, 5), (37, 40, 127), (300, 72, 1000), (257, 520, 2049), (64, 256, 513),
     (100, 64, 20000), (513, 128, 8193),
+    # 3, 5 and 6 K stages in the regenerated logits (the three-buffer W ring ends in each
+    # of its states), and in the products over the tokens
+    (129, 136, 700), (260, 192, 1300), (70, 320, 257), (300, 384, 900),
 ])
 def test_small_shapes(N, D, V):
     H, W, y = inputs.linear_ce(N, D, V, seed_stream=N * 11 + D + V)

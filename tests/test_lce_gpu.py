@@ -48,6 +48,8 @@ def check(H, W, y, rows=None, W64=None, ref=None):
 @pytest.mark.parametrize("N,D,V", [
     (1, 8, 1), (3, 8, 5), (16, 64, 300), (37, 40, 127), (300, 72, 1000), (257, 520, 2049),
     (64, 4096, 513), (513, 128, 4097), (255, 200, 256),
+    # 3, 5 and 6 K stages: the three-buffer W ring ends in each of its states
+    (129, 136, 700), (260, 192, 1300), (70, 320, 257), (33, 384, 900),
 ])
 def test_small_shapes(N, D, V):
     H, W, y = inputs.linear_ce(N, D, V, seed_stream=N * 7 + D + V)
