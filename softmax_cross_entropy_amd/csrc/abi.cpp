@@ -131,7 +131,8 @@ ce_status make_plan(bool narrow_ok, int64_t V, int es, int64_t n_rows, int32_t l
         // (a VJP with one lane per 4-vector row ran 1.6x slower, per 8-vector row 2.2x).
         // ce_vjp with 4 vectors per lane instead of 8 ran 7-13% faster VJP after VJP on
         // 512 MiB batches of rows of 64 to 256 vectors (fp32 and bf16), and the same after a
-        // clean cache or a forward; ce_forward gained nothing from it.
+        // clean cache or a forward; kl_vjp and js_vjp (two rows read per row written) ran
+        // 5-9% faster VJP after VJP and 3-8% after a clean cache; ce_forward gained nothing.
         if (narrow_ok && nvec <= (vjp ? 1 : 2)) {
             p.narrow_nv = (int)(V / vec);
         } else {
@@ -522,7 +523,7 @@ ce_status div_vjp_impl(Div div, const void* q, ce_layout ql, const void* p, ce_l
     if (ce_status s = device_cus(&cus)) return s;
     Plan plan;
     if (lanes != 0 || !chunk_plan(V, es, n_rows, cus, &plan))
-        if (ce_status s = make_plan(false, V, es, n_rows, lanes, true, cus, &plan)) return s;
+        if (ce_status s = make_plan(false, V, es, n_rows, lanes, true, cus, &plan, true)) return s;
     if (js) {
         ce::JSVjpCall c{q, host_layout(ql, n_rows), p, host_layout(pl, n_rows), (Dt)dt, lse_q, lse_p, hq, g,
                         n_rows, V, dq, host_layout(dl, n_rows), plan, stream};
