@@ -116,7 +116,7 @@ int narrow_rows_per_thread(int nv) { return nv == 1 ? 4 : nv == 2 ? 2 : 1; }
 // Picks the row-to-lane mapping and the (capped) grid.  The grid never needs to
 // cover every row: all kernels loop over 64-bit row indices.
 ce_status make_plan(bool narrow_ok, int64_t V, int es, int64_t n_rows, int32_t lanes_req, bool vjp,
-                    int cus, Plan* plan, bool four_per_lane = false) {
+                    int cus, Plan* plan) {
     const int vec = 16 / es;
     const int64_t nvec = (V + vec - 1) / vec;
     Plan p{0, 0, 0, 0, 0};
@@ -125,21 +125,22 @@ ce_status make_plan(bool narrow_ok, int64_t V, int es, int64_t n_rows, int32_t l
         p.narrow_nv = (int)(V / vec);
     } else if (lanes_req == 0) {
         // One lane per row only where that measured fastest: forward rows of up to two
-        // vectors, VJP rows of one.  Otherwise about 8 vectors per lane (4 with
-        // four_per_lane, up to 64 lanes), and at least min(nvec, 8) lanes per row, so that
-        // the lanes of a row cover whole 128-byte lines in each load and store instruction
-        // (a VJP with one lane per 4-vector row ran 1.6x slower, per 8-vector row 2.2x).
-        // ce_vjp with 4 vectors per lane instead of 8 ran 7-13% faster VJP after VJP on
-        // 512 MiB batches of rows of 64 to 256 vectors (fp32 and bf16), and the same after a
-        // clean cache or a forward; kl_vjp and js_vjp (two rows read per row written) ran
-        // 5-9% faster VJP after VJP and 3-8% after a clean cache; ce_forward gained nothing.
+        // vectors, VJP rows of one.  Otherwise about 8 vectors per lane in a forward and 4
+        // in a VJP (while that takes at most 64 lanes), and at least min(nvec, 8) lanes per
+        // row, so that the lanes of a row cover whole 128-byte lines in each load and store
+        // instruction (a VJP with one lane per 4-vector row ran 1.6x slower, per 8-vector
+        // row 2.2x).  On 512 MiB batches of rows of 64 to 256 vectors, 4 vectors per lane
+        // instead of 8 ran ce_vjp 7-13% faster VJP after VJP (the same after a clean cache
+        // or a forward), kl_vjp, js_vjp and ce_vjp_probs (two rows read per row written)
+        // 5-9% faster VJP after VJP and 3-8% after a clean cache, ce_vjp_ex 6-14% faster VJP
+        // after VJP; ce_forward gained nothing.
         if (narrow_ok && nvec <= (vjp ? 1 : 2)) {
             p.narrow_nv = (int)(V / vec);
         } else {
             const int spread = pow2_ceil(nvec < 8 ? nvec : 8);
             const int per8 = pow2_ceil((nvec + 7) / 8);
             const int per4 = pow2_ceil((nvec + 3) / 4);
-            const int per = four_per_lane && per4 <= 64 ? per4 : per8;
+            const int per = vjp && per4 <= 64 ? per4 : per8;
             p.lanes = per > spread ? per : spread;
         }
     } else {
@@ -260,7 +261,7 @@ ce_status vjp_impl(const void* logits, ce_layout in, ce_dtype dt, const int32_t*
                            V % vec == 0 && (V / vec == 1 || V / vec == 2 || V / vec == 4 || V / vec == 8);
     Plan plan;
     if (lanes != 0 || !chunk_plan(V, es, n_rows, cus, &plan))
-        if (ce_status s = make_plan(narrow_ok, V, es, n_rows, lanes, true, cus, &plan, true)) return s;
+        if (ce_status s = make_plan(narrow_ok, V, es, n_rows, lanes, true, cus, &plan)) return s;
     ce::VjpCall c{logits, host_layout(in, n_rows), (Dt)dt, targets, lse, g, n_rows, V, dlogits,
                   host_layout(out, n_rows), plan, stream};
     return from_hip(ce::launch_ce_vjp(c));
@@ -523,7 +524,7 @@ ce_status div_vjp_impl(Div div, const void* q, ce_layout ql, const void* p, ce_l
     if (ce_status s = device_cus(&cus)) return s;
     Plan plan;
     if (lanes != 0 || !chunk_plan(V, es, n_rows, cus, &plan))
-        if (ce_status s = make_plan(false, V, es, n_rows, lanes, true, cus, &plan, true)) return s;
+        if (ce_status s = make_plan(false, V, es, n_rows, lanes, true, cus, &plan)) return s;
     if (js) {
         ce::JSVjpCall c{q, host_layout(ql, n_rows), p, host_layout(pl, n_rows), (Dt)dt, lse_q, lse_p, hq, g,
                         n_rows, V, dq, host_layout(dl, n_rows), plan, stream};
