@@ -126,21 +126,22 @@ ce_status make_plan(bool narrow_ok, int64_t V, int es, int64_t n_rows, int32_t l
     } else if (lanes_req == 0) {
         // One lane per row only where that measured fastest: forward rows of up to two
         // vectors, VJP rows of one.  Otherwise about 8 vectors per lane in a forward and 4
-        // in a VJP (while that takes at most 64 lanes), and at least min(nvec, 8) lanes per
+        // in a VJP (while that takes at most 256 lanes), and at least min(nvec, 8) lanes per
         // row, so that the lanes of a row cover whole 128-byte lines in each load and store
         // instruction (a VJP with one lane per 4-vector row ran 1.6x slower, per 8-vector
         // row 2.2x).  On 512 MiB batches of rows of 64 to 256 vectors, 4 vectors per lane
         // instead of 8 ran ce_vjp 7-13% faster VJP after VJP (the same after a clean cache
         // or a forward), kl_vjp, js_vjp and ce_vjp_probs (two rows read per row written)
         // 5-9% faster VJP after VJP and 3-8% after a clean cache, ce_vjp_ex 6-14% faster VJP
-        // after VJP; ce_forward gained nothing.
+        // after VJP; ce_forward gained nothing.  On rows of 512 and 1024 vectors ce_vjp ran
+        // 4-7% faster VJP after VJP and 1-4% after a clean cache; at 2000 the same.
         if (narrow_ok && nvec <= (vjp ? 1 : 2)) {
             p.narrow_nv = (int)(V / vec);
         } else {
             const int spread = pow2_ceil(nvec < 8 ? nvec : 8);
             const int per8 = pow2_ceil((nvec + 7) / 8);
             const int per4 = pow2_ceil((nvec + 3) / 4);
-            const int per = vjp && per4 <= 64 ? per4 : per8;
+            const int per = vjp && per4 <= 256 ? per4 : per8;
             p.lanes = per > spread ? per : spread;
         }
     } else {
